@@ -1,0 +1,192 @@
+/*
+ * tp_shard.h -- one rank's shard of a Megatron-style tensor-parallel
+ * transformer layer, computed on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation (undercodenews post 110319 on tensor parallelism in
+ * transformers, section "the Original"; netray glossary "What Is Tensor
+ * Parallelism?", section "Tensor Parallelism Explained"):
+ *
+ *   ATTN stage   n1 = RMSNorm(x)                        (replicated input)
+ *                [q|k|v] = n1 * W_qkv,r^T                (column-parallel: rank r's heads)
+ *                q,k rotated (RoPE); k,v stored in rank r's KV cache
+ *                o = causal softmax(q k^T / sqrt(d)) v   (per local head, no communication)
+ *                partial_attn = o * W_o[:, cols_r]^T     (row-parallel: one summand)
+ *   reduce       h = x + sum_r partial_attn_r            (the all-reduce's sum)
+ *   MLP stage    n2 = RMSNorm(h)
+ *                act = SiLU(n2 W_gate,r^T) * (n2 W_up,r^T)   or GELU(n2 W_1,r^T)
+ *                partial_mlp = act * W_down[:, F_r]^T    (row-parallel: one summand)
+ *   reduce       y = h + sum_r partial_mlp_r
+ *
+ * Rank r owns contiguous blocks: query heads [r*H/t, (r+1)*H/t), KV heads
+ * [r*Hkv/t, (r+1)*Hkv/t) and FFN columns [r*F/t, (r+1)*F/t).  Query head j
+ * reads KV head floor(j / (H/Hkv)).  RoPE is rotate-half (pairs i, i+d/2),
+ * theta_i = base^(-2i/d); prefill positions are 0..S-1, a decode token sits
+ * at position L (the cache length before the call).  No biases.
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device addresses on the current device; host
+ *    pointers are marked "host".  Tensors are dense row-major, innermost
+ *    dimension last.  Weight matrices are stored [out, in].
+ *  - Element type: TP_BF16 (bfloat16 storage, fp32 arithmetic) or TP_F32,
+ *    chosen at create time for activations, weights, KV cache and outputs.
+ *    Partial sums are always fp32.
+ *  - Ownership: the caller owns every pointer it passes and must keep the
+ *    memory alive until the work enqueued on `stream` has completed.  The
+ *    library owns the packed weight slices, the KV cache and its workspace
+ *    and frees them in the matching *_destroy call.
+ *  - Asynchrony: all device work is enqueued on `stream` (a hipStream_t;
+ *    NULL means the null stream) and no call synchronises with the device,
+ *    except that tp_shard_load_weights, tp_shard_reserve, tp_kv_create and
+ *    the destroy calls may allocate or free device memory.
+ *  - Errors: argument and state errors are detected on the host before any
+ *    device work is enqueued and leave no side effects.  A failed HIP call
+ *    returns TP_E_HIP; tp_status_string() then also reports the HIP error.
+ *  - Handles are not thread-safe: use one handle from one host thread and
+ *    one stream at a time.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TP_OK          0
+#define TP_E_ARG      -1   /* bad pointer, size, layout or unsupported shape */
+#define TP_E_DIVIDE   -2   /* heads, kv_heads or ffn not divisible by tp_degree, or tp_degree > heads */
+#define TP_E_RANK     -3   /* rank outside [0, tp_degree) */
+#define TP_E_NOMEM    -4   /* device or host allocation failed */
+#define TP_E_HIP      -5   /* a HIP runtime call or kernel launch failed */
+#define TP_E_KV_FULL  -6   /* the KV cache has no room for the tokens asked for */
+#define TP_E_STATE    -7   /* call out of order (e.g. forward before weights are loaded) */
+
+/* element types */
+#define TP_F32   0
+#define TP_BF16  1
+
+/* stages of a shard's forward pass */
+#define TP_STAGE_ATTN  0
+#define TP_STAGE_MLP   1
+
+/* FFN activation */
+#define TP_ACT_SWIGLU  0   /* act = SiLU(n W_gate^T) * (n W_up^T); three FFN matrices */
+#define TP_ACT_GELU    1   /* act = GELU_erf(n W_up^T); two FFN matrices (w_gate unused) */
+
+typedef struct tp_shard tp_shard;   /* opaque: one rank's packed weights + workspace */
+typedef struct tp_kv    tp_kv;      /* opaque: K/V cache of one rank's KV heads      */
+
+typedef struct {
+    int   dtype;        /* TP_BF16 or TP_F32                                  */
+    int   act;          /* TP_ACT_SWIGLU or TP_ACT_GELU                       */
+    int   rmsnorm;      /* 1: RMSNorm (gamma g1/g2) before each stage; 0: none */
+    float eps;          /* RMSNorm epsilon                                    */
+    int   rope;         /* 1: rotate-half RoPE on q and k; 0: none            */
+    float rope_theta;   /* RoPE base                                          */
+} tp_opts;
+
+/* Full, unsharded layer weights (device pointers, element type = dtype):
+ *   wq [heads*d, hidden], wk/wv [kv_heads*d, hidden], wo [hidden, heads*d],
+ *   w_gate/w_up [ffn, hidden], w_down [hidden, ffn], g1/g2 [hidden].
+ * Every rank is handed the same full weights and keeps only its slices
+ * (column blocks of wq/wk/wv/w_gate/w_up, row-parallel column blocks of
+ * wo/w_down).  w_gate is ignored for TP_ACT_GELU; g1/g2 for rmsnorm == 0. */
+typedef struct {
+    const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down, *g1, *g2;
+} tp_weights;
+
+/* tp_shard_create -- validate the partition and create rank `rank`'s shard
+ * of a layer split `tp_degree` ways.  Host-only: no device call is made.
+ * The split rules are the pages' (undercodenews post 110319, "the
+ * Original": degree <= heads, heads % degree == 0, ffn % degree == 0) plus
+ * kv_heads % degree == 0 so that KV heads split too (byteledger "Tensor
+ * Parallelism: Splitting One Layer Across GPUs": the KV cache is split).
+ * Violations return TP_E_DIVIDE; a rank outside [0, tp_degree) returns
+ * TP_E_RANK.  Kernel limits return TP_E_ARG: hidden % heads == 0,
+ * heads % kv_heads == 0, head_dim % 64 == 0 when rope, head_dim <= 128 and
+ * even, hidden % 64 == 0, (ffn / degree) % 64 == 0.
+ * opts == NULL selects {TP_BF16, TP_ACT_SWIGLU, rmsnorm 1, eps 1e-5, rope 1,
+ * theta 10000}.  *out receives the handle (host memory owned by the library). */
+int tp_shard_create(int hidden, int heads, int kv_heads, int ffn,
+                    int tp_degree, int rank, const tp_opts *opts,
+                    tp_shard **out);
+
+/* tp_shard_load_weights -- copy rank r's slices out of the full weights into
+ * library-owned device memory, in the layout the kernels read (Q/K/V rows
+ * of the rank's heads; gate/up rows of the rank's FFN columns interleaved
+ * in 32-row blocks; the matching column blocks of wo and w_down).  Enqueued
+ * on `stream`; the caller's weights may be freed once the stream has
+ * drained.  May be called again to replace the weights. */
+int tp_shard_load_weights(tp_shard *s, const tp_weights *full, void *stream);
+
+/* tp_shard_reserve -- pre-size the workspace for calls of up to
+ * `max_tokens` = batch * seq tokens (and decode batches up to that size),
+ * so that later forward calls allocate nothing.  Forward calls grow the
+ * workspace on demand otherwise (which frees the old one and therefore
+ * waits for the device). */
+int tp_shard_reserve(tp_shard *s, long long max_tokens);
+
+/* tp_kv_create -- KV cache for this rank's kv_heads/t heads:
+ * K and V each [batch, kv_heads/t, max_seq, head_dim] in the shard's dtype,
+ * zero-filled, length 0. */
+int tp_kv_create(const tp_shard *s, int batch, int max_seq, tp_kv **out);
+
+/* tp_kv_view -- device pointers to the K and V arrays (layout above), e.g.
+ * to fill a cache with synthetic content.  Either output may be NULL. */
+int tp_kv_view(tp_kv *kv, void **k, void **v);
+
+/* tp_kv_set_len / tp_kv_get_len -- number of valid positions [0, len). */
+int tp_kv_set_len(tp_kv *kv, int len);
+int tp_kv_get_len(const tp_kv *kv, int *len);
+
+/* tp_shard_forward_prefill -- one stage over a prompt batch.
+ *   stage TP_STAGE_ATTN: x = layer input [batch, seq, hidden]; positions
+ *     0..seq-1; K/V of the rank's heads are written to kv positions
+ *     [0, seq) and the cache length becomes seq (kv may be NULL: K/V then
+ *     live in the workspace only).  Requires seq <= max_seq.
+ *   stage TP_STAGE_MLP: x = reduced h [batch, seq, hidden]; kv must be NULL.
+ *   partial [batch, seq, hidden] fp32 receives this rank's summand. */
+int tp_shard_forward_prefill(tp_shard *s, int stage, const void *x,
+                             int batch, int seq, tp_kv *kv, float *partial,
+                             void *stream);
+
+/* tp_shard_forward_decode -- one stage for one new token per sequence.
+ *   stage TP_STAGE_ATTN: x [batch, hidden] sits at position L = the cache
+ *     length; its k, v are appended at slot L, the query attends to
+ *     positions 0..L, and the cache length becomes L+1 (updated on the
+ *     host when the call returns).  TP_E_KV_FULL if L == max_seq; batch
+ *     must equal the cache's batch.
+ *   stage TP_STAGE_MLP: x = reduced h [batch, hidden]; kv must be NULL.
+ *   partial [batch, hidden] fp32 receives this rank's summand. */
+int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
+                            tp_kv *kv, float *partial, void *stream);
+
+/* tp_partial_reduce -- the all-reduce's arithmetic on one device:
+ *   out[i] = (sum_{r=0..t-1} partials[r][i]) + residual[i]
+ * summed in fp32 in rank order, then stored as out_dtype (TP_BF16 rounds to
+ * nearest even).  `partials` is a HOST array of t device pointers, each to
+ * n fp32 values; residual and out hold n elements of out_dtype (residual
+ * may be NULL for none; out may alias residual).  1 <= t <= 64; a NULL
+ * entry (a lost rank) returns TP_E_ARG. */
+int tp_partial_reduce(const float *const *partials, int t,
+                      const void *residual, void *out, long long n,
+                      int out_dtype, void *stream);
+
+/* tp_shard_debug_view -- device address of a workspace tensor from the last
+ * forward call, for diagnostics: which = 0 attention output o
+ * [tokens, heads/t * d]; 1 FFN activation act [tokens, ffn/t]; 2 the
+ * normalised stage input [tokens, hidden].  The contents are valid until
+ * the next forward call on this shard. */
+int tp_shard_debug_view(tp_shard *s, int which, void **ptr);
+
+void tp_shard_destroy(tp_shard *s);
+void tp_kv_destroy(tp_kv *kv);
+
+/* tp_status_string -- static text for a status code; for TP_E_HIP it names
+ * the last HIP error seen by this library (thread-local). */
+const char *tp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_SHARD_H */

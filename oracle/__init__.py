@@ -1,0 +1,17 @@
+"""CPU oracle for one rank's shard of a tensor-parallel transformer layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) may import, call or link anything in this package; only
+the test-suite, the smoke check and the CPU-baseline leg of the benchmark do.
+
+Two independent implementations live here:
+
+* ``oracle.layer``  -- NumPy float64, whole-tensor operations (matmul as the
+  only library primitive), with optional bf16 storage-point mirroring.
+* ``oracle.brute``  -- pure-Python scalar loops for tiny shapes, written
+  separately, used only to pin ``oracle.layer``.
+
+Neither shares any code with the GPU path.
+"""
+
+from . import layer, brute  # noqa: F401
