@@ -25,8 +25,10 @@
  *
  * Conventions for every call:
  *  - Device pointers are HIP device addresses on the current device; host
- *    pointers are marked "host".  Tensors are dense row-major, innermost
- *    dimension last.  Weight matrices are stored [out, in].
+ *    pointers are marked "host".  Activation, partial, residual and output
+ *    pointers must be 16-byte aligned (TP_E_ARG otherwise).  Tensors are
+ *    dense row-major, innermost dimension last.  Weight matrices are stored
+ *    [out, in].
  *  - Element type: TP_BF16 (bfloat16 storage, fp32 arithmetic) or TP_F32,
  *    chosen at create time for activations, weights, KV cache and outputs.
  *    Partial sums are always fp32.
@@ -103,8 +105,8 @@ typedef struct {
  * Parallelism: Splitting One Layer Across GPUs": the KV cache is split).
  * Violations return TP_E_DIVIDE; a rank outside [0, tp_degree) returns
  * TP_E_RANK.  Kernel limits return TP_E_ARG: hidden % heads == 0,
- * heads % kv_heads == 0, head_dim % 64 == 0 when rope, head_dim <= 128 and
- * even, hidden % 64 == 0, (ffn / degree) % 64 == 0.
+ * heads % kv_heads == 0, head_dim = hidden/heads in {64, 128},
+ * hidden % 64 == 0, (ffn / degree) % 64 == 0.
  * opts == NULL selects {TP_BF16, TP_ACT_SWIGLU, rmsnorm 1, eps 1e-5, rope 1,
  * theta 10000}.  *out receives the handle (host memory owned by the library). */
 int tp_shard_create(int hidden, int heads, int kv_heads, int ffn,
@@ -128,7 +130,7 @@ int tp_shard_reserve(tp_shard *s, long long max_tokens);
 
 /* tp_kv_create -- KV cache for this rank's kv_heads/t heads:
  * K and V each [batch, kv_heads/t, max_seq, head_dim] in the shard's dtype,
- * zero-filled, length 0. */
+ * zero-filled, length 0.  TP_F32 caches hold at most 16000 positions. */
 int tp_kv_create(const tp_shard *s, int batch, int max_seq, tp_kv **out);
 
 /* tp_kv_view -- device pointers to the K and V arrays (layout above), e.g.
@@ -167,7 +169,8 @@ int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
  * nearest even).  `partials` is a HOST array of t device pointers, each to
  * n fp32 values; residual and out hold n elements of out_dtype (residual
  * may be NULL for none; out may alias residual).  1 <= t <= 64; a NULL
- * entry (a lost rank) returns TP_E_ARG. */
+ * entry (a lost rank) returns TP_E_ARG.  n == 0 returns TP_OK and touches
+ * no pointer. */
 int tp_partial_reduce(const float *const *partials, int t,
                       const void *residual, void *out, long long n,
                       int out_dtype, void *stream);
@@ -178,6 +181,13 @@ int tp_partial_reduce(const float *const *partials, int t,
  * normalised stage input [tokens, hidden].  The contents are valid until
  * the next forward call on this shard. */
 int tp_shard_debug_view(tp_shard *s, int which, void **ptr);
+
+/* tp_tune_set_gemm_config -- tuning hook: force the projection GEMM's tile
+ * configuration (0..3: 256x256, 256x128, 128x128, 128x256 output tiles) for
+ * every later call in this process, or -1 to restore the shape-based choice.
+ * Configurations a kernel variant cannot use are skipped.  TP_E_ARG if out
+ * of range. */
+int tp_tune_set_gemm_config(int cfg);
 
 void tp_shard_destroy(tp_shard *s);
 void tp_kv_destroy(tp_kv *kv);

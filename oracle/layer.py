@@ -315,3 +315,30 @@ def decode_attn_stage(x_new, k_cache, v_cache, W, spec: Spec, t: int = 1, r: int
     partial = out_proj_rank(o, W, spec, t, r)[:, 0, :]
     return {"n1": n1[:, 0, :], "q": q[:, :, 0, :], "k_new": k[:, :, 0, :],
             "v_new": v[:, :, 0, :], "o": o[:, :, 0, :], "partial": partial}
+
+
+def attn_stage_rows(x, W, spec: Spec, t: int, r: int, rows):
+    """The prefill ATTN stage of rank r evaluated only at the token rows
+    ``rows`` (indices into the sequence) of every batch element: the same
+    definition as ``attn_stage``, restricted so that large layers stay
+    checkable.  Row i needs the keys and values of tokens 0..i, so those are
+    computed for the prefix up to the largest requested row.
+
+    Returns {"o": [B, H_l, len(rows), d], "partial": [B, len(rows), hidden],
+    "k", "v": [B, Hkv_l, max(rows)+1, d]}."""
+    x = np.asarray(x, np.float64)
+    rows = np.asarray(rows)
+    last = int(rows.max()) + 1
+    pos = np.arange(last)
+    n1 = norm1(x[:, :last], W, spec)
+    _, k, v = qkv_rank(n1, W, spec, t, r, pos)
+    q, _, _ = qkv_rank(n1[:, rows], W, spec, t, r, rows)
+    o = _store(spec, attention(q, k, v, rows, pos))
+    partial = out_proj_rank(o, W, spec, t, r)
+    return {"o": o, "partial": partial, "k": k, "v": v}
+
+
+def mlp_stage_rows(h, W, spec: Spec, t: int, r: int, rows):
+    """The MLP stage of rank r at the token rows ``rows`` only (rows are
+    independent in this stage)."""
+    return mlp_stage(np.asarray(h)[:, rows], W, spec, t, r)

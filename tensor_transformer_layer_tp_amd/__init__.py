@@ -1,0 +1,252 @@
+"""One rank's shard of a tensor-parallel transformer layer on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libtpshard.so`` (include/tp_shard.h):
+argument checking and marshalling only.  Every step of the layer runs in the
+library's HIP kernels; PyTorch supplies device memory and streams.
+
+    shard = Shard(4096, 32, 32, 11008, tp=2, rank=0)      # bf16, SwiGLU, RMSNorm, RoPE
+    shard.load_weights(full_weights)                      # dict of FULL device tensors
+    kv = shard.kv_cache(batch, max_seq)
+    pa = shard.prefill(ATTN, x, kv)                       # fp32 partial [B, S, h]
+    h = partial_reduce([pa, *other_ranks], residual=x)    # h = x + sum of partials
+    pm = shard.prefill(MLP, h)
+    y = partial_reduce([pm, *other_ranks], residual=h)
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+from . import _native as N
+from ._native import (TP_ACT_GELU, TP_ACT_SWIGLU, TP_BF16, TP_F32, TPError, TP_E_ARG, TP_E_DIVIDE,  # noqa: F401
+                      TP_E_HIP, TP_E_KV_FULL, TP_E_NOMEM, TP_E_RANK, TP_E_STATE, TP_OK)
+
+ATTN = N.TP_STAGE_ATTN
+MLP = N.TP_STAGE_MLP
+
+_DT = {"bf16": (N.TP_BF16, torch.bfloat16), "f32": (N.TP_F32, torch.float32)}
+
+
+def _stream(stream) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> C.c_void_p:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return C.c_void_p(t.data_ptr())
+
+
+_hip = None
+
+
+def _memcpy_d2d(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
+    """Device-to-device copy on the stream (hipMemcpyAsync of the HIP runtime
+    torch already loaded)."""
+    global _hip
+    if _hip is None:
+        _hip = C.CDLL("libamdhip64.so.7")
+        _hip.hipMemcpyAsync.restype = C.c_int
+        _hip.hipMemcpyAsync.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+    err = _hip.hipMemcpyAsync(C.c_void_p(dst_ptr), C.c_void_p(src_ptr), nbytes, 3, _stream(stream))
+    if err != 0:
+        raise RuntimeError(f"hipMemcpyAsync failed with HIP error {err}")
+
+
+class KVCache:
+    """K/V cache of one rank's KV heads: K and V [batch, kv_heads/t, max_seq, d]."""
+
+    def __init__(self, shard: "Shard", batch: int, max_seq: int):
+        h = C.c_void_p()
+        N.check(N.lib().tp_kv_create(shard._h, batch, max_seq, C.byref(h)), "tp_kv_create")
+        self._h = h
+        self.shard = shard
+        self.batch, self.max_seq = batch, max_seq
+        self.shape = (batch, shard.kv_local, max_seq, shard.head_dim)
+        k, v = C.c_void_p(), C.c_void_p()
+        N.check(N.lib().tp_kv_view(h, C.byref(k), C.byref(v)), "tp_kv_view")
+        self._k, self._v = k.value, v.value
+
+    @property
+    def nbytes(self) -> int:
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n * self.shard.elem_size
+
+    @property
+    def length(self) -> int:
+        n = C.c_int()
+        N.check(N.lib().tp_kv_get_len(self._h, C.byref(n)), "tp_kv_get_len")
+        return n.value
+
+    @length.setter
+    def length(self, n: int) -> None:
+        N.check(N.lib().tp_kv_set_len(self._h, int(n)), "tp_kv_set_len")
+
+    def write(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        """Copy whole caches in (device tensors of the cache's shape and dtype)."""
+        for name, src, dst in (("k", k, self._k), ("v", v, self._v)):
+            _dev(src, name, self.shard.torch_dtype, self.shape)
+            _memcpy_d2d(dst, src.data_ptr(), self.nbytes, stream)
+
+    def read(self, stream=None):
+        """Copies of the K and V arrays as device tensors."""
+        out = []
+        for src in (self._k, self._v):
+            t = torch.empty(self.shape, dtype=self.shard.torch_dtype, device="cuda")
+            _memcpy_d2d(t.data_ptr(), src, self.nbytes, stream)
+            out.append(t)
+        return tuple(out)
+
+    def close(self) -> None:
+        if self._h:
+            N.lib().tp_kv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Shard:
+    """Rank ``rank`` of a layer split ``tp`` ways."""
+
+    def __init__(self, hidden: int, heads: int, kv_heads: int, ffn: int, tp: int = 1, rank: int = 0, *,
+                 dtype: str = "bf16", act: str = "swiglu", rmsnorm: bool = True, eps: float = 1e-5,
+                 rope: bool = True, rope_theta: float = 10000.0):
+        if dtype not in _DT:
+            raise ValueError("dtype must be 'bf16' or 'f32'")
+        if act not in ("swiglu", "gelu"):
+            raise ValueError("act must be 'swiglu' or 'gelu'")
+        code, tdt = _DT[dtype]
+        opts = N.tp_opts(code, N.TP_ACT_SWIGLU if act == "swiglu" else N.TP_ACT_GELU, int(rmsnorm), eps,
+                         int(rope), rope_theta)
+        h = C.c_void_p()
+        N.check(N.lib().tp_shard_create(hidden, heads, kv_heads, ffn, tp, rank, C.byref(opts), C.byref(h)),
+                "tp_shard_create")
+        self._h = h
+        self.hidden, self.heads, self.kv_heads, self.ffn, self.tp, self.rank = hidden, heads, kv_heads, ffn, tp, rank
+        self.dtype, self.torch_dtype, self.elem_size = dtype, tdt, (2 if dtype == "bf16" else 4)
+        self.act, self.rmsnorm, self.rope = act, rmsnorm, rope
+        self.head_dim = hidden // heads
+        self.heads_local = heads // tp
+        self.kv_local = kv_heads // tp
+        self.ffn_local = ffn // tp
+
+    # ---- setup
+    def load_weights(self, W: dict, stream=None) -> None:
+        """W: FULL unsharded weights as device tensors (wq, wk, wv, wo, w_gate
+        for SwiGLU, w_up, w_down, g1/g2 with RMSNorm).  Waits for the copy."""
+        d, h = self.head_dim, self.hidden
+        shapes = {"wq": (self.heads * d, h), "wk": (self.kv_heads * d, h), "wv": (self.kv_heads * d, h),
+                  "wo": (h, self.heads * d), "w_up": (self.ffn, h), "w_down": (h, self.ffn)}
+        if self.act == "swiglu":
+            shapes["w_gate"] = (self.ffn, h)
+        if self.rmsnorm:
+            shapes["g1"] = (h,)
+            shapes["g2"] = (h,)
+        w = N.tp_weights()
+        for name, shp in shapes.items():
+            if name not in W:
+                raise ValueError(f"missing weight {name}")
+            setattr(w, name, _dev(W[name], name, self.torch_dtype, shp))
+        N.check(N.lib().tp_shard_load_weights(self._h, C.byref(w), _stream(stream)), "tp_shard_load_weights")
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
+
+    def reserve(self, max_tokens: int) -> None:
+        N.check(N.lib().tp_shard_reserve(self._h, int(max_tokens)), "tp_shard_reserve")
+
+    def kv_cache(self, batch: int, max_seq: int) -> KVCache:
+        return KVCache(self, batch, max_seq)
+
+    # ---- forward
+    def prefill(self, stage: int, x: torch.Tensor, kv: KVCache | None = None, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+        """x [B, S, hidden] (layer input for ATTN, reduced h for MLP) ->
+        this rank's fp32 partial [B, S, hidden]."""
+        if x.dim() != 3 or x.shape[2] != self.hidden:
+            raise ValueError("x must be [batch, seq, hidden]")
+        B, S = int(x.shape[0]), int(x.shape[1])
+        if out is None:
+            out = torch.empty((B, S, self.hidden), dtype=torch.float32, device=x.device)
+        N.check(N.lib().tp_shard_forward_prefill(
+            self._h, stage, _dev(x, "x", self.torch_dtype), B, S, kv._h if kv is not None else None,
+            _dev(out, "partial", torch.float32, (B, S, self.hidden)), _stream(stream)), "tp_shard_forward_prefill")
+        return out
+
+    def decode(self, stage: int, x: torch.Tensor, kv: KVCache | None = None, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+        """x [B, hidden] (one token per sequence) -> fp32 partial [B, hidden]."""
+        if x.dim() != 2 or x.shape[1] != self.hidden:
+            raise ValueError("x must be [batch, hidden]")
+        B = int(x.shape[0])
+        if out is None:
+            out = torch.empty((B, self.hidden), dtype=torch.float32, device=x.device)
+        N.check(N.lib().tp_shard_forward_decode(
+            self._h, stage, _dev(x, "x", self.torch_dtype), B, kv._h if kv is not None else None,
+            _dev(out, "partial", torch.float32, (B, self.hidden)), _stream(stream)), "tp_shard_forward_decode")
+        return out
+
+    def debug_tensor(self, which: str, shape, stream=None) -> torch.Tensor:
+        """Copy of a workspace tensor of the last call: 'o' [tokens, heads/t*d],
+        'act' [tokens, ffn/t] or 'n' [tokens, hidden]."""
+        code = {"o": 0, "act": 1, "n": 2}[which]
+        p = C.c_void_p()
+        N.check(N.lib().tp_shard_debug_view(self._h, code, C.byref(p)), "tp_shard_debug_view")
+        t = torch.empty(shape, dtype=self.torch_dtype, device="cuda")
+        _memcpy_d2d(t.data_ptr(), p.value, t.numel() * self.elem_size, stream)
+        return t
+
+    def close(self) -> None:
+        if self._h:
+            N.lib().tp_shard_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def partial_reduce(partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   dtype: str | None = None, stream=None) -> torch.Tensor:
+    """out = (sum of fp32 partials in rank order) + residual, stored as the
+    residual's dtype (or ``dtype``)."""
+    partials = list(partials)
+    if not partials:
+        raise ValueError("need at least one partial")
+    shape = tuple(partials[0].shape)
+    n = partials[0].numel()
+    ptrs = (C.c_void_p * len(partials))(*[_dev(p, f"partial[{i}]", torch.float32, shape).value
+                                          for i, p in enumerate(partials)])
+    if dtype is None:
+        dtype = "bf16" if residual is None or residual.dtype == torch.bfloat16 else "f32"
+    code, tdt = _DT[dtype]
+    if residual is not None:
+        _dev(residual, "residual", tdt)
+        if residual.numel() != n:
+            raise ValueError("residual size differs from the partials")
+    if out is None:
+        out = torch.empty(shape, dtype=tdt, device=partials[0].device)
+    N.check(N.lib().tp_partial_reduce(ptrs, len(partials), C.c_void_p(residual.data_ptr()) if residual is not None
+                                      else None, _dev(out, "out", tdt), n, code, _stream(stream)),
+            "tp_partial_reduce")
+    return out
+
+
+def set_gemm_config(cfg: int) -> None:
+    """Tuning hook: force a projection tile configuration (-1 = automatic)."""
+    N.check(N.lib().tp_tune_set_gemm_config(int(cfg)), "tp_tune_set_gemm_config")

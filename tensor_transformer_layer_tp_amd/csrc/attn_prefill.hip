@@ -1,0 +1,194 @@
+// Causal attention over one rank's own heads (prefill), bf16 MFMA, fp32 softmax.
+//
+// Each rank attends locally over the heads it owns; no other rank's data is
+// needed (undercodenews post 110319 on tensor parallelism, sections "the
+// Original" and "What Undercode Say": heads are independent, so the
+// column-parallel split of Q/K/V needs no communication inside attention).
+//
+// Work-group = 4 waves = 128 queries of one (batch, head); each wave owns 32
+// queries.  Keys stream through LDS in blocks of 64.  The wave computes the
+// transposed score tile S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K block as
+// the A operand from LDS, the wave's Q fragment held in registers as the B
+// operand), so that every lane owns ONE query column: the online-softmax
+// row max / row sum is a per-lane reduction over 16 registers plus one
+// exchange between the two 32-lane halves.  The probabilities are then fed
+// straight from the accumulator registers as the B operand of
+// O^T += V^T P^T; V is stored transposed in LDS with its keys permuted to
+// match the accumulator's register order, so each A-operand fragment is one
+// 16-byte LDS read.  Grouped-query attention maps query head j to KV head
+// j / (Hl / Hkvl).
+#include "kernels.h"
+
+namespace tp {
+
+namespace {
+
+constexpr int BQ = 128, BKV = 64;
+
+// LDS position of key k (0..63) inside a transposed V row: keys are ordered
+// to match the PV MFMA operand, (16j + 4h + p%4 + 8(p/4)) -> 16j + 8h + p.
+__device__ __forceinline__ int vt_pos(int k) {
+    const int j = k >> 4, w = k & 15;
+    return (j << 4) + (((w >> 2) & 1) << 3) + (w & 3) + ((w >> 3) << 2);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                           const bf16* __restrict__ V, bf16* __restrict__ O,
+                                                           int hl, int kvl, int S, int ld_seq, float scale_log2) {
+    constexpr int KC = D / 8;        // 16-byte chunks per K row
+    constexpr int NT = D / 32;       // O^T tiles (32 dims each)
+    constexpr int KSTEPS = D / 16;   // k16 steps of the QK^T contraction
+    __shared__ __attribute__((aligned(16))) bf16 sK[BKV * D];
+    __shared__ __attribute__((aligned(16))) bf16 sVt[D * BKV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, col = lane & 31;
+    const int nqb = (S + BQ - 1) / BQ;
+    const int qb = nqb - 1 - (int)blockIdx.x;  // longest (latest) query blocks first
+    const int head = blockIdx.y, b = blockIdx.z;
+    const int kvh = head / (hl / kvl);
+    const int q0 = qb * BQ + wave * 32;
+    const int qme = q0 + col;                  // this lane's query
+
+    const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
+    const bf16* Vb = V + ((long long)b * kvl + kvh) * ld_seq * D;
+
+    bf16x8 qf[KSTEPS];
+    {
+        const int qrow = min(qme, S - 1);
+        const bf16* qp = Q + (((long long)b * hl + head) * S + qrow) * D + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+    }
+
+    f32x16 oacc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) oacc[i] = (f32x16){};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int kv_end = min(S, qb * BQ + BQ);
+    const int nkb = (kv_end + BKV - 1) / BKV;
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int k0 = kb * BKV;
+        __syncthreads();
+        // K block -> LDS [key][dim], chunk swizzled by key
+#pragma unroll
+        for (int i = 0; i < BKV * KC / 256; ++i) {
+            const int idx = tid + 256 * i;
+            const int key = idx / KC, dc = idx % KC;
+            const int gk = min(k0 + key, S - 1);
+            const bf16x8 v = *(const bf16x8*)(Kb + (long long)gk * D + dc * 8);
+            *(bf16x8*)(sK + key * D + ((dc ^ (key & (KC - 1))) << 3)) = v;
+        }
+        // V block -> LDS transposed [dim][permuted key], two keys per 32-bit store
+#pragma unroll
+        for (int i = 0; i < (BKV / 2) * KC / 256; ++i) {
+            const int idx = tid + 256 * i;
+            const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
+            const int g0 = min(k0 + 2 * a, S - 1), g1 = min(k0 + 2 * a + 1, S - 1);
+            const u16x8 v0 = *(const u16x8*)(Vb + (long long)g0 * D + dc * 8);
+            const u16x8 v1 = *(const u16x8*)(Vb + (long long)g1 * D + dc * 8);
+            const int p = vt_pos(2 * a);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int dim = dc * 8 + e;
+                const int off = dim * BKV + ((((p >> 3) ^ (dim & 7)) << 3) | (p & 7));
+                *(uint32_t*)(sVt + off) = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+            }
+        }
+        __syncthreads();
+        if (k0 > q0 + 31) continue;  // every key of this block is after every query of the wave
+
+        // S^T tile: keys (32t + row) x this wave's 32 queries
+        f32x16 st[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[t] = (f32x16){};
+            const int krow = 32 * t + col;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const bf16x8 a = *(const bf16x8*)(sK + krow * D + (((2 * kk + h) ^ (krow & (KC - 1))) << 3));
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[t], 0, 0, 0);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                float s = st[t][r] * scale_log2;
+                s = key > qme ? -INFINITY : s;
+                st[t][r] = s;
+                mx = fmaxf(mx, s);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2f(st[t][r] - m_new);
+                st[t][r] = p;
+                lsum += p;
+            }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) oacc[i] *= alpha;
+
+        // O^T[dim][q] += V^T[dim][key] P^T[key][q], 16 keys per MFMA
+#pragma unroll
+        for (int j = 0; j < BKV / 16; ++j) {
+            bf16x8 pb;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) pb[p] = f2bf(st[j >> 1][8 * (j & 1) + p]);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const int dim = 32 * i + col;
+                const bf16x8 a = *(const bf16x8*)(sVt + dim * BKV + ((((2 * j + h) ^ (dim & 7))) << 3));
+                oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
+            }
+        }
+    }
+
+    // normalise and store through LDS so that the global writes are whole rows
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.f / l_tot;
+    __syncthreads();
+    bf16* sO = (tid < 128 ? sK : sVt) + (wave & 1) * 32 * D;  // 32 queries x D per wave
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int dim = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            sO[col * D + dim] = f2bf(oacc[i][r] * inv);
+        }
+    __syncthreads();
+    const long long ldo = (long long)hl * D;
+#pragma unroll
+    for (int i = 0; i < 32 * KC / 64; ++i) {
+        const int idx = lane + 64 * i;
+        const int qr = idx / KC, dc = idx % KC;
+        const int q = q0 + qr;
+        if (q < S) *(bf16x8*)(O + ((long long)b * S + q) * ldo + head * D + dc * 8) = *(const bf16x8*)(sO + qr * D + dc * 8);
+    }
+}
+
+}  // namespace
+
+void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl, int S,
+                       int ld_seq, int d, hipStream_t st) {
+    if (B <= 0 || S <= 0) return;
+    dim3 grid((S + BQ - 1) / BQ, hl, B);
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    if (d == 128)
+        hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq, scale_log2);
+    else
+        hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq, scale_log2);
+}
+
+}  // namespace tp

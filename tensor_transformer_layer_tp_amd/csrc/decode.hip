@@ -1,0 +1,364 @@
+// Decode (one new token per sequence): weight-streaming GEMV and split-KV
+// attention over the rank's KV-cache heads.
+//
+// Decode is a sequence of small steps whose local products are too small to
+// keep a GPU busy (clusterbid "When Tensor Parallelism Makes a Small Model
+// Slower"): at batch 1..8 every projection reads its weight slice once and
+// does ~1 FLOP per byte, so these kernels are organised around streaming
+// the weights from HBM with 16-byte coalesced loads, not around MFMA.
+#include "kernels.h"
+
+namespace tp {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// GEMV: y[b, n] = sum_k W[n, k] * in[b, k] for b < NB, optionally with the
+// RMSNorm of x fused in front (in = bf16(x * rsqrt(mean x^2 + eps) * gamma)).
+//
+// A work-group owns P row pairs (rows r and r + 32 of one 64-row group of the
+// packed weight; see packed_to_dim) so that the RoPE / SwiGLU partners meet in
+// one work-group.  All 256 threads sweep K together in 16-byte chunks (each
+// row is read as contiguous 4 KB bursts), then the per-thread sums are
+// reduced across the work-group.
+template <int NB, int P, int MODE, bool NORM>
+__global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, const bf16* __restrict__ gamma,
+                                                   float eps, const bf16* __restrict__ W, int N, int K,
+                                                   Epilogue epi) {
+    constexpr int R = 2 * P;
+    __shared__ float red[4][R * NB];
+    __shared__ float rs_s[NB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per_group = 32 / P;
+    const int grp = blockIdx.x / per_group, sub = blockIdx.x % per_group;
+    const int rbase = 64 * grp + P * sub;   // rows rbase + e and rbase + 32 + e, e < P
+    const int KC = K >> 3;
+
+    float rs[NB];
+    if constexpr (NORM) {
+        float ss[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+        for (int c = tid; c < KC; c += 256) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const u16x8 v = *(const u16x8*)(x + (long long)b * K + c * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = bfbits2f(v[e]);
+                    ss[b] += f * f;
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float s = wave_sum(ss[b]);
+            if (lane == 0) red[wave][b] = s;
+        }
+        __syncthreads();
+        if (tid < NB) rs_s[tid] = rsqrtf((red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) / (float)K + eps);
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) rs[b] = rs_s[b];
+    }
+
+    float acc[R][NB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+    const bf16* wrow[R];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        wrow[e] = W + (long long)(rbase + e) * K;
+        wrow[P + e] = W + (long long)(rbase + 32 + e) * K;
+    }
+
+    for (int c = tid; c < KC; c += 256) {
+        u16x8 wv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) wv[r] = *(const u16x8*)(wrow[r] + c * 8);
+        float xin[NB][8];
+        u16x8 gv;
+        if constexpr (NORM) gv = *(const u16x8*)(gamma + c * 8);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u16x8 xv = *(const u16x8*)(x + (long long)b * K + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float f = bfbits2f(xv[e]);
+                if constexpr (NORM) f = round_bf(f * rs[b] * bfbits2f(gv[e]));
+                xin[b][e] = f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float w = bfbits2f(wv[r][e]);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[r][b] += w * xin[b][e];
+            }
+    }
+
+    // reduce: wave sums, then across the 4 waves
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float s = wave_sum(acc[r][b]);
+            if (lane == 0) red[wave][r * NB + b] = s;
+        }
+    __syncthreads();
+    if (tid >= P * NB) return;
+    const int e = tid / NB, b = tid % NB;
+    const float y1 = red[0][e * NB + b] + red[1][e * NB + b] + red[2][e * NB + b] + red[3][e * NB + b];
+    const int j2 = (P + e) * NB + b;
+    const float y2 = red[0][j2] + red[1][j2] + red[2][j2] + red[3][j2];
+    const int r1 = rbase + e, r2 = rbase + 32 + e;
+
+    if constexpr (MODE == EPI_F32) {
+        float* o = (float*)epi.out + (long long)b * epi.ldo;
+        o[r1] = y1;
+        o[r2] = y2;
+    } else if constexpr (MODE == EPI_STORE || MODE == EPI_GELU) {
+        bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
+        o[r1] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y1) : y1);
+        o[r2] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y2) : y2);
+    } else if constexpr (MODE == EPI_SWIGLU) {
+        bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
+        o[(r1 >> 6) * 32 + (r1 & 31)] = f2bf(silu_f(y1) * y2);
+    } else {  // EPI_QKV, one token per sequence at position pos0
+        const QKVDest& q = epi.qkv;
+        const int d = q.d, half = d >> 1;
+        const int qcols = q.hl * d, kcols = q.kvl * d;
+        const int region = r1 < qcols ? 0 : (r1 < qcols + kcols ? 1 : 2);
+        const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
+        const int head = (r1 - base) / d;
+        const int i1 = 32 * (((r1 - base) % d) >> 6) + (r1 & 31);
+        float o1 = y1, o2 = y2;
+        if (region < 2 && q.rope_cos != nullptr) {
+            const float c = q.rope_cos[(long long)q.pos0 * half + i1];
+            const float s = q.rope_sin[(long long)q.pos0 * half + i1];
+            o1 = y1 * c - y2 * s;
+            o2 = y2 * c + y1 * s;
+        }
+        bf16* dst = region == 0 ? (bf16*)q.q + ((long long)b * q.hl + head) * d
+                                : (bf16*)(region == 1 ? q.k : q.v) +
+                                      (((long long)b * q.kvl + head) * q.ld_seq + q.pos0) * d;
+        dst[i1] = f2bf(o1);
+        dst[i1 + half] = f2bf(o2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV decode attention.  Work-group (chunk, kv head, batch) scores CH
+// cached positions for every query head of the GQA group, and writes the
+// chunk's running max, sum and unnormalised output; a second kernel merges
+// the chunks.
+constexpr int CH = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict__ q, const bf16* __restrict__ K,
+                                                         const bf16* __restrict__ V, float* __restrict__ scr,
+                                                         int hl, int kvl, int len, int ld_seq, float scale_log2) {
+    const int G = hl / kvl;
+    const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int nchunks = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    extern __shared__ float sm[];
+    float* sq = sm;                 // [G][D]
+    float* ss = sm + G * D;         // [G][CH]
+    const int k0 = chunk * CH;
+
+    for (int i = tid; i < G * D; i += 256) {
+        const int g = i / D, dd = i % D;
+        sq[i] = bf2f(q[((long long)b * hl + kvh * G + g) * D + dd]);
+    }
+    __syncthreads();
+
+    const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
+    const bf16* Vb = V + ((long long)b * kvl + kvh) * ld_seq * D;
+    // scores: thread = (key, quarter of the head dim)
+    {
+        constexpr int QD = D / 4;
+        const int key = tid >> 2, seg = tid & 3;
+        const int gk = min(k0 + key, len - 1);
+        float kf[QD];
+#pragma unroll
+        for (int c = 0; c < QD / 8; ++c) {
+            const u16x8 v = *(const u16x8*)(Kb + (long long)gk * D + seg * QD + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[c * 8 + e] = bfbits2f(v[e]);
+        }
+        for (int g = 0; g < G; ++g) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < QD; ++e) s += kf[e] * sq[g * D + seg * QD + e];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            if (seg == 0) ss[g * CH + key] = (k0 + key < len) ? s * scale_log2 : -INFINITY;
+        }
+    }
+    __syncthreads();
+    // softmax pieces per head: wave w handles heads w, w+4, ...
+    float* stat = scr + ((long long)b * hl + kvh * G) * nchunks * (D + 2);
+    for (int g = wave; g < G; g += 4) {
+        const float s = ss[g * CH + lane];
+        const float m = wave_max(s);
+        const float p = exp2f(s - m);
+        const float l = wave_sum(p);
+        ss[g * CH + lane] = p;
+        if (lane == 0) {
+            float* st = stat + ((long long)g * nchunks + chunk) * (D + 2);
+            st[D] = m;
+            st[D + 1] = l;
+        }
+    }
+    __syncthreads();
+    // o[g][dim] = sum_key p[g][key] V[key][dim]; thread = (dim chunk of 8, key group of 4)
+    {
+        constexpr int DC = D / 8;               // dim chunks
+        constexpr int KG = 256 / DC;            // key groups
+        constexpr int KPG = CH / KG;            // keys per group
+        const int dc = tid % DC, kg = tid / DC;
+        float vf[KPG][8];
+#pragma unroll
+        for (int i = 0; i < KPG; ++i) {
+            const int key = kg * KPG + i;
+            const int gk = min(k0 + key, len - 1);
+            const u16x8 v = *(const u16x8*)(Vb + (long long)gk * D + dc * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[i][e] = bfbits2f(v[e]);
+        }
+        __syncthreads();
+        float* part = sm;  // reuse: [KG][8] per head pass (scores stay in ss)
+        for (int g = 0; g < G; ++g) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < KPG; ++i) {
+                const float p = ss[g * CH + kg * KPG + i];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += p * vf[i][e];
+            }
+            // sum over key groups: thread (dc, kg) -> part[kg][dc*8+e]
+            float* pg = part + G * D + G * CH;  // scratch after sq and ss
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pg[kg * D + dc * 8 + e] = o[e];
+            __syncthreads();
+            if (tid < D) {
+                float a = 0.f;
+                for (int k = 0; k < KG; ++k) a += pg[k * D + tid];
+                stat[((long long)g * nchunks + chunk) * (D + 2) + tid] = a;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
+                                                         int hl, int nchunks) {
+    const int head = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+    const float* st = scr + ((long long)b * hl + head) * nchunks * (D + 2);
+    float M = -INFINITY;
+    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, st[c * (D + 2) + D]);
+    float L = 0.f, acc = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+        const float w = exp2f(st[c * (D + 2) + D] - M);
+        L += w * st[c * (D + 2) + D + 1];
+        acc += w * st[c * (D + 2) + dim];
+    }
+    O[((long long)b * hl + head) * D + dim] = f2bf(acc / L);
+}
+
+template <int NB, int P, bool NORM>
+void gemv_mode(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
+               hipStream_t st) {
+    dim3 g(N / (2 * P)), b(256);
+    switch (epi.mode) {
+        case EPI_F32: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_F32, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_QKV, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_SWIGLU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_GELU: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_GELU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        default: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_STORE, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+    }
+}
+
+template <int NB>
+void gemv_nb(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
+             hipStream_t st) {
+    // 4 rows per work-group when 8 would leave the GPU short of work-groups
+    const bool small = N / 8 < 512;
+    if (gamma) {
+        if (small) gemv_mode<NB, 2, true>(x, gamma, eps, W, N, K, epi, st);
+        else gemv_mode<NB, 4, true>(x, gamma, eps, W, N, K, epi, st);
+    } else {
+        if (small) gemv_mode<NB, 2, false>(x, gamma, eps, W, N, K, epi, st);
+        else gemv_mode<NB, 4, false>(x, gamma, eps, W, N, K, epi, st);
+    }
+}
+
+}  // namespace
+
+void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W, int N, int K,
+               const Epilogue& epi, hipStream_t st) {
+    switch (B) {
+        case 1: gemv_nb<1>(x, gamma, eps, W, N, K, epi, st); break;
+        case 2: gemv_nb<2>(x, gamma, eps, W, N, K, epi, st); break;
+        case 3: gemv_nb<3>(x, gamma, eps, W, N, K, epi, st); break;
+        case 4: gemv_nb<4>(x, gamma, eps, W, N, K, epi, st); break;
+        default: {
+            // batches above 4 run in slices of 4 rows (the caller keeps B <= 8)
+            for (int b0 = 0; b0 < B; b0 += 4) {
+                const int nb = B - b0 < 4 ? B - b0 : 4;
+                Epilogue e = epi;
+                if (epi.mode == EPI_QKV) {
+                    // slices of the batch: shift the q and cache bases by b0 sequences
+                    e.qkv.q = (bf16*)epi.qkv.q + (long long)b0 * epi.qkv.hl * epi.qkv.d;
+                    e.qkv.k = (bf16*)epi.qkv.k + (long long)b0 * epi.qkv.kvl * epi.qkv.ld_seq * epi.qkv.d;
+                    e.qkv.v = (bf16*)epi.qkv.v + (long long)b0 * epi.qkv.kvl * epi.qkv.ld_seq * epi.qkv.d;
+                } else if (epi.mode == EPI_F32) {
+                    e.out = (float*)epi.out + (long long)b0 * epi.ldo;
+                } else {
+                    e.out = (bf16*)epi.out + (long long)b0 * epi.ldo;
+                }
+                const bf16* xb = x + (long long)b0 * K;
+                switch (nb) {
+                    case 1: gemv_nb<1>(xb, gamma, eps, W, N, K, e, st); break;
+                    case 2: gemv_nb<2>(xb, gamma, eps, W, N, K, e, st); break;
+                    case 3: gemv_nb<3>(xb, gamma, eps, W, N, K, e, st); break;
+                    default: gemv_nb<4>(xb, gamma, eps, W, N, K, e, st); break;
+                }
+            }
+        }
+    }
+}
+
+size_t attn_decode_scratch_bytes(int B, int hl, int len) {
+    const int nchunks = (len + CH - 1) / CH;
+    return (size_t)B * hl * nchunks * (128 + 2) * sizeof(float);
+}
+
+void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
+                      int kvl, int len, int ld_seq, int d, hipStream_t st) {
+    const int nchunks = (len + CH - 1) / CH;
+    const int G = hl / kvl;
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    dim3 grid(nchunks, kvl, B);
+    // LDS: q [G][d], scores [G][CH], per-head partial sums [256/(d/8)][d]
+    const size_t lds = ((size_t)G * d + (size_t)G * CH + (size_t)(256 / (d / 8)) * d) * sizeof(float);
+    if (d == 128) {
+        hipLaunchKernelGGL(attn_decode_chunk<128>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len, ld_seq, scale_log2);
+        hipLaunchKernelGGL(attn_decode_combine<128>, dim3(hl, B), dim3(128), 0, st, scratch, O, hl, nchunks);
+    } else {
+        hipLaunchKernelGGL(attn_decode_chunk<64>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len, ld_seq, scale_log2);
+        hipLaunchKernelGGL(attn_decode_combine<64>, dim3(hl, B), dim3(64), 0, st, scratch, O, hl, nchunks);
+    }
+}
+
+}  // namespace tp

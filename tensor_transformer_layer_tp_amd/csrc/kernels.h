@@ -1,0 +1,76 @@
+// Internal launch API of the shard kernels (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+
+namespace tp {
+
+// What a projection does with its fp32 accumulator tile.
+enum EpiMode {
+    EPI_F32 = 0,     // out[m, n] = acc (fp32 partial sum of a row-parallel linear)
+    EPI_QKV = 1,     // rotary embedding on q/k, scatter q to [B,Hl,S,d], k/v to the cache
+    EPI_SWIGLU = 2,  // act[m, j] = SiLU(gate) * up, gate/up interleaved in 32-column blocks
+    EPI_GELU = 3,    // act[m, n] = GELU_erf(acc)
+    EPI_STORE = 4,   // out[m, n] = acc in the storage type
+};
+
+struct QKVDest {
+    int S;              // tokens per sequence in this call (1 for decode)
+    int pos0;           // position of token 0 (0 for prefill, L for decode)
+    int hl, kvl, d;     // local query heads, local kv heads, head dim
+    void* q;            // [B, hl, S, d]
+    void* k;            // [B, kvl, ld_seq, d], written at slots pos0 + s
+    void* v;
+    int ld_seq;         // cache capacity (positions)
+    const float* rope_cos;  // [max_pos, d/2] or nullptr (no rotary embedding)
+    const float* rope_sin;
+};
+
+struct Epilogue {
+    int mode;
+    void* out;          // F32: float*, others: element-type pointer
+    long long ldo;      // leading dimension of out, in elements
+    QKVDest qkv;
+};
+
+// Packed column layout shared by the projection kernels: for Q/K/V heads and
+// for the gate/up pair, every 64-row group of the packed weight holds two
+// 32-row halves that belong together: (dims i, i + d/2) of one head for the
+// rotary embedding, or (gate j, up j) for SwiGLU.  Packed row p of a head's
+// block maps to head dim:  g = p / 64, w = p % 64,
+//   dim = 32 g + w            (w < 32)
+//   dim = d/2 + 32 g + w - 32 (w >= 32).
+__host__ __device__ inline int packed_to_dim(int p, int d) {
+    int g = p >> 6, w = p & 63;
+    return w < 32 ? 32 * g + w : (d >> 1) + 32 * g + (w - 32);
+}
+
+// ---- bf16 path (gfx950 MFMA) ----
+void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M, int N, int K,
+               const Epilogue& epi, hipStream_t st);
+void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st);
+void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl,
+                       int S, int ld_seq, int d, hipStream_t st);
+void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W, int N, int K,
+               const Epilogue& epi, hipStream_t st);
+void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B,
+                      int hl, int kvl, int len, int ld_seq, int d, hipStream_t st);
+size_t attn_decode_scratch_bytes(int B, int hl, int len);
+
+// ---- fp32 path ----
+void gemm_f32(const float* A, long long lda, const float* B, long long ldb, int M, int N, int K,
+              const Epilogue& epi, hipStream_t st);
+void rmsnorm_f32(const float* x, const float* g, float* out, int rows, int n, float eps, hipStream_t st);
+void attn_f32(const float* Q, const float* K, const float* V, float* O, int B, int hl, int kvl, int Sq,
+              int q_pos0, int ld_seq, int d, hipStream_t st);
+
+// ---- shared ----
+void partial_reduce(const float* const* parts, int t, const void* residual, void* out, long long n,
+                    int bf16_out, hipStream_t st);
+void rope_table(float* cos_t, float* sin_t, int npos, int d, float theta, hipStream_t st);
+
+// tuning: -1 = heuristic, otherwise a fixed GEMM tile configuration index
+void set_gemm_config(int cfg);
+int gemm_config_count();
+
+}  // namespace tp

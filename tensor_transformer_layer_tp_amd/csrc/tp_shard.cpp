@@ -1,0 +1,557 @@
+// Host runtime and C ABI of one rank's tensor-parallel layer shard.
+//
+// Validation happens here, before any device call, so that every argument or
+// state error returns without side effects.  The partition rules are the
+// pages' (undercodenews post 110319 on tensor parallelism, section "the
+// Original": the degree may not exceed the head count; heads and FFN width
+// must divide by it), plus kv_heads % degree == 0 so that the KV heads --
+// and with them the KV cache (byteledger "Tensor Parallelism: Splitting One
+// Layer Across GPUs", "Interaction with the rest of serving") -- split too.
+#include "../../include/tp_shard.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "kernels.h"
+
+using namespace tp;
+
+struct tp_shard {
+    int hidden, heads, kv_heads, ffn, t, rank;
+    tp_opts o;
+    int d, hl, kvl, fl, nqkv, nup;
+    size_t esz;
+    int device;
+    bool loaded;
+    void *w_qkv, *w_o, *w_up, *w_down, *g1, *g2;
+    char* ws;
+    size_t ws_bytes;
+    float *rcos, *rsin;
+    int rope_npos;
+    // offsets of the last call's workspace tensors (debug view)
+    size_t off_n, off_o, off_act;
+};
+
+struct tp_kv {
+    int batch, max_seq, len;
+    int kvl, d;
+    size_t esz;
+    int dtype;
+    void *k, *v;
+};
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_fail(hipError_t e, const char* what) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s", what, hipGetErrorString(e));
+    return TP_E_HIP;
+}
+
+#define HIP_TRY(call)                                         \
+    do {                                                      \
+        hipError_t e_ = (call);                               \
+        if (e_ != hipSuccess) return hip_fail(e_, #call);     \
+    } while (0)
+
+#define LAUNCH_CHECK(what)                                    \
+    do {                                                      \
+        hipError_t e_ = hipGetLastError();                    \
+        if (e_ != hipSuccess) return hip_fail(e_, what);      \
+    } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int ensure_ws(tp_shard* s, size_t bytes) {
+    if (bytes <= s->ws_bytes) return TP_OK;
+    if (s->ws) {
+        hipError_t e = hipFree(s->ws);  // waits for work that may still use it
+        s->ws = nullptr;
+        s->ws_bytes = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    size_t b = (bytes + 255) & ~(size_t)255;
+    hipError_t e = hipMalloc((void**)&s->ws, b);
+    if (e != hipSuccess) {
+        s->ws = nullptr;
+        hip_fail(e, "hipMalloc(workspace)");
+        return TP_E_NOMEM;
+    }
+    s->ws_bytes = b;
+    return TP_OK;
+}
+
+int ensure_rope(tp_shard* s, int npos, hipStream_t st) {
+    if (!s->o.rope || npos <= s->rope_npos) return TP_OK;
+    int want = std::max(npos, std::max(2 * s->rope_npos, 4096));
+    if (s->rcos) {
+        hipError_t e1 = hipFree(s->rcos), e2 = hipFree(s->rsin);
+        s->rcos = s->rsin = nullptr;
+        s->rope_npos = 0;
+        if (e1 != hipSuccess) return hip_fail(e1, "hipFree(rope)");
+        if (e2 != hipSuccess) return hip_fail(e2, "hipFree(rope)");
+    }
+    size_t bytes = (size_t)want * (s->d / 2) * sizeof(float);
+    if (hipMalloc((void**)&s->rcos, bytes) != hipSuccess || hipMalloc((void**)&s->rsin, bytes) != hipSuccess) {
+        if (s->rcos) (void)hipFree(s->rcos);
+        s->rcos = s->rsin = nullptr;
+        return TP_E_NOMEM;
+    }
+    rope_table(s->rcos, s->rsin, want, s->d, s->o.rope_theta, st);
+    LAUNCH_CHECK("rope_table");
+    s->rope_npos = want;
+    return TP_OK;
+}
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout for T tokens: n | q | o | k,v (when no cache) | act | decode scratch
+struct Layout {
+    size_t n, q, o, kv, act, scr, total;
+};
+Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) {
+    Layout L;
+    size_t e = s->esz;
+    L.n = 0;
+    L.q = L.n + al((size_t)T * s->hidden * e);
+    L.o = L.q + al((size_t)T * s->hl * s->d * e);
+    L.kv = L.o + al((size_t)T * s->hl * s->d * e);
+    L.act = L.kv + al((size_t)2 * T * s->kvl * s->d * e);
+    L.scr = L.act + al((size_t)T * s->fl * e);
+    size_t scr = len_decode > 0 ? attn_decode_scratch_bytes(batch_decode, s->hl, len_decode) : 0;
+    L.total = L.scr + al(scr);
+    return L;
+}
+
+int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void* q, void* k, void* v,
+               int ld_seq, hipStream_t st) {
+    Epilogue epi{};
+    epi.mode = EPI_QKV;
+    epi.qkv.S = S;
+    epi.qkv.pos0 = pos0;
+    epi.qkv.hl = s->hl;
+    epi.qkv.kvl = s->kvl;
+    epi.qkv.d = s->d;
+    epi.qkv.q = q;
+    epi.qkv.k = k;
+    epi.qkv.v = v;
+    epi.qkv.ld_seq = ld_seq;
+    epi.qkv.rope_cos = s->o.rope ? s->rcos : nullptr;
+    epi.qkv.rope_sin = s->o.rope ? s->rsin : nullptr;
+    if (s->o.dtype == TP_BF16)
+        gemm_bf16((const bf16*)n_in, s->hidden, (const bf16*)s->w_qkv, s->hidden, (int)M, s->nqkv, s->hidden, epi, st);
+    else
+        gemm_f32((const float*)n_in, s->hidden, (const float*)s->w_qkv, s->hidden, (int)M, s->nqkv, s->hidden, epi, st);
+    LAUNCH_CHECK("qkv projection");
+    return TP_OK;
+}
+
+int launch_proj(tp_shard* s, const void* A, long long M, int K, const void* W, int N, int mode, void* out,
+                long long ldo, hipStream_t st) {
+    Epilogue epi{};
+    epi.mode = mode;
+    epi.out = out;
+    epi.ldo = ldo;
+    if (s->o.dtype == TP_BF16)
+        gemm_bf16((const bf16*)A, K, (const bf16*)W, K, (int)M, N, K, epi, st);
+    else
+        gemm_f32((const float*)A, K, (const float*)W, K, (int)M, N, K, epi, st);
+    LAUNCH_CHECK("projection");
+    return TP_OK;
+}
+
+int launch_norm(tp_shard* s, const void* x, const void* g, void* out, long long rows, hipStream_t st) {
+    if (s->o.dtype == TP_BF16)
+        rmsnorm_bf16((const bf16*)x, (const bf16*)g, (bf16*)out, (int)rows, s->hidden, s->o.eps, st);
+    else
+        rmsnorm_f32((const float*)x, (const float*)g, (float*)out, (int)rows, s->hidden, s->o.eps, st);
+    LAUNCH_CHECK("rmsnorm");
+    return TP_OK;
+}
+
+// decode projections at batch <= 8 stream the weights through the GEMV kernel
+constexpr int kGemvMaxBatch = 8;
+
+int launch_gemv(tp_shard* s, const void* x, int B, const void* gamma, const void* W, int N, int K,
+                const Epilogue& epi, hipStream_t st) {
+    gemv_bf16((const bf16*)x, B, (const bf16*)gamma, s->o.eps, (const bf16*)W, N, K, epi, st);
+    LAUNCH_CHECK("gemv");
+    return TP_OK;
+}
+
+#define TRY(x)                    \
+    do {                          \
+        int r_ = (x);             \
+        if (r_ != TP_OK) return r_; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(int status) {
+    switch (status) {
+        case TP_OK: return "ok";
+        case TP_E_ARG: return "invalid argument";
+        case TP_E_DIVIDE: return "heads, kv_heads or ffn not divisible by the tp degree, or degree above the head count";
+        case TP_E_RANK: return "rank outside [0, tp_degree)";
+        case TP_E_NOMEM: return "out of memory";
+        case TP_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+        case TP_E_KV_FULL: return "KV cache full";
+        case TP_E_STATE: return "call out of order (weights not loaded?)";
+        default: return "unknown status";
+    }
+}
+
+int tp_shard_create(int hidden, int heads, int kv_heads, int ffn, int tp_degree, int rank, const tp_opts* opts,
+                    tp_shard** out) {
+    if (!out) return TP_E_ARG;
+    *out = nullptr;
+    if (hidden <= 0 || heads <= 0 || kv_heads <= 0 || ffn <= 0 || tp_degree <= 0) return TP_E_ARG;
+    tp_opts o = {TP_BF16, TP_ACT_SWIGLU, 1, 1e-5f, 1, 10000.0f};
+    if (opts) o = *opts;
+    if (o.dtype != TP_BF16 && o.dtype != TP_F32) return TP_E_ARG;
+    if (o.act != TP_ACT_SWIGLU && o.act != TP_ACT_GELU) return TP_E_ARG;
+    if (o.rmsnorm && !(o.eps >= 0.f)) return TP_E_ARG;
+    if (o.rope && !(o.rope_theta > 0.f)) return TP_E_ARG;
+    if (hidden % heads || heads % kv_heads) return TP_E_ARG;
+    if (rank < 0 || rank >= tp_degree) return TP_E_RANK;
+    if (tp_degree > heads || heads % tp_degree || kv_heads % tp_degree || ffn % tp_degree) return TP_E_DIVIDE;
+    const int d = hidden / heads;
+    if (d != 64 && d != 128) return TP_E_ARG;         // packed head layout and attention tiles
+    if (hidden % 64) return TP_E_ARG;                 // GEMM K steps / GEMV rows
+    if ((ffn / tp_degree) % 64) return TP_E_ARG;      // gate/up pairing and down-projection K steps
+    tp_shard* s = new (std::nothrow) tp_shard();
+    if (!s) return TP_E_NOMEM;
+    s->hidden = hidden;
+    s->heads = heads;
+    s->kv_heads = kv_heads;
+    s->ffn = ffn;
+    s->t = tp_degree;
+    s->rank = rank;
+    s->o = o;
+    s->d = d;
+    s->hl = heads / tp_degree;
+    s->kvl = kv_heads / tp_degree;
+    s->fl = ffn / tp_degree;
+    s->nqkv = (s->hl + 2 * s->kvl) * d;
+    s->nup = o.act == TP_ACT_SWIGLU ? 2 * s->fl : s->fl;
+    s->esz = o.dtype == TP_BF16 ? 2 : 4;
+    s->device = -1;
+    *out = s;
+    return TP_OK;
+}
+
+int tp_shard_load_weights(tp_shard* s, const tp_weights* W, void* stream) {
+    if (!s || !W) return TP_E_ARG;
+    const bool swiglu = s->o.act == TP_ACT_SWIGLU;
+    if (!W->wq || !W->wk || !W->wv || !W->wo || !W->w_up || !W->w_down) return TP_E_ARG;
+    if (swiglu && !W->w_gate) return TP_E_ARG;
+    if (s->o.rmsnorm && (!W->g1 || !W->g2)) return TP_E_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t e = s->esz;
+    const int h = s->hidden, d = s->d, r = s->rank;
+    if (!s->w_qkv) {
+        HIP_TRY(hipGetDevice(&s->device));
+        void** bufs[] = {&s->w_qkv, &s->w_o, &s->w_up, &s->w_down, &s->g1, &s->g2};
+        size_t sizes[] = {(size_t)s->nqkv * h * e, (size_t)h * s->hl * d * e, (size_t)s->nup * h * e,
+                          (size_t)h * s->fl * e, (size_t)h * e, (size_t)h * e};
+        for (int i = 0; i < 6; ++i) {
+            if (hipMalloc(bufs[i], sizes[i]) != hipSuccess) {
+                for (int j = 0; j < 6; ++j)
+                    if (*bufs[j]) { (void)hipFree(*bufs[j]); *bufs[j] = nullptr; }
+                return TP_E_NOMEM;
+            }
+        }
+    }
+    // Q/K/V rows of the rank's heads, each head's rows packed in 64-row groups
+    // whose halves are the rotate-half partners (dims 32g.. and d/2 + 32g..).
+    struct Region { const void* src; int heads_total, first, count; size_t dst_row; };
+    Region regs[3] = {{W->wq, s->heads, r * s->hl, s->hl, 0},
+                      {W->wk, s->kv_heads, r * s->kvl, s->kvl, (size_t)s->hl * d},
+                      {W->wv, s->kv_heads, r * s->kvl, s->kvl, (size_t)(s->hl + s->kvl) * d}};
+    for (const Region& R : regs) {
+        for (int g = 0; g < d / 64; ++g)
+            for (int c = 0; c < 2; ++c) {
+                char* dst = (char*)s->w_qkv + (R.dst_row + 64 * g + 32 * c) * h * e;
+                const char* src = (const char*)R.src + ((size_t)R.first * d + c * (d / 2) + 32 * g) * h * e;
+                HIP_TRY(hipMemcpy2DAsync(dst, (size_t)d * h * e, src, (size_t)d * h * e, (size_t)32 * h * e, R.count,
+                                         hipMemcpyDeviceToDevice, st));
+            }
+    }
+    // W_o columns of the rank's heads (row-parallel): [h, hl*d] from [h, heads*d]
+    HIP_TRY(hipMemcpy2DAsync(s->w_o, (size_t)s->hl * d * e, (const char*)W->wo + (size_t)r * s->hl * d * e,
+                             (size_t)s->heads * d * e, (size_t)s->hl * d * e, h, hipMemcpyDeviceToDevice, st));
+    // FFN up (and gate): the rank's FFN rows; SwiGLU interleaves gate/up in 32-row blocks
+    if (swiglu) {
+        const size_t blk = (size_t)32 * h * e;
+        const char* gsrc = (const char*)W->w_gate + (size_t)r * s->fl * h * e;
+        const char* usrc = (const char*)W->w_up + (size_t)r * s->fl * h * e;
+        HIP_TRY(hipMemcpy2DAsync(s->w_up, 2 * blk, gsrc, blk, blk, s->fl / 32, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpy2DAsync((char*)s->w_up + blk, 2 * blk, usrc, blk, blk, s->fl / 32, hipMemcpyDeviceToDevice, st));
+    } else {
+        HIP_TRY(hipMemcpyAsync(s->w_up, (const char*)W->w_up + (size_t)r * s->fl * h * e, (size_t)s->fl * h * e,
+                               hipMemcpyDeviceToDevice, st));
+    }
+    // W_down columns of the rank's FFN block (row-parallel): [h, fl] from [h, ffn]
+    HIP_TRY(hipMemcpy2DAsync(s->w_down, (size_t)s->fl * e, (const char*)W->w_down + (size_t)r * s->fl * e,
+                             (size_t)s->ffn * e, (size_t)s->fl * e, h, hipMemcpyDeviceToDevice, st));
+    if (s->o.rmsnorm) {
+        HIP_TRY(hipMemcpyAsync(s->g1, W->g1, (size_t)h * e, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(s->g2, W->g2, (size_t)h * e, hipMemcpyDeviceToDevice, st));
+    }
+    s->loaded = true;
+    return TP_OK;
+}
+
+int tp_shard_reserve(tp_shard* s, long long max_tokens) {
+    if (!s || max_tokens <= 0) return TP_E_ARG;
+    Layout L = layout(s, max_tokens, 0, 0);
+    return ensure_ws(s, L.total);
+}
+
+int tp_kv_create(const tp_shard* s, int batch, int max_seq, tp_kv** out) {
+    if (!s || !out || batch <= 0 || max_seq <= 0) return TP_E_ARG;
+    if (s->o.dtype == TP_F32 && max_seq > 16000) return TP_E_ARG;  // fp32 attention keeps scores in LDS
+    *out = nullptr;
+    tp_kv* kv = new (std::nothrow) tp_kv();
+    if (!kv) return TP_E_NOMEM;
+    kv->batch = batch;
+    kv->max_seq = max_seq;
+    kv->len = 0;
+    kv->kvl = s->kvl;
+    kv->d = s->d;
+    kv->esz = s->esz;
+    kv->dtype = s->o.dtype;
+    size_t bytes = (size_t)batch * s->kvl * max_seq * s->d * s->esz;
+    if (hipMalloc(&kv->k, bytes) != hipSuccess || hipMalloc(&kv->v, bytes) != hipSuccess) {
+        if (kv->k) (void)hipFree(kv->k);
+        delete kv;
+        return TP_E_NOMEM;
+    }
+    if (hipMemset(kv->k, 0, bytes) != hipSuccess || hipMemset(kv->v, 0, bytes) != hipSuccess) {
+        (void)hipFree(kv->k);
+        (void)hipFree(kv->v);
+        delete kv;
+        return hip_fail(hipGetLastError(), "hipMemset(kv)");
+    }
+    *out = kv;
+    return TP_OK;
+}
+
+int tp_kv_view(tp_kv* kv, void** k, void** v) {
+    if (!kv) return TP_E_ARG;
+    if (k) *k = kv->k;
+    if (v) *v = kv->v;
+    return TP_OK;
+}
+
+int tp_kv_set_len(tp_kv* kv, int len) {
+    if (!kv || len < 0 || len > kv->max_seq) return TP_E_ARG;
+    kv->len = len;
+    return TP_OK;
+}
+
+int tp_kv_get_len(const tp_kv* kv, int* len) {
+    if (!kv || !len) return TP_E_ARG;
+    *len = kv->len;
+    return TP_OK;
+}
+
+int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv, float* partial,
+                             void* stream) {
+    if (!s || !x || !partial || batch <= 0 || seq <= 0) return TP_E_ARG;
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return TP_E_ARG;
+    if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
+    if (!s->loaded) return TP_E_STATE;
+    const long long T = (long long)batch * seq;
+    if (T > INT32_MAX / 2) return TP_E_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (stage == TP_STAGE_MLP && kv) return TP_E_ARG;
+    if (stage == TP_STAGE_ATTN && kv) {
+        if (kv->batch != batch || kv->dtype != s->o.dtype || kv->kvl != s->kvl) return TP_E_ARG;
+        if (seq > kv->max_seq) return TP_E_KV_FULL;
+    }
+    if (s->o.dtype == TP_F32 && stage == TP_STAGE_ATTN && seq > 16000) return TP_E_ARG;
+    Layout L = layout(s, T, 0, 0);
+    TRY(ensure_ws(s, L.total));
+    char* ws = s->ws;
+    s->off_n = L.n;
+    s->off_o = L.o;
+    s->off_act = L.act;
+    const void* xin = x;
+    if (stage == TP_STAGE_ATTN) {
+        TRY(ensure_rope(s, seq, st));
+        if (s->o.rmsnorm) {
+            TRY(launch_norm(s, x, s->g1, ws + L.n, T, st));
+            xin = ws + L.n;
+        }
+        void *kd, *vd;
+        int ld_seq;
+        if (kv) {
+            kd = kv->k;
+            vd = kv->v;
+            ld_seq = kv->max_seq;
+        } else {
+            kd = ws + L.kv;
+            vd = ws + L.kv + (size_t)T * s->kvl * s->d * s->esz;
+            ld_seq = seq;
+        }
+        TRY(launch_qkv(s, xin, T, seq, 0, ws + L.q, kd, vd, ld_seq, st));
+        if (s->o.dtype == TP_BF16)
+            attn_prefill_bf16((const bf16*)(ws + L.q), (const bf16*)kd, (const bf16*)vd, (bf16*)(ws + L.o), batch,
+                              s->hl, s->kvl, seq, ld_seq, s->d, st);
+        else
+            attn_f32((const float*)(ws + L.q), (const float*)kd, (const float*)vd, (float*)(ws + L.o), batch, s->hl,
+                     s->kvl, seq, 0, ld_seq, s->d, st);
+        LAUNCH_CHECK("attention");
+        TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
+        if (kv) kv->len = seq;
+    } else {
+        if (s->o.rmsnorm) {
+            TRY(launch_norm(s, x, s->g2, ws + L.n, T, st));
+            xin = ws + L.n;
+        }
+        const int mode = s->o.act == TP_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU;
+        TRY(launch_proj(s, xin, T, s->hidden, s->w_up, s->nup, mode, ws + L.act, s->fl, st));
+        TRY(launch_proj(s, ws + L.act, T, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
+    }
+    return TP_OK;
+}
+
+int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial,
+                            void* stream) {
+    if (!s || !x || !partial || batch <= 0) return TP_E_ARG;
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return TP_E_ARG;
+    if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
+    if (!s->loaded) return TP_E_STATE;
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf = s->o.dtype == TP_BF16;
+    const bool use_gemv = bf && batch <= kGemvMaxBatch;
+    if (stage == TP_STAGE_ATTN) {
+        if (!kv) return TP_E_ARG;
+        if (kv->batch != batch || kv->dtype != s->o.dtype || kv->kvl != s->kvl) return TP_E_ARG;
+        if (kv->len >= kv->max_seq) return TP_E_KV_FULL;
+    } else if (kv) {
+        return TP_E_ARG;
+    }
+    const int L = stage == TP_STAGE_ATTN ? kv->len : 0;
+    Layout lay = layout(s, batch, stage == TP_STAGE_ATTN ? L + 1 : 0, batch);
+    TRY(ensure_ws(s, lay.total));
+    char* ws = s->ws;
+    s->off_n = lay.n;
+    s->off_o = lay.o;
+    s->off_act = lay.act;
+    if (stage == TP_STAGE_ATTN) {
+        TRY(ensure_rope(s, L + 1, st));
+        void* qbuf = ws + lay.q;
+        if (use_gemv) {
+            Epilogue epi{};
+            epi.mode = EPI_QKV;
+            epi.qkv = QKVDest{1, L, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
+                              s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
+            TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi, st));
+        } else {
+            const void* xin = x;
+            if (s->o.rmsnorm) {
+                TRY(launch_norm(s, x, s->g1, ws + lay.n, batch, st));
+                xin = ws + lay.n;
+            }
+            TRY(launch_qkv(s, xin, batch, 1, L, qbuf, kv->k, kv->v, kv->max_seq, st));
+        }
+        if (bf)
+            attn_decode_bf16((const bf16*)qbuf, (const bf16*)kv->k, (const bf16*)kv->v, (bf16*)(ws + lay.o),
+                             (float*)(ws + lay.scr), batch, s->hl, s->kvl, L + 1, kv->max_seq, s->d, st);
+        else
+            attn_f32((const float*)qbuf, (const float*)kv->k, (const float*)kv->v, (float*)(ws + lay.o), batch, s->hl,
+                     s->kvl, 1, L, kv->max_seq, s->d, st);
+        LAUNCH_CHECK("decode attention");
+        if (use_gemv) {
+            Epilogue epi{};
+            epi.mode = EPI_F32;
+            epi.out = partial;
+            epi.ldo = s->hidden;
+            TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, st));
+        } else {
+            TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
+        }
+        kv->len = L + 1;
+    } else {
+        const int mode = s->o.act == TP_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU;
+        if (use_gemv) {
+            Epilogue epi{};
+            epi.mode = mode;
+            epi.out = ws + lay.act;
+            epi.ldo = s->fl;
+            TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi, st));
+            Epilogue e2{};
+            e2.mode = EPI_F32;
+            e2.out = partial;
+            e2.ldo = s->hidden;
+            TRY(launch_gemv(s, ws + lay.act, batch, nullptr, s->w_down, s->hidden, s->fl, e2, st));
+        } else {
+            const void* xin = x;
+            if (s->o.rmsnorm) {
+                TRY(launch_norm(s, x, s->g2, ws + lay.n, batch, st));
+                xin = ws + lay.n;
+            }
+            TRY(launch_proj(s, xin, batch, s->hidden, s->w_up, s->nup, mode, ws + lay.act, s->fl, st));
+            TRY(launch_proj(s, ws + lay.act, batch, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
+        }
+    }
+    return TP_OK;
+}
+
+int tp_partial_reduce(const float* const* partials, int t, const void* residual, void* out, long long n,
+                      int out_dtype, void* stream) {
+    if (!partials || t < 1 || t > 64 || n < 0) return TP_E_ARG;
+    if (out_dtype != TP_BF16 && out_dtype != TP_F32) return TP_E_ARG;
+    if (n == 0) return TP_OK;  // nothing to sum (empty tensors may have NULL addresses)
+    if (!out) return TP_E_ARG;
+    for (int r = 0; r < t; ++r)
+        if (!partials[r] || !aligned16(partials[r])) return TP_E_ARG;
+    if (!aligned16(out) || (residual && !aligned16(residual))) return TP_E_ARG;
+    partial_reduce(partials, t, residual, out, n, out_dtype == TP_BF16, (hipStream_t)stream);
+    LAUNCH_CHECK("partial_reduce");
+    return TP_OK;
+}
+
+int tp_shard_debug_view(tp_shard* s, int which, void** ptr) {
+    if (!s || !ptr || !s->ws) return TP_E_ARG;
+    switch (which) {
+        case 0: *ptr = s->ws + s->off_o; return TP_OK;
+        case 1: *ptr = s->ws + s->off_act; return TP_OK;
+        case 2: *ptr = s->ws + s->off_n; return TP_OK;
+        default: return TP_E_ARG;
+    }
+}
+
+int tp_tune_set_gemm_config(int cfg) {
+    if (cfg < -1 || cfg >= gemm_config_count()) return TP_E_ARG;
+    set_gemm_config(cfg);
+    return TP_OK;
+}
+
+void tp_shard_destroy(tp_shard* s) {
+    if (!s) return;
+    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin};
+    for (void* b : bufs)
+        if (b) (void)hipFree(b);
+    delete s;
+}
+
+void tp_kv_destroy(tp_kv* kv) {
+    if (!kv) return;
+    if (kv->k) (void)hipFree(kv->k);
+    if (kv->v) (void)hipFree(kv->v);
+    delete kv;
+}
+
+}  // extern "C"

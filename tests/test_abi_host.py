@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+- the built library exports every function include/tp_shard.h declares;
+- tp_shard_create applies the partition rules (golden cases, with their
+  citations in tests/golden/partition_cases.txt) and the kernel limits
+  before touching a device;
+- argument and state errors of the other entry points return their codes
+  without launching anything.
+"""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from tensor_transformer_layer_tp_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "partition_cases.txt")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(N.LIB_PATH), reason="libtpshard.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = N.lib()
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(n for n, _, _ in N.SIGNATURES) == names
+
+
+def test_status_strings():
+    lib = N.lib()
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+        assert lib.tp_status_string(code)
+
+
+def create(hidden, heads, kv, ffn, t, r, dtype=N.TP_BF16, act=N.TP_ACT_SWIGLU, rope=1):
+    opts = N.tp_opts(dtype, act, 1, 1e-5, rope, 10000.0)
+    h = C.c_void_p()
+    st = N.lib().tp_shard_create(hidden, heads, kv, ffn, t, r, C.byref(opts), C.byref(h))
+    if st == N.TP_OK:
+        N.lib().tp_shard_destroy(h)
+    return st
+
+
+def golden_cases():
+    out = []
+    for line in open(GOLDEN):
+        line = line.split("#")[0].strip()
+        if line:
+            H, Hk, Fw, t, e = line.split()
+            out.append((int(H), int(Hk), int(Fw), int(t), e))
+    return out
+
+
+@pytest.mark.parametrize("case", golden_cases(), ids=str)
+def test_create_partition_rules(case):
+    H, Hk, Fw, t, expect = case
+    st = create(H * 128, H, Hk, Fw, t, 0)
+    if expect == "divide":
+        assert st == N.TP_E_DIVIDE
+    else:
+        # allowed by the pages; the kernels additionally need (ffn/t) % 64 == 0
+        assert st == (N.TP_OK if (Fw // t) % 64 == 0 else N.TP_E_ARG)
+
+
+def test_create_rank_and_args():
+    assert create(4096, 32, 32, 11008, 2, 2) == N.TP_E_RANK
+    assert create(4096, 32, 32, 11008, 2, -1) == N.TP_E_RANK
+    assert create(4096, 32, 32, 11008, 0, 0) == N.TP_E_ARG
+    assert create(4000, 32, 32, 11008, 2, 0) == N.TP_E_ARG          # hidden % heads
+    assert create(4096, 32, 5, 11008, 1, 0) == N.TP_E_ARG           # heads % kv_heads
+    assert create(4096, 16, 16, 11008, 2, 0) == N.TP_E_ARG          # head_dim 256 unsupported
+    assert create(256, 4, 4, 1024, 2, 1, dtype=N.TP_F32, act=N.TP_ACT_GELU, rope=0) == N.TP_OK
+    assert create(4096, 32, 32, 11008, 2, 1) == N.TP_OK
+    assert create(8192, 64, 8, 28672, 8, 7) == N.TP_OK
+    assert N.lib().tp_shard_create(64, 1, 1, 64, 1, 0, None, None) == N.TP_E_ARG
+    bad = N.tp_opts(7, 0, 1, 1e-5, 1, 1e4)
+    h = C.c_void_p()
+    assert N.lib().tp_shard_create(4096, 32, 32, 11008, 2, 0, C.byref(bad), C.byref(h)) == N.TP_E_ARG
+
+
+def test_forward_before_weights_is_state_error():
+    lib = N.lib()
+    h = C.c_void_p()
+    assert lib.tp_shard_create(4096, 32, 32, 11008, 2, 0, None, C.byref(h)) == N.TP_OK
+    fake = C.c_void_p(0x10000)  # never dereferenced: validation comes first
+    try:
+        assert lib.tp_shard_forward_prefill(h, N.TP_STAGE_ATTN, fake, 1, 16, None, fake, None) == N.TP_E_STATE
+        assert lib.tp_shard_forward_decode(h, N.TP_STAGE_MLP, fake, 1, None, fake, None) == N.TP_E_STATE
+        assert lib.tp_shard_forward_prefill(h, 5, fake, 1, 16, None, fake, None) == N.TP_E_ARG
+        assert lib.tp_shard_forward_prefill(h, 0, C.c_void_p(0x10002), 1, 16, None, fake, None) == N.TP_E_ARG
+        assert lib.tp_shard_forward_prefill(h, 0, fake, 0, 16, None, fake, None) == N.TP_E_ARG
+        assert lib.tp_shard_forward_prefill(h, 0, None, 1, 16, None, fake, None) == N.TP_E_ARG
+        assert lib.tp_shard_reserve(h, 0) == N.TP_E_ARG
+        p = C.c_void_p()
+        assert lib.tp_shard_debug_view(h, 0, C.byref(p)) == N.TP_E_ARG   # no workspace yet
+        w = N.tp_weights()
+        assert lib.tp_shard_load_weights(h, C.byref(w), None) == N.TP_E_ARG  # NULL weights
+    finally:
+        lib.tp_shard_destroy(h)
+
+
+def test_partial_reduce_argument_errors():
+    lib = N.lib()
+    fake = 0x10000
+    out = C.c_void_p(0x20000)
+    arr = (C.c_void_p * 2)(fake, fake)
+    assert lib.tp_partial_reduce(arr, 0, None, out, 16, N.TP_BF16, None) == N.TP_E_ARG
+    assert lib.tp_partial_reduce(arr, 65, None, out, 16, N.TP_BF16, None) == N.TP_E_ARG
+    lost = (C.c_void_p * 2)(fake, None)                           # a lost rank
+    assert lib.tp_partial_reduce(lost, 2, None, out, 16, N.TP_BF16, None) == N.TP_E_ARG
+    mis = (C.c_void_p * 2)(fake, fake + 4)
+    assert lib.tp_partial_reduce(mis, 2, None, out, 16, N.TP_BF16, None) == N.TP_E_ARG
+    assert lib.tp_partial_reduce(arr, 2, None, None, 16, N.TP_BF16, None) == N.TP_E_ARG
+    assert lib.tp_partial_reduce(arr, 2, None, out, 16, 9, None) == N.TP_E_ARG
+    assert lib.tp_partial_reduce(arr, 2, None, out, 0, N.TP_BF16, None) == N.TP_OK   # nothing to do
+
+
+def test_kv_argument_errors():
+    lib = N.lib()
+    n = C.c_int()
+    assert lib.tp_kv_set_len(None, 3) == N.TP_E_ARG
+    assert lib.tp_kv_get_len(None, C.byref(n)) == N.TP_E_ARG
+    assert lib.tp_kv_view(None, None, None) == N.TP_E_ARG
+    assert lib.tp_kv_create(None, 1, 16, C.byref(C.c_void_p())) == N.TP_E_ARG
+
+
+def test_tune_hook_range():
+    lib = N.lib()
+    assert lib.tp_tune_set_gemm_config(99) == N.TP_E_ARG
+    assert lib.tp_tune_set_gemm_config(-1) == N.TP_OK

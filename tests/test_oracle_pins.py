@@ -381,3 +381,17 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
     for t in ((1,) if mutation == "gqa_map" else (1, 2)):
         got = O.layer(x, W, spec, t=t)["y"]
         assert np.abs(got - want).max() > 1e-6, (mutation, t)
+
+
+def test_row_restricted_stages_match_full_stages():
+    spec = O.Spec(64, 8, 2, 96, mirror_bf16=True)
+    W = weights(spec, seed=101)
+    x = O.bf16_round(rnd((2, 13, 64), 102))
+    rows = np.array([0, 5, 12])
+    full = O.attn_stage(x, W, spec, 2, 1)
+    part = O.attn_stage_rows(x, W, spec, 2, 1, rows)
+    np.testing.assert_allclose(part["partial"], full["partial"][:, rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["o"], full["o"][:, :, rows], rtol=1e-12, atol=1e-12)
+    m_full = O.mlp_stage(x, W, spec, 2, 0)
+    m_part = O.mlp_stage_rows(x, W, spec, 2, 0, rows)
+    np.testing.assert_allclose(m_part["partial"], m_full["partial"][:, rows], rtol=1e-12, atol=1e-12)
