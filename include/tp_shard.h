@@ -182,6 +182,29 @@ int tp_partial_reduce(const float *const *partials, int t,
  * the next forward call on this shard. */
 int tp_shard_debug_view(tp_shard *s, int which, void **ptr);
 
+/* Kernel timer (diagnostics): while enabled, every kernel a forward call
+ * launches is bracketed by two hipEvents recorded on the launch stream, and
+ * the elapsed times are summed per kernel kind.  Recording adds a marker
+ * between kernels, so time whole steps with the timer off.
+ * tp_shard_timing(s, 1) enables and resets the sums (it creates the event
+ * pool on first use); tp_shard_timing(s, 0) stops recording.
+ * tp_shard_timing_read waits for the recorded events and returns the total
+ * milliseconds and launch count of one kernel kind (TP_K_*). */
+#define TP_K_RMSNORM      0
+#define TP_K_GEMM_QKV     1
+#define TP_K_ATTN_PREFILL 2
+#define TP_K_GEMM_OUT     3
+#define TP_K_GEMM_UP      4
+#define TP_K_GEMM_DOWN    5
+#define TP_K_GEMV_QKV     6
+#define TP_K_ATTN_DECODE  7
+#define TP_K_GEMV_OUT     8
+#define TP_K_GEMV_UP      9
+#define TP_K_GEMV_DOWN    10
+#define TP_K_COUNT        11
+int tp_shard_timing(tp_shard *s, int enable);
+int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *launches);
+
 /* tp_tune_set_gemm_config -- tuning hook: force the projection GEMM's tile
  * configuration (0..3: 256x256, 256x128, 128x128, 128x256 output tiles) for
  * every later call in this process, or -1 to restore the shape-based choice.

@@ -209,6 +209,20 @@ class Shard:
         _memcpy_d2d(t.data_ptr(), p.value, t.numel() * self.elem_size, stream)
         return t
 
+    def timing(self, enable: bool) -> None:
+        """Turn the per-kernel event timer on (resetting it) or off."""
+        N.check(N.lib().tp_shard_timing(self._h, int(enable)), "tp_shard_timing")
+
+    def timing_read(self) -> dict:
+        """{kernel kind: (total ms, launches)} of the recorded launches."""
+        out = {}
+        for i, name in enumerate(N.KERNEL_KINDS):
+            ms, n = C.c_double(), C.c_longlong()
+            N.check(N.lib().tp_shard_timing_read(self._h, i, C.byref(ms), C.byref(n)), "tp_shard_timing_read")
+            if n.value:
+                out[name] = (ms.value, n.value)
+        return out
+
     def close(self) -> None:
         if self._h:
             N.lib().tp_shard_destroy(self._h)

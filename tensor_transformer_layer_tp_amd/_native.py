@@ -16,6 +16,9 @@ TP_OK, TP_E_ARG, TP_E_DIVIDE, TP_E_RANK, TP_E_NOMEM, TP_E_HIP, TP_E_KV_FULL, TP_
 TP_F32, TP_BF16 = 0, 1
 TP_STAGE_ATTN, TP_STAGE_MLP = 0, 1
 TP_ACT_SWIGLU, TP_ACT_GELU = 0, 1
+# kernel kinds of the shard's event timer (TP_K_*)
+KERNEL_KINDS = ["rmsnorm", "gemm_qkv", "attn_prefill", "gemm_out", "gemm_up", "gemm_down", "gemv_qkv",
+                "attn_decode", "gemv_out", "gemv_up", "gemv_down"]
 
 
 class tp_opts(C.Structure):
@@ -45,6 +48,8 @@ SIGNATURES = [
                                     C.c_void_p]),
     ("tp_shard_debug_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),
     ("tp_tune_set_gemm_config", C.c_int, [C.c_int]),
+    ("tp_shard_timing", C.c_int, [C.c_void_p, C.c_int]),
+    ("tp_shard_timing_read", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),
     ("tp_shard_destroy", None, [C.c_void_p]),
     ("tp_kv_destroy", None, [C.c_void_p]),
     ("tp_status_string", C.c_char_p, [C.c_int]),

@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 
 #include "kernels.h"
 
@@ -36,6 +37,11 @@ struct tp_shard {
     int rope_npos;
     // offsets of the last call's workspace tensors (debug view)
     size_t off_n, off_o, off_act;
+    // kernel timer: event pairs in launch order and the kind of each pair
+    bool timing;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> evkind;
+    size_t evused;
 };
 
 struct tp_kv {
@@ -185,6 +191,27 @@ int launch_gemv(tp_shard* s, const void* x, int B, const void* gamma, const void
     LAUNCH_CHECK("gemv");
     return TP_OK;
 }
+
+// Brackets one kernel launch with two events when the shard's timer is on.
+struct KTimer {
+    tp_shard* s;
+    hipStream_t st;
+    size_t slot;
+    bool on;
+    KTimer(tp_shard* s_, int kind, hipStream_t st_) : s(s_), st(st_), slot(0), on(false) {
+        if (s->timing && s->evused + 2 <= s->ev.size()) {
+            on = true;
+            slot = s->evused;
+            s->evused += 2;
+            s->evkind.push_back(kind);
+            (void)hipEventRecord(s->ev[slot], st);
+        }
+    }
+    ~KTimer() {
+        if (on) (void)hipEventRecord(s->ev[slot + 1], st);
+    }
+};
+constexpr size_t kTimerEvents = 8192;
 
 #define TRY(x)                    \
     do {                          \
@@ -390,6 +417,7 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
     if (stage == TP_STAGE_ATTN) {
         TRY(ensure_rope(s, seq, st));
         if (s->o.rmsnorm) {
+            KTimer kt(s, TP_K_RMSNORM, st);
             TRY(launch_norm(s, x, s->g1, ws + L.n, T, st));
             xin = ws + L.n;
         }
@@ -404,24 +432,40 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
             vd = ws + L.kv + (size_t)T * s->kvl * s->d * s->esz;
             ld_seq = seq;
         }
-        TRY(launch_qkv(s, xin, T, seq, 0, ws + L.q, kd, vd, ld_seq, st));
-        if (s->o.dtype == TP_BF16)
-            attn_prefill_bf16((const bf16*)(ws + L.q), (const bf16*)kd, (const bf16*)vd, (bf16*)(ws + L.o), batch,
-                              s->hl, s->kvl, seq, ld_seq, s->d, st);
-        else
-            attn_f32((const float*)(ws + L.q), (const float*)kd, (const float*)vd, (float*)(ws + L.o), batch, s->hl,
-                     s->kvl, seq, 0, ld_seq, s->d, st);
-        LAUNCH_CHECK("attention");
-        TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
+        {
+            KTimer kt(s, TP_K_GEMM_QKV, st);
+            TRY(launch_qkv(s, xin, T, seq, 0, ws + L.q, kd, vd, ld_seq, st));
+        }
+        {
+            KTimer kt(s, TP_K_ATTN_PREFILL, st);
+            if (s->o.dtype == TP_BF16)
+                attn_prefill_bf16((const bf16*)(ws + L.q), (const bf16*)kd, (const bf16*)vd, (bf16*)(ws + L.o),
+                                  batch, s->hl, s->kvl, seq, ld_seq, s->d, st);
+            else
+                attn_f32((const float*)(ws + L.q), (const float*)kd, (const float*)vd, (float*)(ws + L.o), batch,
+                         s->hl, s->kvl, seq, 0, ld_seq, s->d, st);
+            LAUNCH_CHECK("attention");
+        }
+        {
+            KTimer kt(s, TP_K_GEMM_OUT, st);
+            TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
+        }
         if (kv) kv->len = seq;
     } else {
         if (s->o.rmsnorm) {
+            KTimer kt(s, TP_K_RMSNORM, st);
             TRY(launch_norm(s, x, s->g2, ws + L.n, T, st));
             xin = ws + L.n;
         }
         const int mode = s->o.act == TP_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU;
-        TRY(launch_proj(s, xin, T, s->hidden, s->w_up, s->nup, mode, ws + L.act, s->fl, st));
-        TRY(launch_proj(s, ws + L.act, T, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
+        {
+            KTimer kt(s, TP_K_GEMM_UP, st);
+            TRY(launch_proj(s, xin, T, s->hidden, s->w_up, s->nup, mode, ws + L.act, s->fl, st));
+        }
+        {
+            KTimer kt(s, TP_K_GEMM_DOWN, st);
+            TRY(launch_proj(s, ws + L.act, T, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
+        }
     }
     return TP_OK;
 }
@@ -457,29 +501,37 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.mode = EPI_QKV;
             epi.qkv = QKVDest{1, L, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
                               s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
+            KTimer kt(s, TP_K_GEMV_QKV, st);
             TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi, st));
         } else {
             const void* xin = x;
             if (s->o.rmsnorm) {
+                KTimer kt(s, TP_K_RMSNORM, st);
                 TRY(launch_norm(s, x, s->g1, ws + lay.n, batch, st));
                 xin = ws + lay.n;
             }
+            KTimer kt(s, TP_K_GEMM_QKV, st);
             TRY(launch_qkv(s, xin, batch, 1, L, qbuf, kv->k, kv->v, kv->max_seq, st));
         }
-        if (bf)
-            attn_decode_bf16((const bf16*)qbuf, (const bf16*)kv->k, (const bf16*)kv->v, (bf16*)(ws + lay.o),
-                             (float*)(ws + lay.scr), batch, s->hl, s->kvl, L + 1, kv->max_seq, s->d, st);
-        else
-            attn_f32((const float*)qbuf, (const float*)kv->k, (const float*)kv->v, (float*)(ws + lay.o), batch, s->hl,
-                     s->kvl, 1, L, kv->max_seq, s->d, st);
-        LAUNCH_CHECK("decode attention");
+        {
+            KTimer kt(s, TP_K_ATTN_DECODE, st);
+            if (bf)
+                attn_decode_bf16((const bf16*)qbuf, (const bf16*)kv->k, (const bf16*)kv->v, (bf16*)(ws + lay.o),
+                                 (float*)(ws + lay.scr), batch, s->hl, s->kvl, L + 1, kv->max_seq, s->d, st);
+            else
+                attn_f32((const float*)qbuf, (const float*)kv->k, (const float*)kv->v, (float*)(ws + lay.o), batch,
+                         s->hl, s->kvl, 1, L, kv->max_seq, s->d, st);
+            LAUNCH_CHECK("decode attention");
+        }
         if (use_gemv) {
             Epilogue epi{};
             epi.mode = EPI_F32;
             epi.out = partial;
             epi.ldo = s->hidden;
+            KTimer kt(s, TP_K_GEMV_OUT, st);
             TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, st));
         } else {
+            KTimer kt(s, TP_K_GEMM_OUT, st);
             TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
         }
         kv->len = L + 1;
@@ -490,19 +542,28 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.mode = mode;
             epi.out = ws + lay.act;
             epi.ldo = s->fl;
-            TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi, st));
+            {
+                KTimer kt(s, TP_K_GEMV_UP, st);
+                TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi, st));
+            }
             Epilogue e2{};
             e2.mode = EPI_F32;
             e2.out = partial;
             e2.ldo = s->hidden;
+            KTimer kt(s, TP_K_GEMV_DOWN, st);
             TRY(launch_gemv(s, ws + lay.act, batch, nullptr, s->w_down, s->hidden, s->fl, e2, st));
         } else {
             const void* xin = x;
             if (s->o.rmsnorm) {
+                KTimer kt(s, TP_K_RMSNORM, st);
                 TRY(launch_norm(s, x, s->g2, ws + lay.n, batch, st));
                 xin = ws + lay.n;
             }
-            TRY(launch_proj(s, xin, batch, s->hidden, s->w_up, s->nup, mode, ws + lay.act, s->fl, st));
+            {
+                KTimer kt(s, TP_K_GEMM_UP, st);
+                TRY(launch_proj(s, xin, batch, s->hidden, s->w_up, s->nup, mode, ws + lay.act, s->fl, st));
+            }
+            KTimer kt(s, TP_K_GEMM_DOWN, st);
             TRY(launch_proj(s, ws + lay.act, batch, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
         }
     }
@@ -533,6 +594,44 @@ int tp_shard_debug_view(tp_shard* s, int which, void** ptr) {
     }
 }
 
+int tp_shard_timing(tp_shard* s, int enable) {
+    if (!s) return TP_E_ARG;
+    if (enable) {
+        if (s->ev.empty()) {
+            s->ev.resize(kTimerEvents, nullptr);
+            for (size_t i = 0; i < kTimerEvents; ++i) {
+                hipError_t e = hipEventCreate(&s->ev[i]);
+                if (e != hipSuccess) {
+                    for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(s->ev[j]);
+                    s->ev.clear();
+                    return hip_fail(e, "hipEventCreate");
+                }
+            }
+        }
+        s->evused = 0;
+        s->evkind.clear();
+    }
+    s->timing = enable != 0;
+    return TP_OK;
+}
+
+int tp_shard_timing_read(tp_shard* s, int kernel, double* total_ms, long long* launches) {
+    if (!s || !total_ms || !launches || kernel < 0 || kernel >= TP_K_COUNT) return TP_E_ARG;
+    double tot = 0.0;
+    long long n = 0;
+    for (size_t i = 0; i < s->evkind.size(); ++i) {
+        if (s->evkind[i] != kernel) continue;
+        HIP_TRY(hipEventSynchronize(s->ev[2 * i + 1]));
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, s->ev[2 * i], s->ev[2 * i + 1]));
+        tot += ms;
+        ++n;
+    }
+    *total_ms = tot;
+    *launches = n;
+    return TP_OK;
+}
+
 int tp_tune_set_gemm_config(int cfg) {
     if (cfg < -1 || cfg >= gemm_config_count()) return TP_E_ARG;
     set_gemm_config(cfg);
@@ -541,6 +640,8 @@ int tp_tune_set_gemm_config(int cfg) {
 
 void tp_shard_destroy(tp_shard* s) {
     if (!s) return;
+    for (hipEvent_t e : s->ev)
+        if (e) (void)hipEventDestroy(e);
     void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin};
     for (void* b : bufs)
         if (b) (void)hipFree(b);

@@ -14,7 +14,7 @@ import torch
 from oracle import layer as O
 from tensor_transformer_layer_tp_amd import ATTN, MLP, Shard, TPError, TP_E_KV_FULL, partial_reduce, synth
 
-from helpers import Layer, assert_close, rank_cache, to_np
+from helpers import Layer, assert_close, rank_cache, sum_magnitude, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -28,14 +28,21 @@ def nan_like(shape):
 
 
 def run_chain(layer: Layer, tp: int, B: int, S: int, check_kv=True):
-    """All tp ranks of a prefill: ATTN stages, reduce, MLP stages, reduce;
-    every tensor compared with the oracle's layer(t=tp)."""
+    """All tp ranks of a prefill: ATTN stages, reduce, MLP stages, reduce.
+
+    Every stage is compared with the oracle on identical inputs: the ATTN
+    stages on x, the reduce on the ranks' partials, the MLP stages on the
+    oracle's h (bf16 values, so exactly representable as GPU input).  The
+    fully chained GPU result (MLP on the GPU's own h) carries the in-tolerance
+    difference between the two h's through the FFN, so it is compared
+    norm-wise (relative Frobenius error <= 1e-2)."""
     dt = layer.dtype
     x_dev = layer.dev["x"]
+    hid = layer.spec.hidden
     ref = O.layer(layer.exact["x"], layer.W, layer.spec, t=tp)
     shards = [layer.shard(tp, r) for r in range(tp)]
     kvs = [sh.kv_cache(B, S + 5) for sh in shards]
-    pa = [sh.prefill(ATTN, x_dev, kv, out=nan_like((B, S, layer.spec.hidden))) for sh, kv in zip(shards, kvs)]
+    pa = [sh.prefill(ATTN, x_dev, kv, out=nan_like((B, S, hid))) for sh, kv in zip(shards, kvs)]
     torch.cuda.synchronize()
     for r in range(tp):
         assert_close(to_np(pa[r]), ref["attn"][r]["partial"], f"attn partial r{r}", dt)
@@ -46,15 +53,23 @@ def run_chain(layer: Layer, tp: int, B: int, S: int, check_kv=True):
             assert kvs[r].length == S
     h = partial_reduce(pa, residual=x_dev)
     torch.cuda.synchronize()
-    assert_close(to_np(h), ref["h"], "h", dt)
-    # the MLP stage takes the oracle-independent GPU h; its reference is the oracle's
-    # own chain, so compare the stage against the oracle on the same h as well
-    pm = [sh.prefill(MLP, h, out=nan_like((B, S, layer.spec.hidden))) for sh in shards]
-    y = partial_reduce(pm, residual=h)
+    assert_close(to_np(h), ref["h"], "h", dt,
+                 sum_magnitude(layer.exact["x"], [a["partial"] for a in ref["attn"]]))
+    # MLP stages on the oracle's h
+    h_ref = torch.from_numpy(ref["h"].astype(np.float32)).to(layer.torch_dtype).cuda()
+    pm = [sh.prefill(MLP, h_ref, out=nan_like((B, S, hid))) for sh in shards]
+    y = partial_reduce(pm, residual=h_ref)
     torch.cuda.synchronize()
-    assert_close(to_np(y), ref["y"], "y", dt)
     for r in range(tp):
         assert_close(to_np(pm[r]), ref["mlp"][r]["partial"], f"mlp partial r{r}", dt)
+    assert_close(to_np(y), ref["y"], "y", dt, sum_magnitude(ref["h"], [m["partial"] for m in ref["mlp"]]))
+    # fully chained on the GPU's own h
+    pm2 = [sh.prefill(MLP, h, out=nan_like((B, S, hid))) for sh in shards]
+    y2 = to_np(partial_reduce(pm2, residual=h))
+    torch.cuda.synchronize()
+    assert np.isfinite(y2).all()
+    rel = np.linalg.norm(y2 - ref["y"]) / np.linalg.norm(ref["y"])
+    assert rel <= 1e-2, f"chained y: relative Frobenius error {rel:.3g}"
     return shards, kvs
 
 
@@ -73,8 +88,9 @@ def test_partial_reduce(dtype, t, n):
         assert out.numel() == 0
         return
     out = partial_reduce(parts, residual=res.cuda())
-    want = O.reduce([p.astype(np.float32) for p in parts64], res.float().numpy(), spec)
-    assert_close(to_np(out), want, "reduce", dtype)
+    p32 = [p.astype(np.float32) for p in parts64]
+    want = O.reduce(p32, res.float().numpy(), spec)
+    assert_close(to_np(out), want, "reduce", dtype, sum_magnitude(res.float().numpy(), p32))
     out2 = partial_reduce(parts, residual=None, dtype=dtype)
     want2 = O.reduce([p.astype(np.float32) for p in parts64], np.zeros(n), spec)
     assert_close(to_np(out2), want2, "reduce no residual", dtype)
