@@ -206,10 +206,13 @@ int tp_shard_timing(tp_shard *s, int enable);
 int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *launches);
 
 /* tp_tune_set_gemm_config -- tuning hook: force the projection GEMM's tile
- * configuration (0..3: 256x256, 256x128, 128x128, 128x256 output tiles) for
- * every later call in this process, or -1 to restore the shape-based choice.
- * Configurations a kernel variant cannot use are skipped.  TP_E_ARG if out
- * of range. */
+ * configuration for every later call in this process, or -1 to restore the
+ * shape-based choice.  0..2: register-staged 256x128, 128x128, 128x256
+ * output tiles; 3..8: direct-to-LDS rings 256x256 (K-step 64, 2 stages),
+ * 256x256 (32, 4), 256x128 (64, 3), 128x128 (64, 4), 128x128 (64, 2),
+ * 256x128 (32, 4).  A configuration that a projection cannot use (256x256
+ * with the rotary or GELU epilogue) falls back to the shape-based choice.
+ * TP_E_ARG if out of range. */
 int tp_tune_set_gemm_config(int cfg);
 
 void tp_shard_destroy(tp_shard *s);

@@ -10,133 +10,52 @@
 // column-parallel = full input times a column slice, row-parallel = matching
 // blocks giving partial results).
 //
-// Structure: 256 threads = 4 waves in a WM x WN grid; each wave owns a
-// (BM/WM) x (BN/WN) tile of 32x32 MFMA accumulators (v_mfma_f32_32x32x16_bf16).
-// K advances in steps of 64 through a double-buffered LDS stage filled from
-// registers; LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled
-// by (row & 7) so that the fragment reads hit distinct banks.  Work-groups
-// are remapped so that each XCD (hardware places work-group i on XCD i % 8)
-// receives a contiguous, L2-friendly block of tiles.
+// Structure: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
+// (BM/2) x (BN/2) tile of 32x32 MFMA accumulators (v_mfma_f32_32x32x16_bf16).
+// Two main-loop variants feed the MFMAs from LDS:
+//  * "dma": buffer_load ... lds moves 16-byte chunks straight from HBM into a
+//    ring of ST LDS stages (no staging registers, ST-1 tiles in flight);
+//  * "reg": buffer loads into two register stages, then ds_write into a
+//    double-buffered LDS stage (used where the DMA ring does not fit).
+// LDS rows hold BK bf16 with the 16-byte chunk index XOR-swizzled by row so
+// that the fragment reads of 16 consecutive rows hit distinct bank groups.
+// Work-groups are remapped so that each XCD (hardware places work-group i on
+// XCD i % 8) receives a contiguous, L2-friendly block of tiles.
 #include "kernels.h"
 
-#include <stdlib.h>
+#include <stdint.h>
 
 namespace tp {
 
 namespace {
 
-constexpr int BK = 64;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__ A, long long lda,
-                                                        const bf16* __restrict__ B, long long ldb, int M,
-                                                        int N, int K, Epilogue epi, int tiles_m,
-                                                        int tiles_n) {
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int CA = BM * 8 / 256, CB = BN * 8 / 256;  // 16-byte chunks per thread
-    static_assert(WM * WN == 4, "4 waves");
-    static_assert(FN % 2 == 0, "wave N-tile must cover whole 64-column groups");
-
-    __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * BK];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-
-    // ---- tile index: XCD-contiguous blocks, then grouped row-major order
-    int bid = blockIdx.x;
+// tile (tm, tn) of block b: XCD-contiguous ranges, then groups of GROUP tile rows
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int ntiles = tiles_m * tiles_n;
     if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
     constexpr int GROUP = 4;
     const int gsize = GROUP * tiles_n;
-    const int gidx = bid / gsize;
-    const int first_m = gidx * GROUP;
+    const int first_m = (bid / gsize) * GROUP;
     const int gm = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (bid % gsize) % gm;
-    const int tn = (bid % gsize) / gm;
-    const int m0 = tm * BM, n0 = tn * BN;
+    tm = first_m + (bid % gsize) % gm;
+    tn = (bid % gsize) / gm;
+}
 
-    // ---- global -> register staging assignment: thread t copies 16-byte chunk
-    // (t & 7) of rows (t >> 3) + 32 i; the swizzle (row & 7) is the same for all i.
-    const int srow = tid >> 3, skc = tid & 7;
-    const bf16* pa0 = A + skc * 8;
-    const bf16* pb0 = B + skc * 8;
-    long long oa[CA], ob[CB];
-#pragma unroll
-    for (int i = 0; i < CA; ++i) oa[i] = (long long)min(m0 + srow + 32 * i, M - 1) * lda;
-#pragma unroll
-    for (int i = 0; i < CB; ++i) ob[i] = (long long)min(n0 + srow + 32 * i, N - 1) * ldb;
-    const int l0 = srow * BK + ((skc ^ (srow & 7)) << 3);
+// 16-byte chunk slot of logical chunk c in LDS row r (CPR chunks per row)
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+    return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+}
 
-    bf16x8 ra[CA], rb[CB];
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
-
-    const int KT = K / BK;
-
-#pragma unroll
-    for (int i = 0; i < CA; ++i) ra[i] = *(const bf16x8*)(pa0 + oa[i]);
-#pragma unroll
-    for (int i = 0; i < CB; ++i) rb[i] = *(const bf16x8*)(pb0 + ob[i]);
-#pragma unroll
-    for (int i = 0; i < CA; ++i) *(bf16x8*)(&sA[0][l0 + i * 32 * BK]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) *(bf16x8*)(&sB[0][l0 + i * 32 * BK]) = rb[i];
-    __syncthreads();
-
-    // fragment read offsets (row part); row & 7 == lane & 7 since tile rows are 32-aligned
-    const int frow = lane & 31;
-    const int khalf = lane >> 5;
-    const int swz = lane & 7;
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) {
-            const int koff = (kt + 1) * BK;
-#pragma unroll
-            for (int i = 0; i < CA; ++i) ra[i] = *(const bf16x8*)(pa0 + oa[i] + koff);
-#pragma unroll
-            for (int i = 0; i < CB; ++i) rb[i] = *(const bf16x8*)(pb0 + ob[i] + koff);
-        }
-        const bf16* a_s = sA[cur];
-        const bf16* b_s = sB[cur];
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int kc = ((kk * 2 + khalf) ^ swz) << 3;
-            bf16x8 fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(a_s + (wm * TM + i * 32 + frow) * BK + kc);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(b_s + (wn * TN + j * 32 + frow) * BK + kc);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < CA; ++i) *(bf16x8*)(&sA[cur ^ 1][l0 + i * 32 * BK]) = ra[i];
-#pragma unroll
-            for (int i = 0; i < CB; ++i) *(bf16x8*)(&sB[cur ^ 1][l0 + i * 32 * BK]) = rb[i];
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue.  acc[i][j][r] sits at row 8*(r/4) + 4*(lane/32) + r%4 and
-    // column lane%32 of MFMA tile (i, j).
+// Write the accumulator tile of one wave.  acc[i][j][r] sits at row
+// 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of MFMA tile (i, j).
+template <int FM, int FN, int MODE>
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& epi, int lane, int wrow0,
+                                         int wcol0, int M, int N) {
     const int col_in = lane & 31;
     const int row_in = 4 * (lane >> 5);
-    const int wrow0 = m0 + wm * TM;
-    const int wcol0 = n0 + wn * TN;
-
     // Stores are predicated per element (no early exits): divergent control
     // flow around the accumulator tile makes the compiler spill it.
     if constexpr (MODE == EPI_F32) {
@@ -224,60 +143,311 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__
     }
 }
 
+// Direct-to-LDS load of one 16-byte chunk per lane: lane i of the wave lands
+// at LDS byte m0 + 16 i.  The compiler does not see this as an LDS write, so
+// it adds no conservative waits; the caller waits on vmcnt before the barrier
+// that publishes a stage.  M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+        : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15: no wait)
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    u32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// The MFMAs of one LDS stage.  Fragments of k-slice kk+1 are read before the
+// MFMAs of slice kk issue (the scheduling barriers keep that order), so the
+// LDS latency of every slice but the first hides behind 16-wide MFMA work.
+template <int FM, int FN, int BK, int CPR>
+__device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const bf16* a_s, const bf16* b_s, int frow,
+                                          int khalf) {
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int kk = 0; kk < BK / 16 + 1; ++kk) {
+        if (kk < BK / 16) {
+            const int c = swz<CPR>(frow, 2 * kk + khalf) << 3;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[kk & 1][i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[kk & 1][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk > 0) {
+            const int p = (kk - 1) & 1;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// DMA main loop: ST-stage LDS ring, tile k+ST-1 requested while tile k is used.
+template <int BM, int BN, int BK, int ST, int MODE>
+__global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ A, long long lda,
+                                                       const bf16* __restrict__ B, long long ldb, int M, int N,
+                                                       int K, Epilogue epi, int tiles_m, int tiles_n) {
+    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+    constexpr int CPR = BK / 8;              // 16-byte chunks per LDS row
+    constexpr int RPI = 64 / CPR;            // rows per wave-wide DMA (64 lanes x 16 B)
+    constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;  // DMAs per wave per stage
+    constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
+    static_assert(FN % 2 == 0 && IA >= 1 && IB >= 1, "tile shape");
+    __shared__ __attribute__((aligned(1024))) bf16 smem[ST * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // rows past M / N fall outside the resources and read as zeros
+    const u32x4_t rsa = make_rsrc(A + (long long)m0 * lda, (uint32_t)(min(BM, M - m0) * lda * 2));
+    const u32x4_t rsb = make_rsrc(B + (long long)n0 * ldb, (uint32_t)(min(BN, N - n0) * ldb * 2));
+    const int lrow = lane / CPR, lslot = lane % CPR;
+    uint32_t va[IA], vb[IB];
+#pragma unroll
+    for (int j = 0; j < IA; ++j) {
+        const int r = (wave * IA + j) * RPI + lrow;
+        va[j] = (uint32_t)((r * lda + 8 * swz<CPR>(r, lslot)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+        const int r = (wave * IB + j) * RPI + lrow;
+        vb[j] = (uint32_t)((r * ldb + 8 * swz<CPR>(r, lslot)) * 2);
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    auto issue = [&](int kt, int slot) {
+        const uint32_t soff = (uint32_t)(kt * BK * 2);
+        const uint32_t sa = lds0 + (uint32_t)(slot * STAGE * 2);
+        const uint32_t sb = sa + (uint32_t)(BM * BK * 2);
+#pragma unroll
+        for (int j = 0; j < IA; ++j)
+            dma16(rsa, va[j], soff, __builtin_amdgcn_readfirstlane(sa + (uint32_t)((wave * IA + j) * RPI * BK * 2)));
+#pragma unroll
+        for (int j = 0; j < IB; ++j)
+            dma16(rsb, vb[j], soff, __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave * IB + j) * RPI * BK * 2)));
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
+
+    const int KT = K / BK;
+    const int frow = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < ST - 1; ++s) issue(min(s, KT - 1), s);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        // tile kt has landed once at most the (ST-2) newer tiles are pending
+        wait_vm<(ST - 2) * (IA + IB)>();
+        __syncthreads();
+        // every wave is past tile kt-1: its slot takes tile kt+ST-1
+        issue(min(kt + ST - 1, KT - 1), (kt + ST - 1) % ST);
+        const bf16* a_s = smem + (kt % ST) * STAGE + (wm * TM + frow) * BK;
+        const bf16* b_s = smem + (kt % ST) * STAGE + BM * BK + (wn * TN + frow) * BK;
+        mma_stage<FM, FN, BK, CPR>(acc, a_s, b_s, frow, khalf);
+    }
+    wait_vm<0>();  // no LDS write may still be in flight when the work-group ends
+    epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged main loop (two register stages, double-buffered LDS, BK 64).
+template <int BM, int BN, int MODE>
+__global__ __launch_bounds__(256) void gemm_reg_kernel(const bf16* __restrict__ A, long long lda,
+                                                       const bf16* __restrict__ B, long long ldb, int M, int N,
+                                                       int K, Epilogue epi, int tiles_m, int tiles_n) {
+    constexpr int BK = 64;
+    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+    constexpr int CA = BM * 8 / 256, CB = BN * 8 / 256;  // 16-byte chunks per thread
+    static_assert(FN % 2 == 0, "wave N-tile must cover whole 64-column groups");
+    __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // thread t copies 16-byte chunk (t & 7) of tile rows (t >> 3) + 32 i; rows
+    // past M (or N) fall outside the buffer resources and read as zeros
+    const int srow = tid >> 3, skc = tid & 7;
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t rsa =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long long)m0 * lda), (short)0, rows_a * (int)lda * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(B + (long long)n0 * ldb), (short)0, rows_b * (int)ldb * 2, 0x00020000);
+    const int va0 = (srow * (int)lda + skc * 8) * 2;
+    const int vb0 = (srow * (int)ldb + skc * 8) * 2;
+    const int l0 = srow * BK + (swz<8>(srow, skc) << 3);   // (srow + 32 i) has the same swizzle
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
+
+    const int KT = K / BK;
+    const int frow = lane & 31, khalf = lane >> 5;
+    // Two register stages: the global loads of tile k+2 are issued before the
+    // MFMAs of tile k, so each load has two K-steps of compute to arrive.
+    // The loop body covers two tiles so that every register set is named
+    // statically.
+    u32x4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+#define TP_GLOAD(RA, RB, KT)                                                                             \
+    do {                                                                                                 \
+        const int koff_ = (KT) * BK * 2;                                                                 \
+        _Pragma("unroll") for (int i = 0; i < CA; ++i)                                                   \
+            RA[i] = __builtin_amdgcn_raw_buffer_load_b128(rsa, va0 + i * 32 * (int)lda * 2, koff_, 0);   \
+        _Pragma("unroll") for (int i = 0; i < CB; ++i)                                                   \
+            RB[i] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vb0 + i * 32 * (int)ldb * 2, koff_, 0);   \
+    } while (0)
+#define TP_LSTORE(RA, RB, BUF)                                                                           \
+    do {                                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < CA; ++i) *(u32x4*)(&sA[BUF][l0 + i * 32 * BK]) = RA[i];    \
+        _Pragma("unroll") for (int i = 0; i < CB; ++i) *(u32x4*)(&sB[BUF][l0 + i * 32 * BK]) = RB[i];    \
+    } while (0)
+#define TP_COMPUTE(BUF) \
+    mma_stage<FM, FN, BK, 8>(acc, sA[BUF] + (wm * TM + frow) * BK, sB[BUF] + (wn * TN + frow) * BK, frow, khalf)
+
+    TP_GLOAD(ra0, rb0, 0);
+    TP_GLOAD(ra1, rb1, min(1, KT - 1));
+    TP_LSTORE(ra0, rb0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        // buffer 0 holds tile kt; ra1/rb1 carry tile kt+1
+        TP_GLOAD(ra0, rb0, min(kt + 2, KT - 1));
+        TP_COMPUTE(0);
+        TP_LSTORE(ra1, rb1, 1);
+        __syncthreads();
+        // buffer 1 holds tile kt+1; ra0/rb0 carry tile kt+2
+        TP_GLOAD(ra1, rb1, min(kt + 3, KT - 1));
+        TP_COMPUTE(1);
+        if (kt + 2 < KT) TP_LSTORE(ra0, rb0, 0);
+        __syncthreads();
+    }
+    if (kt < KT) TP_COMPUTE(0);  // odd tile count: the last tile sits in buffer 0
+#undef TP_GLOAD
+#undef TP_LSTORE
+#undef TP_COMPUTE
+    epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+}
+
 struct Cfg {
     int bm, bn;
-    float eff;   // guessed relative MFMA efficiency of one work-group
+    float eff;   // relative MFMA efficiency of one work-group (measured on the 7B/70B shapes)
     int occ;     // work-groups per CU
 };
+// index: 0-2 register-staged, 3-8 DMA ring
 const Cfg kCfgs[] = {
-    {256, 256, 1.00f, 1},
-    {256, 128, 0.90f, 1},
-    {128, 128, 0.70f, 2},
-    {128, 256, 0.90f, 1},
+    {256, 128, 0.86f, 1},  // 0 reg 256x128
+    {128, 128, 0.90f, 2},  // 1 reg 128x128
+    {128, 256, 0.88f, 1},  // 2 reg 128x256
+    {256, 256, 1.00f, 1},  // 3 dma 256x256 BK64 ST2
+    {256, 256, 0.92f, 1},  // 4 dma 256x256 BK32 ST4
+    {256, 128, 0.95f, 1},  // 5 dma 256x128 BK64 ST3
+    {128, 128, 0.78f, 1},  // 6 dma 128x128 BK64 ST4
+    {128, 128, 0.90f, 2},  // 7 dma 128x128 BK64 ST2
+    {256, 128, 0.85f, 1},  // 8 dma 256x128 BK32 ST4
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
 
-template <int BM, int BN, int WM, int WN>
-void launch(const bf16* A, long long lda, const bf16* B, long long ldb, int M, int N, int K,
-            const Epilogue& epi, hipStream_t st) {
-    int tm = cdiv(M, BM), tn = cdiv(N, BN);
-    dim3 g(tm * tn), b(256);
-    switch (epi.mode) {
-        case EPI_F32:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_F32>), g, b, 0, st, A, lda, B, ldb, M, N, K, epi, tm, tn);
-            break;
-        case EPI_QKV:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), g, b, 0, st, A, lda, B, ldb, M, N, K, epi, tm, tn);
-            break;
-        case EPI_SWIGLU:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_SWIGLU>), g, b, 0, st, A, lda, B, ldb, M, N, K, epi, tm, tn);
-            break;
-        case EPI_GELU:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU>), g, b, 0, st, A, lda, B, ldb, M, N, K, epi, tm, tn);
-            break;
-        default:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE>), g, b, 0, st, A, lda, B, ldb, M, N, K, epi, tm, tn);
-            break;
+struct Args {
+    const bf16* A;
+    long long lda;
+    const bf16* B;
+    long long ldb;
+    int M, N, K;
+    Epilogue epi;
+    hipStream_t st;
+};
+
+template <int BM, int BN, int BK, int ST, int MODE>
+void launch_dma(const Args& a) {
+    const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, ST, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda, a.B,
+                       a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
+}
+template <int BM, int BN, int MODE>
+void launch_reg(const Args& a) {
+    const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    hipLaunchKernelGGL((gemm_reg_kernel<BM, BN, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda, a.B, a.ldb,
+                       a.M, a.N, a.K, a.epi, tm, tn);
+}
+
+template <int MODE>
+void launch_cfg(int c, const Args& a) {
+    switch (c) {
+        case 0: launch_reg<256, 128, MODE>(a); break;
+        case 1: launch_reg<128, 128, MODE>(a); break;
+        case 2: launch_reg<128, 256, MODE>(a); break;
+        case 3: launch_dma<256, 256, 64, 2, MODE>(a); break;
+        case 4: launch_dma<256, 256, 32, 4, MODE>(a); break;
+        case 5: launch_dma<256, 128, 64, 3, MODE>(a); break;
+        case 6: launch_dma<128, 128, 64, 4, MODE>(a); break;
+        case 7: launch_dma<128, 128, 64, 2, MODE>(a); break;
+        default: launch_dma<256, 128, 32, 4, MODE>(a); break;
     }
 }
 
-// The 256x256 tile keeps 256 accumulators per lane; with the rotary and the
-// erf epilogues the compiler spills them, so those modes skip it.
-bool usable(int c, int mode) { return !(c == 0 && (mode == EPI_QKV || mode == EPI_GELU)); }
+// Tiles of 256 rows and columns keep 256 accumulators per lane; with the
+// rotary and the erf epilogues the register-staged kernel spills them.
+bool usable(int c, int mode) {
+    return !(kCfgs[c].bm == 256 && kCfgs[c].bn == 256 && (mode == EPI_QKV || mode == EPI_GELU));
+}
 
+// Shape-based choice.  Large problems (at least 1.5 waves of 256x256 tiles)
+// take the 256x256 DMA ring, which has the highest per-CU efficiency.
+// Otherwise the modelled time of a configuration is the number of tiles the
+// busiest CU runs times the tile's work over its efficiency; the DMA rings
+// lose 20% with the rotary epilogue (measured on the 7B Q/K/V projection).
 int pick(int M, int N, int mode) {
     if (g_forced_cfg >= 0 && g_forced_cfg < kNumCfg && usable(g_forced_cfg, mode)) return g_forced_cfg;
+    if (usable(3, mode) && (long long)cdiv(M, 256) * cdiv(N, 256) >= 384) return 3;
     int best = 1;
     double best_t = 1e30;
     for (int c = 0; c < kNumCfg; ++c) {
         if (!usable(c, mode)) continue;
         const Cfg& f = kCfgs[c];
-        long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
-        long long slots = 256LL * f.occ;
-        long long waves = (tiles + slots - 1) / slots;
-        double t = (double)waves * f.bm * f.bn * f.occ / f.eff;
-        if (t < best_t * 0.999) { best_t = t; best = c; }
+        const long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
+        const double eff = f.eff * ((c >= 3 && mode == EPI_QKV) ? 0.8 : 1.0);
+        const double t = (double)((tiles + 255) / 256) * f.bm * f.bn / eff;
+        if (t < best_t * 0.999) {
+            best_t = t;
+            best = c;
+        }
     }
     return best;
 }
@@ -289,11 +459,14 @@ int gemm_config_count() { return kNumCfg; }
 
 void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M, int N, int K,
                const Epilogue& epi, hipStream_t st) {
-    switch (pick(M, N, epi.mode)) {
-        case 0: launch<256, 256, 2, 2>(A, lda, B, ldb, M, N, K, epi, st); break;
-        case 1: launch<256, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, st); break;
-        case 2: launch<128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, st); break;
-        default: launch<128, 256, 2, 2>(A, lda, B, ldb, M, N, K, epi, st); break;
+    const Args a{A, lda, B, ldb, M, N, K, epi, st};
+    const int c = pick(M, N, epi.mode);
+    switch (epi.mode) {
+        case EPI_F32: launch_cfg<EPI_F32>(c, a); break;
+        case EPI_QKV: launch_cfg<EPI_QKV>(c, a); break;
+        case EPI_SWIGLU: launch_cfg<EPI_SWIGLU>(c, a); break;
+        case EPI_GELU: launch_cfg<EPI_GELU>(c, a); break;
+        default: launch_cfg<EPI_STORE>(c, a); break;
     }
 }
 

@@ -337,3 +337,31 @@ def test_70b_t8_decode_full(layer70b):
     torch.cuda.synchronize()
     refm = O.mlp_stage(h.float().numpy()[:, None], L.W, L.spec, 8, 0)
     assert_close(to_np(pm), refm["partial"][:, 0], "70B decode mlp partial", "bf16")
+
+
+# ---------------------------------------------------------------- every GEMM tile configuration
+
+@pytest.mark.parametrize("ffn", [2816, 2688])   # FFN shard 1408 (22 K-steps of 64) and 1344 (21: odd)
+def test_every_gemm_config(ffn):
+    """Each projection tile configuration (register-staged and DMA-ring
+    variants), forced in turn, on a ragged token count, against the oracle."""
+    from tensor_transformer_layer_tp_amd import set_gemm_config
+    from tensor_transformer_layer_tp_amd import _native as N
+    announce(f"every GEMM configuration, ffn={ffn}")
+    L = Layer(1024, 8, 4, ffn, batch=1, seq=300, gamma_noise=True, seed=13)
+    h = synth.to_storage(synth.draw_normal((1, 300, 1024), 14), "bf16")
+    ref_a = O.attn_stage(L.exact["x"], L.W, L.spec, 2, 1)
+    ref_m = O.mlp_stage(h.float().numpy(), L.W, L.spec, 2, 1)
+    sh = L.shard(2, 1)
+    n_cfg = 9
+    assert N.lib().tp_tune_set_gemm_config(n_cfg) == N.TP_E_ARG   # the table has exactly n_cfg entries
+    try:
+        for cfg in range(n_cfg):
+            set_gemm_config(cfg)
+            pa = sh.prefill(ATTN, L.dev["x"], out=nan_like((1, 300, 1024)))
+            pm = sh.prefill(MLP, h.cuda(), out=nan_like((1, 300, 1024)))
+            torch.cuda.synchronize()
+            assert_close(to_np(pa), ref_a["partial"], f"cfg {cfg} attn partial", "bf16")
+            assert_close(to_np(pm), ref_m["partial"], f"cfg {cfg} mlp partial", "bf16")
+    finally:
+        set_gemm_config(-1)
