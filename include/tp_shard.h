@@ -186,8 +186,11 @@ int tp_shard_debug_view(tp_shard *s, int which, void **ptr);
  * launches is bracketed by two hipEvents recorded on the launch stream, and
  * the elapsed times are summed per kernel kind.  Recording adds a marker
  * between kernels, so time whole steps with the timer off.
- * tp_shard_timing(s, 1) enables and resets the sums (it creates the event
- * pool on first use); tp_shard_timing(s, 0) stops recording.
+ * tp_shard_timing(s, mask) enables and resets the sums (it creates the event
+ * pool on first use): mask -1 brackets every kernel kind, any other nonzero
+ * mask only the kinds k with bit (1 << k) set (TP_K_MASK), so that a timed
+ * run can bracket just the kernel of interest; tp_shard_timing(s, 0) stops
+ * recording.
  * tp_shard_timing_read waits for the recorded events and returns the total
  * milliseconds and launch count of one kernel kind (TP_K_*). */
 #define TP_K_RMSNORM      0
@@ -202,6 +205,7 @@ int tp_shard_debug_view(tp_shard *s, int which, void **ptr);
 #define TP_K_GEMV_UP      9
 #define TP_K_GEMV_DOWN    10
 #define TP_K_COUNT        11
+#define TP_K_MASK(k)      (1 << (k))
 int tp_shard_timing(tp_shard *s, int enable);
 int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *launches);
 

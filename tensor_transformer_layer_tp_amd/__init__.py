@@ -209,9 +209,13 @@ class Shard:
         _memcpy_d2d(t.data_ptr(), p.value, t.numel() * self.elem_size, stream)
         return t
 
-    def timing(self, enable: bool) -> None:
-        """Turn the per-kernel event timer on (resetting it) or off."""
-        N.check(N.lib().tp_shard_timing(self._h, int(enable)), "tp_shard_timing")
+    def timing(self, enable, kinds=None) -> None:
+        """Turn the per-kernel event timer on (resetting it) or off; ``kinds``
+        limits it to the named kernel kinds (see _native.KERNEL_KINDS)."""
+        mask = 0
+        if enable:
+            mask = -1 if kinds is None else sum(1 << N.KERNEL_KINDS.index(k) for k in kinds)
+        N.check(N.lib().tp_shard_timing(self._h, mask), "tp_shard_timing")
 
     def timing_read(self) -> dict:
         """{kernel kind: (total ms, launches)} of the recorded launches."""

@@ -180,28 +180,39 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // The MFMAs of one LDS stage.  Fragments of k-slice kk+1 are read before the
 // MFMAs of slice kk issue (the scheduling barriers keep that order), so the
 // LDS latency of every slice but the first hides behind 16-wide MFMA work.
+template <int FM, int FN>
+__device__ __forceinline__ void interleave_reads_mfma() {
+    // one fragment read, then its share of the MFMAs, repeated: keeps both the
+    // LDS and the matrix pipe busy instead of queueing all reads up front
+#pragma unroll
+    for (int q = 0; q < FM + FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);                      // DS read
+        __builtin_amdgcn_sched_group_barrier(0x0008, FM * FN / (FM + FN), 0);    // MFMA
+    }
+}
+
 template <int FM, int FN, int BK, int CPR>
 __device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const bf16* a_s, const bf16* b_s, int frow,
                                           int khalf) {
     bf16x8 fa[2][FM], fb[2][FN];
+    auto rd = [&](int kk, int buf) {
+        const int c = swz<CPR>(frow, 2 * kk + khalf) << 3;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16 + 1; ++kk) {
-        if (kk < BK / 16) {
-            const int c = swz<CPR>(frow, 2 * kk + khalf) << 3;
+        for (int i = 0; i < FM; ++i) fa[buf][i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[kk & 1][i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
+        for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
+    };
+    rd(0, 0);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[kk & 1][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk > 0) {
-            const int p = (kk - 1) & 1;
+    for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < BK / 16) rd(kk + 1, cur ^ 1);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
-        }
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        if (kk + 1 < BK / 16) interleave_reads_mfma<FM, FN>();
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -275,6 +286,138 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ 
         const bf16* a_s = smem + (kt % ST) * STAGE + (wm * TM + frow) * BK;
         const bf16* b_s = smem + (kt % ST) * STAGE + BM * BK + (wn * TN + frow) * BK;
         mma_stage<FM, FN, BK, CPR>(acc, a_s, b_s, frow, khalf);
+    }
+    wait_vm<0>();  // no LDS write may still be in flight when the work-group ends
+    epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+}
+
+// ---------------------------------------------------------------------------
+// DMA main loop for rings of ST >= 3 stages, software-pipelined across the
+// stage boundary: the barrier that publishes tile k+1, the DMA request for
+// tile k+ST-1 and the first fragment reads of tile k+1 all happen before the
+// MFMAs of tile k's last k-slice, and the DMA requests are interleaved with
+// those MFMAs, so the matrix pipe keeps issuing across the boundary.  The
+// DMA of a tile always targets the slot of the tile before the current one,
+// whose fragment reads completed before that tile's MFMAs issued.
+template <int BM, int BN, int BK, int ST, int MODE>
+__global__ __launch_bounds__(256) void gemm_dma_pipe_kernel(const bf16* __restrict__ A, long long lda,
+                                                            const bf16* __restrict__ B, long long ldb, int M,
+                                                            int N, int K, Epilogue epi, int tiles_m, int tiles_n) {
+    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+    constexpr int CPR = BK / 8;
+    constexpr int RPI = 64 / CPR;
+    constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int KK = BK / 16;
+    static_assert(ST >= 3 && FN % 2 == 0 && IA >= 1 && IB >= 1, "tile shape");
+    __shared__ __attribute__((aligned(1024))) bf16 smem[ST * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA addressing scalar
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const u32x4_t rsa = make_rsrc(A + (long long)m0 * lda, (uint32_t)(min(BM, M - m0) * lda * 2));
+    const u32x4_t rsb = make_rsrc(B + (long long)n0 * ldb, (uint32_t)(min(BN, N - n0) * ldb * 2));
+    const int lrow = lane / CPR, lslot = lane % CPR;
+    uint32_t vab[IA + IB];
+#pragma unroll
+    for (int j = 0; j < IA; ++j) {
+        const int r = (wave * IA + j) * RPI + lrow;
+        vab[j] = (uint32_t)((r * lda + 8 * swz<CPR>(r, lslot)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+        const int r = (wave * IB + j) * RPI + lrow;
+        vab[IA + j] = (uint32_t)((r * ldb + 8 * swz<CPR>(r, lslot)) * 2);
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    // LDS byte address of DMA j of this wave in stage `slot`
+    auto dma_lds = [&](int slot, int j) -> uint32_t {
+        const uint32_t base = lds0 + (uint32_t)(slot * STAGE * 2);
+        return j < IA ? base + (uint32_t)((wave * IA + j) * RPI * BK * 2)
+                      : base + (uint32_t)(BM * BK * 2 + (wave * IB + (j - IA)) * RPI * BK * 2);
+    };
+    auto dma = [&](int j, int kt, int slot) {
+        dma16(j < IA ? rsa : rsb, vab[j], (uint32_t)(kt * BK * 2), __builtin_amdgcn_readfirstlane(dma_lds(slot, j)));
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
+
+    const int KT = K / BK;
+    const int frow = lane & 31, khalf = lane >> 5;
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto read = [&](int slot, int kk, int buf) {
+        const bf16* a_s = smem + slot * STAGE + (wm * TM + frow) * BK;
+        const bf16* b_s = smem + slot * STAGE + BM * BK + (wn * TN + frow) * BK;
+        const int c = swz<CPR>(frow, 2 * kk + khalf) << 3;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
+    };
+    auto mma = [&](int buf, int i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
+
+#pragma unroll
+    for (int t = 0; t < ST - 1; ++t)
+#pragma unroll
+        for (int j = 0; j < IA + IB; ++j) dma(j, min(t, KT - 1), t);
+    wait_vm<(ST - 2) * (IA + IB)>();
+    __syncthreads();
+    read(0, 0, 0);
+
+    // all tiles but the last: no branch inside the body (a branch here makes
+    // the compiler shuffle the accumulators between register ranges)
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        const int slot = kt % ST;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < KK) {
+                read(slot, kk + 1, nxt);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) mma(cur, i);
+                interleave_reads_mfma<FM, FN>();
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // tile kt+1 must have landed: only the ST-3 newer tiles may be pending
+                wait_vm<(ST - 3) * (IA + IB)>();
+                __syncthreads();
+                const int dslot = (kt + ST - 1) % ST, dtile = min(kt + ST - 1, KT - 1);
+                // interleave: one MFMA row group, then a share of the DMA requests
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    mma(cur, i);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = i * (IA + IB) / FM; j < (i + 1) * (IA + IB) / FM; ++j) dma(j, dtile, dslot);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (i == 0) {
+                        read((kt + 1) % ST, 0, nxt);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+    }
+    {
+        const int slot = (KT - 1) % ST;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < KK) read(slot, kk + 1, nxt);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) mma(cur, i);
+        }
     }
     wait_vm<0>();  // no LDS write may still be in flight when the work-group ends
     epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
@@ -375,7 +518,7 @@ const Cfg kCfgs[] = {
     {128, 128, 0.90f, 2},  // 1 reg 128x128
     {128, 256, 0.88f, 1},  // 2 reg 128x256
     {256, 256, 1.00f, 1},  // 3 dma 256x256 BK64 ST2
-    {256, 256, 0.92f, 1},  // 4 dma 256x256 BK32 ST4
+    {256, 256, 1.03f, 1},  // 4 dma 256x256 BK32 ST4
     {256, 128, 0.95f, 1},  // 5 dma 256x128 BK64 ST3
     {128, 128, 0.78f, 1},  // 6 dma 128x128 BK64 ST4
     {128, 128, 0.90f, 2},  // 7 dma 128x128 BK64 ST2
@@ -400,6 +543,12 @@ void launch_dma(const Args& a) {
     hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, ST, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda, a.B,
                        a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
 }
+template <int BM, int BN, int BK, int ST, int MODE>
+void launch_pipe(const Args& a) {
+    const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    hipLaunchKernelGGL((gemm_dma_pipe_kernel<BM, BN, BK, ST, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda,
+                       a.B, a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
+}
 template <int BM, int BN, int MODE>
 void launch_reg(const Args& a) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
@@ -414,11 +563,11 @@ void launch_cfg(int c, const Args& a) {
         case 1: launch_reg<128, 128, MODE>(a); break;
         case 2: launch_reg<128, 256, MODE>(a); break;
         case 3: launch_dma<256, 256, 64, 2, MODE>(a); break;
-        case 4: launch_dma<256, 256, 32, 4, MODE>(a); break;
-        case 5: launch_dma<256, 128, 64, 3, MODE>(a); break;
-        case 6: launch_dma<128, 128, 64, 4, MODE>(a); break;
+        case 4: launch_pipe<256, 256, 32, 4, MODE>(a); break;
+        case 5: launch_pipe<256, 128, 64, 3, MODE>(a); break;
+        case 6: launch_pipe<128, 128, 64, 4, MODE>(a); break;
         case 7: launch_dma<128, 128, 64, 2, MODE>(a); break;
-        default: launch_dma<256, 128, 32, 4, MODE>(a); break;
+        default: launch_pipe<256, 128, 32, 4, MODE>(a); break;
     }
 }
 
@@ -429,13 +578,13 @@ bool usable(int c, int mode) {
 }
 
 // Shape-based choice.  Large problems (at least 1.5 waves of 256x256 tiles)
-// take the 256x256 DMA ring, which has the highest per-CU efficiency.
+// take the 4-stage 256x256 DMA ring, which has the highest per-CU efficiency.
 // Otherwise the modelled time of a configuration is the number of tiles the
 // busiest CU runs times the tile's work over its efficiency; the DMA rings
 // lose 20% with the rotary epilogue (measured on the 7B Q/K/V projection).
 int pick(int M, int N, int mode) {
     if (g_forced_cfg >= 0 && g_forced_cfg < kNumCfg && usable(g_forced_cfg, mode)) return g_forced_cfg;
-    if (usable(3, mode) && (long long)cdiv(M, 256) * cdiv(N, 256) >= 384) return 3;
+    if (usable(4, mode) && (long long)cdiv(M, 256) * cdiv(N, 256) >= 384) return 4;
     int best = 1;
     double best_t = 1e30;
     for (int c = 0; c < kNumCfg; ++c) {

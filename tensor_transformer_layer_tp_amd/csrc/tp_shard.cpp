@@ -39,6 +39,7 @@ struct tp_shard {
     size_t off_n, off_o, off_act;
     // kernel timer: event pairs in launch order and the kind of each pair
     bool timing;
+    unsigned tmask;   // kernel kinds being bracketed (bit k = TP_K_k)
     std::vector<hipEvent_t> ev;
     std::vector<int> evkind;
     size_t evused;
@@ -199,7 +200,7 @@ struct KTimer {
     size_t slot;
     bool on;
     KTimer(tp_shard* s_, int kind, hipStream_t st_) : s(s_), st(st_), slot(0), on(false) {
-        if (s->timing && s->evused + 2 <= s->ev.size()) {
+        if (s->timing && ((s->tmask >> kind) & 1u) && s->evused + 2 <= s->ev.size()) {
             on = true;
             slot = s->evused;
             s->evused += 2;
@@ -612,6 +613,7 @@ int tp_shard_timing(tp_shard* s, int enable) {
         s->evkind.clear();
     }
     s->timing = enable != 0;
+    s->tmask = enable == -1 ? 0xffffffffu : (unsigned)enable;
     return TP_OK;
 }
 
