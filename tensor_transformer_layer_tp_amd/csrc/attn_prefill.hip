@@ -32,6 +32,14 @@ __device__ __forceinline__ int vt_pos(int k) {
     return (j << 4) + (((w >> 2) & 1) << 3) + (w & 3) + ((w >> 3) << 2);
 }
 
+// 16-byte chunk slot of chunk c in LDS row r: 16 lanes reading 16 consecutive
+// rows hit 16 distinct bank groups (256-byte rows: r & 15; 128-byte rows:
+// consecutive even and odd rows alternate halves, so (r >> 1) & 7).
+template <int CPR>
+__device__ __forceinline__ int kslot(int r, int c) {
+    return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                            const bf16* __restrict__ V, bf16* __restrict__ O,
@@ -79,7 +87,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
             const int key = idx / KC, dc = idx % KC;
             const int gk = min(k0 + key, S - 1);
             const bf16x8 v = *(const bf16x8*)(Kb + (long long)gk * D + dc * 8);
-            *(bf16x8*)(sK + key * D + ((dc ^ (key & (KC - 1))) << 3)) = v;
+            *(bf16x8*)(sK + key * D + (kslot<KC>(key, dc) << 3)) = v;
         }
         // V block -> LDS transposed [dim][permuted key], two keys per 32-bit store
 #pragma unroll
@@ -90,11 +98,16 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
             const u16x8 v0 = *(const u16x8*)(Vb + (long long)g0 * D + dc * 8);
             const u16x8 v1 = *(const u16x8*)(Vb + (long long)g1 * D + dc * 8);
             const int p = vt_pos(2 * a);
+            const bool hi = (lane >> 5) != 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int dim = dc * 8 + e;
-                const int off = dim * BKV + ((((p >> 3) ^ (dim & 7)) << 3) | (p & 7));
-                *(uint32_t*)(sVt + off) = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+            for (int e0 = 0; e0 < 8; ++e0) {
+                // the two 32-lane halves write rows of opposite parity (distinct banks);
+                // register indices stay static, the upper half takes the partner element
+                const uint32_t a0 = hi ? v0[e0 ^ 1] : v0[e0];
+                const uint32_t a1 = hi ? v1[e0 ^ 1] : v1[e0];
+                const int dim = dc * 8 + (e0 ^ (int)hi);
+                const int off = dim * BKV + ((((p >> 3) ^ ((dim >> 1) & 7)) << 3) | (p & 7));
+                *(uint32_t*)(sVt + off) = a0 | (a1 << 16);
             }
         }
         __syncthreads();
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
             const int krow = 32 * t + col;
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
-                const bf16x8 a = *(const bf16x8*)(sK + krow * D + (((2 * kk + h) ^ (krow & (KC - 1))) << 3));
+                const bf16x8 a = *(const bf16x8*)(sK + krow * D + (kslot<KC>(krow, 2 * kk + h) << 3));
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[t], 0, 0, 0);
             }
         }
@@ -125,14 +138,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         float lsum = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(st[t][r] - m_new);
+                const float p = __builtin_amdgcn_exp2f(st[t][r] - m_new);
                 st[t][r] = p;
                 lsum += p;
             }
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const int dim = 32 * i + col;
-                const bf16x8 a = *(const bf16x8*)(sVt + dim * BKV + ((((2 * j + h) ^ (dim & 7))) << 3));
+                const bf16x8 a = *(const bf16x8*)(sVt + dim * BKV + (((2 * j + h) ^ ((dim >> 1) & 7)) << 3));
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
             }
         }

@@ -14,14 +14,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f2bf_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ bf16 f2bf(float f) { return __builtin_bit_cast(bf16, f2bf_bits(f)); }
+// fp32 -> bf16, round to nearest even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, RNE under the default rounding mode, NaN kept NaN).
+__device__ __forceinline__ bf16 f2bf(float f) { return (bf16)f; }
+__device__ __forceinline__ uint16_t f2bf_bits(float f) { return __builtin_bit_cast(uint16_t, (bf16)f); }
 __device__ __forceinline__ float bf2f(bf16 b) {
     return __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, b)) << 16);
 }
