@@ -18,10 +18,12 @@ namespace {
 //
 // A work-group owns P row pairs (rows r and r + 32 of one 64-row group of the
 // packed weight; see packed_to_dim) so that the RoPE / SwiGLU partners meet in
-// one work-group.  All 256 threads sweep K together in 16-byte chunks (each
-// row is read as contiguous 4 KB bursts), then the per-thread sums are
-// reduced across the work-group.
-template <int NB, int P, int MODE, bool NORM>
+// one work-group.  Thread t owns the 16-byte K-chunks t + 256 i (i < NI), so
+// the 256 threads sweep each row in contiguous 4 KB bursts.  Every weight load
+// of the thread is issued first; the norm's sum of squares comes from the same
+// x chunks while those loads are in flight (the thread chunks together cover
+// all of K, so one work-group reduction gives the whole row's sum).
+template <int NB, int P, int NI, int MODE, bool NORM>
 __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, const bf16* __restrict__ gamma,
                                                    float eps, const bf16* __restrict__ W, int N, int K,
                                                    Epilogue epi) {
@@ -34,26 +36,44 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
     const int rbase = 64 * grp + P * sub;   // rows rbase + e and rbase + 32 + e, e < P
     const int KC = K >> 3;
 
+    int cofs[NI];
+    bool valid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int c = tid + 256 * i;
+        valid[i] = c < KC;
+        cofs[i] = min(c, KC - 1) * 8;   // clamped: every load is issued and in bounds
+    }
+    u16x8 wv[R][NI];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bf16* wrow = W + (long long)(rbase + (r < P ? r : 32 + r - P)) * K;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wv[r][i] = *(const u16x8*)(wrow + cofs[i]);
+    }
+    u16x8 xv[NB][NI];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) xv[b][i] = *(const u16x8*)(x + (long long)b * K + cofs[i]);
+
     float rs[NB];
+    u16x8 gv[NI];
     if constexpr (NORM) {
-        float ss[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) ss[b] = 0.f;
-        for (int c = tid; c < KC; c += 256) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const u16x8 v = *(const u16x8*)(x + (long long)b * K + c * 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = bfbits2f(v[e]);
-                    ss[b] += f * f;
-                }
-            }
-        }
+        for (int i = 0; i < NI; ++i) gv[i] = *(const u16x8*)(gamma + cofs[i]);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const float s = wave_sum(ss[b]);
-            if (lane == 0) red[wave][b] = s;
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = bfbits2f(xv[b][i][e]);
+                    ss += valid[i] ? f * f : 0.f;
+                }
+            ss = wave_sum(ss);
+            if (lane == 0) red[wave][b] = ss;
         }
         __syncthreads();
         if (tid < NB) rs_s[tid] = rsqrtf((red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) / (float)K + eps);
@@ -67,39 +87,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-
-    const bf16* wrow[R];
 #pragma unroll
-    for (int e = 0; e < P; ++e) {
-        wrow[e] = W + (long long)(rbase + e) * K;
-        wrow[P + e] = W + (long long)(rbase + 32 + e) * K;
-    }
-
-    for (int c = tid; c < KC; c += 256) {
-        u16x8 wv[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) wv[r] = *(const u16x8*)(wrow[r] + c * 8);
-        float xin[NB][8];
-        u16x8 gv;
-        if constexpr (NORM) gv = *(const u16x8*)(gamma + c * 8);
+    for (int i = 0; i < NI; ++i) {
+        if (!valid[i]) continue;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const u16x8 xv = *(const u16x8*)(x + (long long)b * K + c * 8);
+            float xin[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float f = bfbits2f(xv[e]);
-                if constexpr (NORM) f = round_bf(f * rs[b] * bfbits2f(gv[e]));
-                xin[b][e] = f;
+                float f = bfbits2f(xv[b][i][e]);
+                if constexpr (NORM) f = round_bf(f * rs[b] * bfbits2f(gv[i][e]));
+                xin[e] = f;
             }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[r][b] += bfbits2f(wv[r][i][e]) * xin[e];
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float w = bfbits2f(wv[r][e]);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) acc[r][b] += w * xin[b][e];
-            }
     }
 
     // reduce: wave sums, then across the 4 waves
@@ -141,9 +145,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
         float o1 = y1, o2 = y2;
         if (region < 2 && q.rope_cos != nullptr) {
             const float c = q.rope_cos[(long long)q.pos0 * half + i1];
-            const float s = q.rope_sin[(long long)q.pos0 * half + i1];
-            o1 = y1 * c - y2 * s;
-            o2 = y2 * c + y1 * s;
+            const float sn = q.rope_sin[(long long)q.pos0 * half + i1];
+            o1 = y1 * c - y2 * sn;
+            o2 = y2 * c + y1 * sn;
         }
         bf16* dst = region == 0 ? (bf16*)q.q + ((long long)b * q.hl + head) * d
                                 : (bf16*)(region == 1 ? q.k : q.v) +
@@ -260,46 +264,88 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     }
 }
 
+// Merge the chunks of one (batch, query head).  The chunk maxima are reduced
+// in parallel; the chunk weights exp2(m_c - M) go to LDS a tile of 1024
+// chunks at a time, and each thread (one head dim) sums the chunks' outputs
+// with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
                                                          int hl, int nchunks) {
-    const int head = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+    constexpr int NW = D / 64, TILE = 1024;
+    __shared__ float sw[TILE];
+    __shared__ float sred[NW];
+    const int head = blockIdx.x, b = blockIdx.y, dim = threadIdx.x, lane = dim & 63, wave = dim >> 6;
     const float* st = scr + ((long long)b * hl + head) * nchunks * (D + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, st[c * (D + 2) + D]);
-    float L = 0.f, acc = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-        const float w = exp2f(st[c * (D + 2) + D] - M);
-        L += w * st[c * (D + 2) + D + 1];
-        acc += w * st[c * (D + 2) + dim];
+    float m = -INFINITY;
+    for (int c = dim; c < nchunks; c += D) m = fmaxf(m, st[c * (D + 2) + D]);
+    m = wave_max(m);
+    if (lane == 0) sred[wave] = m;
+    __syncthreads();
+    float M = sred[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sred[w]);
+    float l = 0.f, acc = 0.f;
+    for (int c0 = 0; c0 < nchunks; c0 += TILE) {
+        const int n = min(TILE, nchunks - c0);
+        __syncthreads();
+        for (int c = dim; c < n; c += D) {
+            const float* sc = st + (c0 + c) * (D + 2);
+            const float w = __builtin_amdgcn_exp2f(sc[D] - M);
+            sw[c] = w;
+            l += w * sc[D + 1];
+        }
+        __syncthreads();
+        for (int c = 0; c < n; ++c) acc += sw[c] * st[(c0 + c) * (D + 2) + dim];
     }
+    l = wave_sum(l);
+    __syncthreads();
+    if (lane == 0) sred[wave] = l;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += sred[w];
     O[((long long)b * hl + head) * D + dim] = f2bf(acc / L);
 }
 
-template <int NB, int P, bool NORM>
+template <int NB, int P, int NI, bool NORM>
 void gemv_mode(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
                hipStream_t st) {
     dim3 g(N / (2 * P)), b(256);
     switch (epi.mode) {
-        case EPI_F32: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_F32, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_QKV, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_SWIGLU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        case EPI_GELU: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_GELU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        default: hipLaunchKernelGGL((gemv_kernel<NB, P, EPI_STORE, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_F32: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_F32, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_QKV, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_SWIGLU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_GELU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_GELU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        default: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_STORE, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
     }
+}
+
+template <int NB, int NI>
+void gemv_ni(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
+             hipStream_t st) {
+    // 8 rows per work-group keep 8 x NI loads in flight per thread; 4 rows when
+    // 8 would leave the GPU short of work-groups or the thread short of registers
+    if constexpr (NI <= 2) {
+        if (N / 8 >= 512) {
+            if (gamma) gemv_mode<NB, 4, NI, true>(x, gamma, eps, W, N, K, epi, st);
+            else gemv_mode<NB, 4, NI, false>(x, gamma, eps, W, N, K, epi, st);
+            return;
+        }
+    }
+    if (gamma) gemv_mode<NB, 2, NI, true>(x, gamma, eps, W, N, K, epi, st);
+    else gemv_mode<NB, 2, NI, false>(x, gamma, eps, W, N, K, epi, st);
 }
 
 template <int NB>
 void gemv_nb(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
              hipStream_t st) {
-    // 4 rows per work-group when 8 would leave the GPU short of work-groups
-    const bool small = N / 8 < 512;
-    if (gamma) {
-        if (small) gemv_mode<NB, 2, true>(x, gamma, eps, W, N, K, epi, st);
-        else gemv_mode<NB, 4, true>(x, gamma, eps, W, N, K, epi, st);
-    } else {
-        if (small) gemv_mode<NB, 2, false>(x, gamma, eps, W, N, K, epi, st);
-        else gemv_mode<NB, 4, false>(x, gamma, eps, W, N, K, epi, st);
+    const int ni = ((K >> 3) + 255) / 256;   // 16-byte chunks per thread (K <= 16384)
+    switch (ni) {
+        case 1: gemv_ni<NB, 1>(x, gamma, eps, W, N, K, epi, st); break;
+        case 2: gemv_ni<NB, 2>(x, gamma, eps, W, N, K, epi, st); break;
+        case 3: gemv_ni<NB, 3>(x, gamma, eps, W, N, K, epi, st); break;
+        case 4: gemv_ni<NB, 4>(x, gamma, eps, W, N, K, epi, st); break;
+        default: gemv_ni<NB, 8>(x, gamma, eps, W, N, K, epi, st); break;
     }
 }
 

@@ -202,8 +202,10 @@ int launch_norm(tp_shard* s, const void* x, const void* g, void* out, long long 
     return TP_OK;
 }
 
-// decode projections at batch <= 8 stream the weights through the GEMV kernel
+// decode projections at batch <= 8 stream the weights through the GEMV kernel,
+// whose threads hold a whole input row in registers (K <= 16384)
 constexpr int kGemvMaxBatch = 8;
+constexpr int kGemvMaxK = 16384;
 
 int launch_gemv(tp_shard* s, const void* x, int B, const void* gamma, const void* W, int N, int K,
                 const Epilogue& epi, hipStream_t st) {
@@ -498,7 +500,8 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
     if (!s->loaded) return TP_E_STATE;
     hipStream_t st = (hipStream_t)stream;
     const bool bf = s->o.dtype == TP_BF16;
-    const bool use_gemv = bf && batch <= kGemvMaxBatch;
+    const bool use_gemv = bf && batch <= kGemvMaxBatch && s->hidden <= kGemvMaxK && s->hl * s->d <= kGemvMaxK &&
+                          s->fl <= kGemvMaxK;
     if (stage == TP_STAGE_ATTN) {
         if (!kv) return TP_E_ARG;
         if (kv->batch != batch || kv->dtype != s->o.dtype || kv->kvl != s->kvl) return TP_E_ARG;

@@ -192,6 +192,56 @@ def test_decode_steps_match_oracle(B):
     assert_close(to_np(pm), ref["partial"][:, 0], "decode mlp partial", "bf16")
 
 
+@pytest.mark.parametrize("hidden,heads,kv,ffn,tp,B", [
+    (768, 6, 6, 6144, 1, 2),      # K = 768 and 6144: 1 and 3 chunks of 2048 per thread
+    (512, 4, 2, 11008, 1, 4),     # K = 11008: 6 chunks (8-chunk variant, ragged)
+    (256, 2, 2, 20480, 1, 1),     # FFN shard 20480 > 16384: decode falls back to the GEMM path
+    (2048, 32, 8, 2816, 2, 7),    # 16 local heads, 4 KV heads (G = 4), batch split 4 + 3
+])
+def test_decode_gemv_shapes(hidden, heads, kv, ffn, tp, B):
+    announce(f"bf16 decode shapes hidden={hidden} heads={heads}/{kv} ffn={ffn} t={tp} B={B}")
+    S = 70
+    L = Layer(hidden, heads, kv, ffn, batch=B, seq=S + 1, gamma_noise=True, seed=21)
+    r = tp - 1
+    sh = L.shard(tp, r)
+    kvc = sh.kv_cache(B, S + 1)
+    sh.prefill(ATTN, L.dev["x"][:, :S].contiguous(), kvc)
+    p = sh.decode(ATTN, L.dev["x"][:, S].contiguous(), kvc, out=nan_like((B, hidden)))
+    torch.cuda.synchronize()
+    pre = O.attn_stage(L.exact["x"][:, :S], L.W, L.spec, tp, r)
+    ref = O.decode_attn_stage(L.exact["x"][:, S], pre["k"], pre["v"], L.W, L.spec, tp, r)
+    assert_close(to_np(p), ref["partial"], "decode attn partial", "bf16")
+    h = synth.to_storage(synth.draw_normal((B, hidden), 22), "bf16")
+    pm = sh.decode(MLP, h.cuda(), out=nan_like((B, hidden)))
+    torch.cuda.synchronize()
+    refm = O.mlp_stage(h.float().numpy()[:, None], L.W, L.spec, tp, r)
+    assert_close(to_np(pm), refm["partial"][:, 0], "decode mlp partial", "bf16")
+
+
+@pytest.mark.parametrize("L_len", [1023, 70000])
+def test_decode_long_cache(L_len):
+    """Decode against a cache written directly (seeded bf16 values), long
+    enough that the split-KV merge covers more than 1024 chunks of 64."""
+    announce(f"bf16 decode over a written cache of {L_len} positions")
+    hidden, heads, kvh, B = 256, 4, 2, 2
+    L = Layer(hidden, heads, kvh, 512, batch=B, seq=1, gamma_noise=True, seed=23)
+    sh = L.shard(1, 0)
+    kvc = sh.kv_cache(B, L_len + 1)
+    shape = kvc.shape
+    kc = synth.to_storage(synth.draw_normal(shape, 24), "bf16")
+    vc = synth.to_storage(synth.draw_normal(shape, 25), "bf16")
+    kvc.write(kc.cuda(), vc.cuda())
+    kvc.length = L_len
+    p = sh.decode(ATTN, L.dev["x"][:, 0].contiguous(), kvc, out=nan_like((B, hidden)))
+    torch.cuda.synchronize()
+    kn = kc.float().numpy()[:, :, :L_len]
+    vn = vc.float().numpy()[:, :, :L_len]
+    ref = O.decode_attn_stage(L.exact["x"][:, 0], kn, vn, L.W, L.spec, 1, 0)
+    assert_close(to_np(p), ref["partial"], "decode attn partial", "bf16")
+    o = to_np(sh.debug_tensor("o", (B, heads * 64)))
+    assert_close(o, ref["o"].reshape(B, -1), "decode o", "bf16")
+
+
 def test_decode_equals_prefill_row():
     """Same math both ways: decode of token L after a prefill of L tokens
     equals row L of a prefill over L+1 tokens (GPU against GPU, then both
