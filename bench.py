@@ -1,6 +1,7 @@
 """Benchmark of one rank's tensor-parallel layer shard on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-70b]
+    python bench.py --sweep          # the 7B t=2 vs t=1 batch x prompt-length sweep
 
 Prints ONE JSON line.  The timed step is the whole prefill hot path of rank 0
 of a 7B-shaped layer split two ways (hidden 4096, 16 of 32 heads x 128,
@@ -16,8 +17,11 @@ second.  `roofline` covers the dominant kernel (the gate/up projection GEMM),
 timed with HIP events on its launch stream inside the timed steps.  `decode`
 reports batch-1 decode of rank 0 of the 7B layer split four ways against a
 1024-position cache, in microseconds per token per layer, over a stack of
-distinct layer copies whose weights (0.8 GB) exceed the 256 MB Infinity Cache.
-`cpu_baseline` times the CPU oracle (NumPy float64) on the same prefill step.
+distinct layer copies whose weights (>= 1 GB) exceed the 256 MB Infinity
+Cache.  `prefill_70b` / `decode_70b` report the same for rank 0 of a
+70B-shaped GQA layer split eight ways (prefill batch 4 x 4096 tokens; decode
+batch 1 at cache length 4096).  `cpu_baseline` times the CPU oracle (NumPy
+float64) on the same 7B prefill step.
 """
 
 from __future__ import annotations
@@ -26,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,6 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "shard-layer prefill TFLOP/s (% MFMA peak) + decode µs/token/layer (% HBM BW)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+XGMI_LINK_GBPS = 153.0         # one xGMI link, used only by the labelled all-reduce model
+ALLREDUCE_LATENCY_US = 5.0     # assumed fixed cost per all-reduce in that model
+MIN_DECODE_FOOTPRINT = 1.0e9   # decode weight copies span at least this many bytes
 
 
 def parse():
@@ -42,107 +50,140 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-layers", type=int, default=8)
+    ap.add_argument("--decode-layers", type=int, default=0,
+                    help="layer copies in the decode stack (0: enough for >= 1 GB of weights)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped prefill and decode")
+    ap.add_argument("--sweep", action="store_true", help="run the 7B t=2 vs t=1 crossover sweep instead")
     return ap.parse_args()
 
 
-def prefill_flops(w, t):
+# ---------------------------------------------------------------- algorithmic work
+
+def dims(hidden, heads, kv_heads, ffn, t):
+    d = hidden // heads
+    return d, heads // t, kv_heads // t, ffn // t
+
+
+def prefill_flops(hidden, heads, kv_heads, ffn, t, B, S):
     """Algorithmic FLOPs of one rank's prefill step: the four projections
     plus causal attention (QK^T and PV over the causal half)."""
-    d = w.hidden // w.heads
-    hl, kvl, fl = w.heads // t, w.kv_heads // t, w.ffn // t
-    T = w.batch * w.seq
-    nqkv = (hl + 2 * kvl) * d
+    d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
+    T = B * S
     gemm = {
-        "gemm_qkv": 2 * T * w.hidden * nqkv,
-        "gemm_out": 2 * T * hl * d * w.hidden,
-        "gemm_up": 2 * T * w.hidden * 2 * fl,
-        "gemm_down": 2 * T * fl * w.hidden,
+        "gemm_qkv": 2 * T * hidden * (hl + 2 * kvl) * d,
+        "gemm_out": 2 * T * hl * d * hidden,
+        "gemm_up": 2 * T * hidden * 2 * fl,
+        "gemm_down": 2 * T * fl * hidden,
     }
-    attn = 2 * w.batch * hl * w.seq * w.seq * d
+    attn = 2 * B * hl * S * S * d
     return gemm, attn
 
 
-def decode_bytes(w, t, L):
-    """Algorithmic HBM bytes of one decode token on one rank at cache length
-    L: the rank's bf16 weights once, K/V of positions 0..L read, one K/V
-    position written (activations are a few KB and left out)."""
-    d = w.hidden // w.heads
-    hl, kvl, fl = w.heads // t, w.kv_heads // t, w.ffn // t
-    weights = 2 * ((hl + 2 * kvl) * d * w.hidden + w.hidden * hl * d + 2 * fl * w.hidden + w.hidden * fl)
-    kv = 2 * 2 * kvl * d * (L + 1) + 2 * 2 * kvl * d
-    per_kernel = {
-        "gemv_qkv": 2 * (hl + 2 * kvl) * d * w.hidden,
-        "gemv_out": 2 * w.hidden * hl * d,
-        "gemv_up": 2 * 2 * fl * w.hidden,
-        "gemv_down": 2 * w.hidden * fl,
-        "attn_decode": 2 * 2 * kvl * d * (L + 1),
-    }
-    return weights + kv, per_kernel
+def weight_bytes(hidden, heads, kv_heads, ffn, t):
+    d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
+    return 2 * ((hl + 2 * kvl) * d * hidden + hidden * hl * d + 2 * fl * hidden + hidden * fl)
 
+
+def decode_bytes(hidden, heads, kv_heads, ffn, t, B, L):
+    """Algorithmic HBM bytes of one decode step (one token for each of B
+    sequences) on one rank at cache length L: the rank's bf16 weights once,
+    K/V of positions 0..L read, one K/V position written per sequence
+    (activations are a few KB per sequence and left out)."""
+    d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
+    kv_read = B * 2 * 2 * kvl * d * (L + 1)
+    per_kernel = {
+        "gemv_qkv": 2 * (hl + 2 * kvl) * d * hidden,
+        "gemv_out": 2 * hidden * hl * d,
+        "gemv_up": 2 * 2 * fl * hidden,
+        "gemv_down": 2 * hidden * fl,
+        "attn_decode": kv_read,
+    }
+    return weight_bytes(hidden, heads, kv_heads, ffn, t) + kv_read + B * 2 * 2 * kvl * d, per_kernel
+
+
+# ---------------------------------------------------------------- timing
 
 def source_sha(name):
     p = os.path.join(ROOT, "tensor_transformer_layer_tp_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def traffic_for(kernel, src, launches_per_step):
+def traffic_for(key, src):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
-    rec = json.load(open(p)).get(kernel)
+    rec = json.load(open(p)).get(key)
     if not rec or rec.get("source_sha") != source_sha(src):
         return None
     return rec.get("bytes_per_launch")
 
 
-def timed(fn, steps, warmup, stream):
-    import torch
+def timed(torch, fn, steps, warmup, stream):
+    """Mean ms per step over `steps` back-to-back steps (one event pair
+    around all of them), and the median / p10 / p90 of per-step times from
+    events recorded between the steps."""
+    import numpy as np
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    total = ev[0].elapsed_time(ev[-1])
+    return total / steps, {"median": round(float(np.median(per)), 4), "p10": round(float(np.percentile(per, 10)), 4),
+                           "p90": round(float(np.percentile(per, 90)), 4)}
 
 
-def bench_prefill(args, torch, T):
-    from tensor_transformer_layer_tp_amd import ATTN, MLP, Shard, partial_reduce, synth
-    w = synth.WORKLOADS["7b-t2-prefill"]
-    t = w.tp
-    raw = synth.draw_workload(w)
-    dev = {k: synth.to_storage(v, "bf16").cuda() for k, v in raw.items()}
-    wdev = {k: v for k, v in dev.items() if k != "x"}
-    x = dev["x"]
-    shards = [Shard(w.hidden, w.heads, w.kv_heads, w.ffn, t, r) for r in range(t)]
-    for sh in shards:
-        sh.load_weights(wdev)
-        sh.reserve(w.batch * w.seq)
-    B, S, h = w.batch, w.seq, w.hidden
-    kv = shards[0].kv_cache(B, S)
-    # the other rank's partials (the contribution a second GPU would send)
-    pa = [torch.empty((B, S, h), dtype=torch.float32, device="cuda") for _ in range(t)]
-    pm = [torch.empty((B, S, h), dtype=torch.float32, device="cuda") for _ in range(t)]
+def rounded(d):
+    return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+# ---------------------------------------------------------------- prefill
+
+def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, kv_cap=None):
+    """Rank 0's shard plus the buffers of one prefill step.  The other
+    ranks' partials are either computed by their own shards once
+    (exact_others) or seeded N(0, 0.1^2) stand-ins (timing only)."""
+    from tensor_transformer_layer_tp_amd import ATTN, MLP, Shard, partial_reduce
+    B, S = int(x.shape[0]), int(x.shape[1])
+    sh = Shard(hidden, heads, kv_heads, ffn, t, 0)
+    sh.load_weights(wdev)
+    sh.reserve(B * S)
+    kv = sh.kv_cache(B, kv_cap or S)
+    pa = [torch.empty((B, S, hidden), dtype=torch.float32, device="cuda") for _ in range(t)]
+    pm = [torch.empty((B, S, hidden), dtype=torch.float32, device="cuda") for _ in range(t)]
     hbuf = torch.empty_like(x)
     ybuf = torch.empty_like(x)
-    for r in range(1, t):
-        shards[r].prefill(ATTN, x, None, out=pa[r])
-    shards[0].prefill(ATTN, x, kv, out=pa[0])
-    partial_reduce(pa, residual=x, out=hbuf)
-    for r in range(1, t):
-        shards[r].prefill(MLP, hbuf, out=pm[r])
+    if exact_others:
+        for r in range(1, t):
+            o = Shard(hidden, heads, kv_heads, ffn, t, r)
+            o.load_weights(wdev)
+            o.prefill(ATTN, x, None, out=pa[r])
+            torch.cuda.synchronize()
+            o.close()
+        sh.prefill(ATTN, x, kv, out=pa[0])
+        partial_reduce(pa, residual=x, out=hbuf)
+        for r in range(1, t):
+            o = Shard(hidden, heads, kv_heads, ffn, t, r)
+            o.load_weights(wdev)
+            o.prefill(MLP, hbuf, out=pm[r])
+            torch.cuda.synchronize()
+            o.close()
+    else:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(99)
+        for r in range(1, t):
+            pa[r].normal_(0.0, 0.1, generator=g)
+            pm[r].normal_(0.0, 0.1, generator=g)
     torch.cuda.synchronize()
-    sh = shards[0]
-    stream = torch.cuda.current_stream()
 
     def step():
         sh.prefill(ATTN, x, kv, out=pa[0])
@@ -150,21 +191,30 @@ def bench_prefill(args, torch, T):
         sh.prefill(MLP, hbuf, out=pm[0])
         partial_reduce(pm, residual=hbuf, out=ybuf)
 
-    # timed region: the kernel timer brackets the dominant kernel (gate/up
-    # projection) with events on its launch stream inside these same steps
+    return sh, kv, step
+
+
+def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, roof_key):
+    """Times the rank-0 prefill step; the timed pass brackets only the
+    dominant kernel (gate/up GEMM) with events, a second pass brackets
+    every kernel for the per-kernel breakdown."""
+    B, S = int(x.shape[0]), int(x.shape[1])
+    sh, kv, step = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others)
+    stream = torch.cuda.current_stream()
     dom = "gemm_up"
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     sh.timing(True, kinds=[dom])
-    ms = timed(step, args.steps, 0, stream)
+    ms, dist = timed(torch, step, args.steps, 0, stream)
     dom_times = sh.timing_read()[dom]
-    # per-kernel breakdown: a second pass with every kernel bracketed
     sh.timing(True)
-    ms_marked = timed(step, args.steps, 0, stream)
+    ms_marked, _ = timed(torch, step, args.steps, 0, stream)
     ktimes = sh.timing_read()
     sh.timing(False)
-    gemm, attn = prefill_flops(w, t)
+    kv.close()
+    sh.close()
+    gemm, attn = prefill_flops(hidden, heads, kv_heads, ffn, t, B, S)
     total = sum(gemm.values()) + attn
     kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in ktimes.items()}
     for k, f in gemm.items():
@@ -175,57 +225,66 @@ def bench_prefill(args, torch, T):
     gemm_us = sum(kern[k]["avg_us"] for k in gemm if k in kern)
     dom_us = 1e3 * dom_times[0] / dom_times[1]
     achieved = gemm[dom] / (dom_us * 1e-6) / 1e12
-    traffic = traffic_for("gemm_up_7b_t2", "gemm_bf16.hip", 1)
-    out = {
-        "w": w, "ms": ms, "ms_marked": ms_marked, "dom_us": dom_us, "flops": total, "gemm_flops": sum(gemm.values()),
-        "attn_flops": attn, "kernels": kern, "gemm_us": gemm_us,
+    d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
+    return {
+        "workload": name,
+        "ms_per_step": round(ms, 4),
+        "step_ms": dist,
+        "tflops": round(total / (ms * 1e-3) / 1e12, 2),
+        "mfma_frac": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": total,
+        "gemm_tflops": round(sum(gemm.values()) / (gemm_us * 1e-6) / 1e12, 2),
+        "gemm_mfma_frac": round(sum(gemm.values()) / (gemm_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_all_kernels_bracketed": round(ms_marked, 4),
+        "kernels": {k: rounded(v) for k, v in kern.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "gemm (gate/up projection + SwiGLU epilogue), M=2048 N=11008 K=4096",
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(roof_key, "gemm_bf16.hip"),
+                     "kernel": f"gemm (gate/up projection + SwiGLU epilogue), M={B * S} N={2 * fl} K={hidden}",
                      "avg_us": round(dom_us, 3), "launches": dom_times[1], "flops_per_launch": gemm[dom]},
-        "state": (w, raw),
     }
-    for s_ in shards:
-        s_.close()
-    kv.close()
-    return out
 
 
-def bench_decode(args, torch):
-    from tensor_transformer_layer_tp_amd import ATTN, MLP, Shard, partial_reduce, synth
-    w = synth.WORKLOADS["7b-t4-decode"]
-    t, L0 = w.tp, w.kv_len
-    raw = synth.draw_workload(w)
-    dev = {k: synth.to_storage(v, "bf16").cuda() for k, v in raw.items()}
-    wdev = {k: v for k, v in dev.items() if k not in ("k_cache", "v_cache", "x_dec")}
-    nl = args.decode_layers
-    cap = L0 + args.warmup + 2 * args.steps + 4
+# ---------------------------------------------------------------- decode
+
+def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copies, fill):
+    """`copies` distinct rank-0 shards (their weights rotate through HBM)
+    with caches at length L0; fill(kv) writes the first copy's cache
+    content, the others copy it."""
+    from tensor_transformer_layer_tp_amd import Shard
     layers = []
-    for _ in range(nl):
-        sh = Shard(w.hidden, w.heads, w.kv_heads, w.ffn, t, 0)
+    for i in range(copies):
+        sh = Shard(hidden, heads, kv_heads, ffn, t, 0)
         sh.load_weights(wdev)
-        kv = sh.kv_cache(1, cap)
-        kfull = torch.zeros(kv.shape, dtype=torch.bfloat16, device="cuda")
-        vfull = torch.zeros(kv.shape, dtype=torch.bfloat16, device="cuda")
-        kvl = w.kv_heads // t
-        kfull[:, :, :L0] = dev["k_cache"][:, :kvl]
-        vfull[:, :, :L0] = dev["v_cache"][:, :kvl]
-        kv.write(kfull, vfull)
+        kv = sh.kv_cache(B, cap)
+        if i == 0:
+            fill(kv)
+        else:
+            kv.copy_from(layers[0][1])
         kv.length = L0
         layers.append((sh, kv))
-    del wdev
-    # the other ranks' partials: fixed buffers standing for the other GPUs
-    others = [torch.randn((1, w.hidden), device="cuda", dtype=torch.float32) * 0.1 for _ in range(t - 1)]
-    x0 = dev["x_dec"]
-    pa = torch.empty((1, w.hidden), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    return layers
+
+
+def decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=None):
+    """One decode token for B sequences through every layer copy: ATTN stage,
+    reduce, MLP stage, reduce (other ranks' partials are fixed stand-ins).
+    With reset_len every step decodes at that cache length."""
+    from tensor_transformer_layer_tp_amd import ATTN, MLP, partial_reduce
+    g = torch.Generator(device="cuda")
+    g.manual_seed(98)
+    others = [torch.randn((B, hidden), device="cuda", dtype=torch.float32, generator=g) * 0.1 for _ in range(t - 1)]
+    pa = torch.empty((B, hidden), dtype=torch.float32, device="cuda")
     pm = torch.empty_like(pa)
     hb = torch.empty_like(x0)
     yb = [torch.empty_like(x0) for _ in range(2)]
-    stream = torch.cuda.current_stream()
 
     def step():
         x = x0
         for i, (sh, kv) in enumerate(layers):
+            if reset_len is not None:
+                kv.length = reset_len
             sh.decode(ATTN, x, kv, out=pa)
             partial_reduce([pa, *others], residual=x, out=hb)
             sh.decode(MLP, hb, out=pm)
@@ -233,11 +292,20 @@ def bench_decode(args, torch):
             partial_reduce([pm, *others], residual=hb, out=y)
             x = y
 
-    ms = timed(step, args.steps, args.warmup, stream)
-    # per-kernel durations from a separate pass with event markers
+    return step
+
+
+def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0):
+    wb = weight_bytes(hidden, heads, kv_heads, ffn, t)
+    nl = args.decode_layers or max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
+    cap = L0 + args.warmup + 2 * args.steps + 4
+    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, 1, L0, cap, nl, fill)
+    stream = torch.cuda.current_stream()
+    step = decode_step_fn(torch, layers, hidden, t, 1, x0)
+    ms, dist = timed(torch, step, args.steps, args.warmup, stream)
     for sh, _ in layers:
         sh.timing(True)
-    timed(step, args.steps, 0, stream)
+    timed(torch, step, args.steps, 0, stream)
     agg = {}
     for sh, _ in layers:
         for k, (tot, n) in sh.timing_read().items():
@@ -245,8 +313,11 @@ def bench_decode(args, torch):
             a[0] += tot
             a[1] += n
         sh.timing(False)
+    for sh, kv in layers:
+        kv.close()
+        sh.close()
     L_avg = L0 + args.warmup + args.steps + (args.steps - 1) / 2.0   # mean cache length of the timed steps
-    nbytes, per_kernel = decode_bytes(w, t, int(L_avg))
+    nbytes, per_kernel = decode_bytes(hidden, heads, kv_heads, ffn, t, 1, int(L_avg))
     us = 1e3 * ms / nl
     kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in agg.items()}
     for k, b in per_kernel.items():
@@ -254,29 +325,175 @@ def bench_decode(args, torch):
             kern[k]["GBps"] = b / (kern[k]["avg_us"] * 1e-6) / 1e9
     dom = "gemv_up"
     ach = per_kernel[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
-    for sh, kv in layers:
-        sh.close()
-        kv.close()
+    d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
     return {
-        "workload": "7b-t4-decode: hidden 4096, rank 0 of t=4 (8 of 32 heads x 128, SwiGLU 2752 of 11008), "
-                    f"bf16, batch 1, cache {L0}+ positions, {nl} distinct layer copies",
+        "workload": f"{name}, {nl} distinct layer copies ({nl * wb / 1e9:.2f} GB of weights)",
         "us_per_token_layer": round(us, 3),
+        "step_ms": dist,
         "bytes_per_token_layer": nbytes,
         "hbm_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
         "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
-                    for k, v in kern.items()},
+        "kernels": {k: rounded(v) for k, v in kern.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "gemv_kernel (gate/up + SwiGLU, fused RMSNorm), N=5504 K=4096",
+                     "kernel": f"gemv_kernel (gate/up + SwiGLU, fused RMSNorm), N={2 * fl} K={hidden}",
                      "bytes_per_launch": per_kernel[dom]},
     }
 
 
+# ---------------------------------------------------------------- workloads
+
+def run_7b(args, torch):
+    from tensor_transformer_layer_tp_amd import synth
+    w = synth.WORKLOADS["7b-t2-prefill"]
+    raw = synth.draw_workload(w)
+    dev = {k: synth.to_storage(v, "bf16").cuda() for k, v in raw.items()}
+    wdev = {k: v for k, v in dev.items() if k != "x"}
+    pre = bench_prefill(args, torch, "7b-t2-prefill", w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, dev["x"],
+                        True, "gemm_up_7b_t2")
+    del dev, wdev
+    return pre, (w, raw)
+
+
+def run_7b_decode(args, torch):
+    from tensor_transformer_layer_tp_amd import synth
+    w = synth.WORKLOADS["7b-t4-decode"]
+    raw = synth.draw_workload(w)
+    dev = {k: synth.to_storage(v, "bf16").cuda() for k, v in raw.items()}
+    wdev = {k: v for k, v in dev.items() if k not in ("k_cache", "v_cache", "x_dec")}
+    kvl = w.kv_heads // w.tp
+
+    def fill(kv):
+        kf = torch.zeros(kv.shape, dtype=torch.bfloat16, device="cuda")
+        vf = torch.zeros(kv.shape, dtype=torch.bfloat16, device="cuda")
+        kf[:, :, :w.kv_len] = dev["k_cache"][:, :kvl]
+        vf[:, :, :w.kv_len] = dev["v_cache"][:, :kvl]
+        kv.write(kf, vf)
+
+    name = ("7b-t4-decode: hidden 4096, rank 0 of t=4 (8 of 32 heads x 128, SwiGLU 2752 of 11008), bf16, batch 1, "
+            f"cache {w.kv_len}+ positions")
+    return bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill,
+                        dev["x_dec"])
+
+
+def run_70b(args, torch):
+    """Rank 0 of the 70B-shaped GQA layer at t=8; inputs drawn on the device
+    (timing only: their values do not change the work)."""
+    from tensor_transformer_layer_tp_amd import synth
+    w = synth.WORKLOADS["70b-t8-prefill"]
+    wdev = synth.draw_layer_device(w.hidden, w.heads, w.kv_heads, w.ffn, seed=0)
+    x = synth.draw_normal_device((w.batch, w.seq, w.hidden), 1)
+    pre = bench_prefill(args, torch,
+                        "70b-t8-prefill: rank 0 of a 70B-shaped GQA layer split t=8 (hidden 8192, 8 of 64 query "
+                        "heads + 1 of 8 KV heads x 128, SwiGLU 3584 of 28672), bf16, batch 4 x seq 4096, causal",
+                        w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, x, False, "gemm_up_70b_t8")
+    del x
+    dec = None
+    if not args.no_decode:
+        wd = synth.WORKLOADS["70b-t8-decode"]
+        kvl = wd.kv_heads // wd.tp
+        d = wd.hidden // wd.heads
+
+        def fill(kv):
+            kf = torch.zeros(kv.shape, dtype=torch.bfloat16, device="cuda")
+            vf = torch.zeros(kv.shape, dtype=torch.bfloat16, device="cuda")
+            kf[:, :, :wd.kv_len] = synth.draw_normal_device((1, kvl, wd.kv_len, d), 2)
+            vf[:, :, :wd.kv_len] = synth.draw_normal_device((1, kvl, wd.kv_len, d), 3)
+            kv.write(kf, vf)
+
+        x0 = synth.draw_normal_device((1, wd.hidden), 4)
+        dec = bench_decode(args, torch,
+                           "70b-t8-decode: rank 0 of t=8 (8 query heads on 1 KV head x 128, SwiGLU 3584 of 28672), "
+                           f"bf16, batch 1, cache {wd.kv_len}+ positions",
+                           wd.hidden, wd.heads, wd.kv_heads, wd.ffn, wd.tp, wdev, wd.kv_len, fill, x0)
+    return pre, dec
+
+
+# ---------------------------------------------------------------- crossover sweep
+
+def allreduce_model_us(nbytes):
+    """Labelled model, not a measurement: one t=2 all-reduce of nbytes over
+    one xGMI link (each GPU sends half and receives half twice = nbytes)."""
+    return ALLREDUCE_LATENCY_US + nbytes / (XGMI_LINK_GBPS * 1e9) * 1e6
+
+
+def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
+    from tensor_transformer_layer_tp_amd import synth
+    stream = torch.cuda.current_stream()
+    x = synth.draw_normal_device((B, S, hidden), 1000 + B * 10000 + S)
+    sh, kv, step = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, False, kv_cap=S + 1)
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    est = time.perf_counter() - t0
+    n = max(3, min(args.steps, int(0.5 / max(est, 1e-6))))
+    ms, dist = timed(torch, step, n, 1, stream)
+    gemm, attn = prefill_flops(hidden, heads, kv_heads, ffn, t, B, S)
+    pre = {"ms": ms, "median_ms": dist["median"], "tflops": (sum(gemm.values()) + attn) / (ms * 1e-3) / 1e12}
+    del step
+    # decode one token per sequence at cache length S over the cache this
+    # prefill left, through enough layer copies to span >= 1 GB of weights
+    wb = weight_bytes(hidden, heads, kv_heads, ffn, t)
+    nl = max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
+    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, S, S + 1, nl, lambda k: k.copy_from(kv))
+    kv.close()
+    sh.close()
+    del x
+    x0 = synth.draw_normal_device((B, hidden), 7)
+    dstep = decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=S)
+    dms, _ = timed(torch, dstep, max(3, min(args.steps, 10)), 2, stream)
+    us = 1e3 * dms / nl
+    nbytes, _ = decode_bytes(hidden, heads, kv_heads, ffn, t, B, S)
+    dec = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
+    for s_, k_ in layers:
+        k_.close()
+        s_.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return pre, dec
+
+
+def run_sweep(args, torch):
+    """7B-shaped layer: rank 0 of t=2 against the unsharded layer (t=1) on
+    the same GPU and kernels, prefill of B x S tokens and decode of one
+    token per sequence at cache length S, timed separately."""
+    from tensor_transformer_layer_tp_amd import synth
+    hidden, heads, kv_heads, ffn = 4096, 32, 32, 11008
+    wdev = synth.draw_layer_device(hidden, heads, kv_heads, ffn, seed=0)
+    res = {}
+    for t in (2, 1):
+        for B in synth.SWEEP_BATCH:
+            for S in synth.SWEEP_SEQ:
+                print(f"[sweep] t={t} B={B} S={S}", file=sys.stderr, flush=True)
+                res[(t, B, S)] = sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S)
+    table = []
+    for B in synth.SWEEP_BATCH:
+        for S in synth.SWEEP_SEQ:
+            p2, d2 = res[(2, B, S)]
+            p1, d1 = res[(1, B, S)]
+            msg_pre = B * S * hidden * 2          # bf16 [T, h] per all-reduce
+            msg_dec = B * hidden * 2
+            table.append({
+                "B": B, "S": S,
+                "prefill_ms_t2": round(p2["ms"], 4), "prefill_ms_t1": round(p1["ms"], 4),
+                "prefill_ratio": round(p2["ms"] / p1["ms"], 3),
+                "prefill_tflops_t2": round(p2["tflops"], 1), "prefill_tflops_t1": round(p1["tflops"], 1),
+                "decode_us_t2": round(d2["us"], 2), "decode_us_t1": round(d1["us"], 2),
+                "decode_ratio": round(d2["us"] / d1["us"], 3),
+                "decode_GBps_t2": round(d2["GBps"], 1), "decode_GBps_t1": round(d1["GBps"], 1),
+                "model_allreduce_us_prefill_t2": round(2 * allreduce_model_us(msg_pre), 1),
+                "model_allreduce_us_decode_t2": round(2 * allreduce_model_us(msg_dec), 1),
+            })
+    return table
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
 def cpu_baseline(state):
     """The CPU oracle (NumPy float64) on the same rank-0 prefill step; the
     other rank's partials are computed first, outside the timed part."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import layer as O
@@ -302,6 +519,18 @@ def cpu_baseline(state):
     return steps, t_tot, threads
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ---------------------------------------------------------------- main
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,18 +539,26 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
-    pre = bench_prefill(args, torch, None)
-    dec = None if args.no_decode else bench_decode(args, torch)
-    w = pre["w"]
-    tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+    if args.sweep:
+        table = run_sweep(args, torch)
+        print(json.dumps({"sweep": "7B-shaped layer, rank 0 of t=2 vs t=1 (unsharded), bf16; prefill B x S tokens "
+                                   "(step = ATTN + reduce + MLP + reduce); decode one token per sequence at cache "
+                                   "length S, per layer; model_allreduce_* is a labelled link-bound model of the two "
+                                   "all-reduces a real t=2 layer adds, not a measurement",
+                          "points": table}), flush=True)
+        return
+    pre, state = run_7b(args, torch)
+    dec = None if args.no_decode else run_7b_decode(args, torch)
+    big = None if args.no_70b else run_70b(args, torch)
+    w = state[0]
     line = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": pre["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(pre["ms"], 4),
+        "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -333,24 +570,23 @@ def main():
                         "+ reduce + MLP stage + reduce",
             "global_batch": w.batch, "seq_len": w.seq, "parallelism": "tp2 shard (rank 0) on 1 GPU",
         },
-        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "flops_per_step": pre["flops"],
-        "gemm_tflops": round(pre["gemm_flops"] / (pre["gemm_us"] * 1e-6) / 1e12, 2),
-        "gemm_mfma_frac": round(pre["gemm_flops"] / (pre["gemm_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "ms_per_step_all_kernels_bracketed": round(pre["ms_marked"], 4),
-        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
-                    for k, v in pre["kernels"].items()},
-        "roofline": pre["roofline"],
     }
+    for k in ("step_ms", "mfma_frac", "flops_per_step", "gemm_tflops", "gemm_mfma_frac",
+              "ms_per_step_all_kernels_bracketed", "kernels", "roofline"):
+        line[k] = pre[k]
     if dec is not None:
         line["decode"] = dec
+    if big is not None:
+        line["prefill_70b"] = big[0]
+        if big[1] is not None:
+            line["decode_70b"] = big[1]
     if not args.no_cpu:
-        steps, secs, threads = cpu_baseline(pre["state"])
+        steps, secs, threads = cpu_baseline(state)
         line["cpu_baseline"] = {
-            "value": round(pre["flops"] * steps / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "value": round(pre["flops_per_step"] * steps / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{steps} full rank-0 prefill step(s) of the same workload (B=1, S=2048) in NumPy float64, "
-                      f"{secs:.1f} s",
+                      f"{secs:.1f} s on {cpu_model()}",
         }
     print(json.dumps(line), flush=True)
 

@@ -99,6 +99,13 @@ class KVCache:
             _dev(src, name, self.shard.torch_dtype, self.shape)
             _memcpy_d2d(dst, src.data_ptr(), self.nbytes, stream)
 
+    def copy_from(self, other: "KVCache", stream=None) -> None:
+        """Copy another cache of the same shape (both K and V arrays)."""
+        if other.shape != self.shape or other.shard.torch_dtype != self.shard.torch_dtype:
+            raise ValueError("KV caches differ in shape or dtype")
+        _memcpy_d2d(self._k, other._k, self.nbytes, stream)
+        _memcpy_d2d(self._v, other._v, self.nbytes, stream)
+
     def read(self, stream=None):
         """Copies of the K and V arrays as device tensors."""
         out = []

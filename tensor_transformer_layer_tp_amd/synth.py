@@ -121,3 +121,37 @@ def to_storage(a, dtype: str):
 def as_f64(t) -> np.ndarray:
     """The exact values of a torch storage tensor as a float64 array."""
     return t.detach().to("cpu").float().numpy().astype(np.float64)
+
+
+def draw_layer_device(hidden, heads, kv_heads, ffn, *, seed=0, device="cuda", dtype=None):
+    """Timing-only variant of ``draw_layer``: the same matrices, scales and
+    order, drawn on the device with torch's generator (Philox) and cast to
+    the storage type, for layers too large to draw quickly on the host.  The
+    values differ from the NumPy draws, so these inputs are never compared
+    with the oracle.  Returns the weight dict (wq, wk, wv, wo, w_gate, w_up,
+    w_down, g1, g2) of a SwiGLU layer."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    d = hidden // heads
+
+    def n(shape, scale):
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * scale).to(dtype)
+
+    std = float(WEIGHT_STD)
+    return {
+        "wq": n((heads * d, hidden), std), "wk": n((kv_heads * d, hidden), std),
+        "wv": n((kv_heads * d, hidden), std), "wo": n((hidden, heads * d), std),
+        "w_gate": n((ffn, hidden), std), "w_up": n((ffn, hidden), std), "w_down": n((hidden, ffn), std),
+        "g1": torch.ones(hidden, device=device, dtype=dtype), "g2": torch.ones(hidden, device=device, dtype=dtype),
+    }
+
+
+def draw_normal_device(shape, seed, scale=1.0, device="cuda", dtype=None):
+    """Timing-only N(0, scale^2) device tensor in the storage type."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * scale
+    return t.to(dtype or torch.bfloat16)
