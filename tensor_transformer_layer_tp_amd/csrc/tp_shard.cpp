@@ -35,8 +35,6 @@ struct tp_shard {
     size_t ws_bytes;
     float *rcos, *rsin;
     int rope_npos;
-    int* attn_cnt;          // prefill attention merge counters (kept zero between calls)
-    size_t attn_cnt_bytes;
     // offsets of the last call's workspace tensors (debug view)
     size_t off_n, off_o, off_act;
     // kernel timer: event pairs in launch order and the kind of each pair
@@ -125,7 +123,7 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
     size_t n, q, o, kv, act, scr, total;
 };
-Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode, size_t extra_scr = 0) {
+Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) {
     Layout L;
     size_t e = s->esz;
     L.n = 0;
@@ -135,25 +133,8 @@ Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode, 
     L.act = L.kv + al((size_t)2 * T * s->kvl * s->d * e);
     L.scr = L.act + al((size_t)T * s->fl * e);
     size_t scr = len_decode > 0 ? attn_decode_scratch_bytes(batch_decode, s->hl, len_decode) : 0;
-    L.total = L.scr + al(std::max(scr, extra_scr));
+    L.total = L.scr + al(scr);
     return L;
-}
-
-int ensure_attn_counters(tp_shard* s, size_t bytes) {
-    if (bytes <= s->attn_cnt_bytes) return TP_OK;
-    if (s->attn_cnt) {
-        hipError_t e = hipFree(s->attn_cnt);
-        s->attn_cnt = nullptr;
-        s->attn_cnt_bytes = 0;
-        if (e != hipSuccess) return hip_fail(e, "hipFree(counters)");
-    }
-    if (hipMalloc((void**)&s->attn_cnt, bytes) != hipSuccess) {
-        s->attn_cnt = nullptr;
-        return TP_E_NOMEM;
-    }
-    HIP_TRY(hipMemset(s->attn_cnt, 0, bytes));
-    s->attn_cnt_bytes = bytes;
-    return TP_OK;
 }
 
 int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void* q, void* k, void* v,
@@ -666,7 +647,7 @@ void tp_shard_destroy(tp_shard* s) {
     if (!s) return;
     for (hipEvent_t e : s->ev)
         if (e) (void)hipEventDestroy(e);
-    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin, s->attn_cnt};
+    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     delete s;
