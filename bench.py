@@ -56,6 +56,11 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped prefill and decode")
     ap.add_argument("--sweep", action="store_true", help="run the 7B t=2 vs t=1 crossover sweep instead")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB three times: the known-size copy that scales rocprofv3 byte counters")
+    ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="no GPU: turn rocprofv3 outputs of this script into profiles/traffic.json and "
+                         "profiles/*.md (see profiles/README.md for the commands)")
     return ap.parse_args()
 
 
@@ -106,8 +111,11 @@ def decode_bytes(hidden, heads, kv_heads, ffn, t, B, L):
 # ---------------------------------------------------------------- timing
 
 def source_sha(name):
-    p = os.path.join(ROOT, "tensor_transformer_layer_tp_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source together with the headers it includes."""
+    h = hashlib.sha256()
+    for f in (name, "common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "tensor_transformer_layer_tp_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(key, src):
@@ -295,7 +303,7 @@ def decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=None):
     return step
 
 
-def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0):
+def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0, roof_key):
     wb = weight_bytes(hidden, heads, kv_heads, ffn, t)
     nl = args.decode_layers or max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
     cap = L0 + args.warmup + 2 * args.steps + 4
@@ -335,7 +343,7 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
         "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "kernels": {k: rounded(v) for k, v in kern.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic_for(roof_key, "decode.hip"),
                      "kernel": f"gemv_kernel (gate/up + SwiGLU, fused RMSNorm), N={2 * fl} K={hidden}",
                      "bytes_per_launch": per_kernel[dom]},
     }
@@ -373,7 +381,7 @@ def run_7b_decode(args, torch):
     name = ("7b-t4-decode: hidden 4096, rank 0 of t=4 (8 of 32 heads x 128, SwiGLU 2752 of 11008), bf16, batch 1, "
             f"cache {w.kv_len}+ positions")
     return bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill,
-                        dev["x_dec"])
+                        dev["x_dec"], "gemv_up_7b_t4")
 
 
 def run_70b(args, torch):
@@ -405,7 +413,8 @@ def run_70b(args, torch):
         dec = bench_decode(args, torch,
                            "70b-t8-decode: rank 0 of t=8 (8 query heads on 1 KV head x 128, SwiGLU 3584 of 28672), "
                            f"bf16, batch 1, cache {wd.kv_len}+ positions",
-                           wd.hidden, wd.heads, wd.kv_heads, wd.ffn, wd.tp, wdev, wd.kv_len, fill, x0)
+                           wd.hidden, wd.heads, wd.kv_heads, wd.ffn, wd.tp, wdev, wd.kv_len, fill, x0,
+                           "gemv_up_70b_t8")
     return pre, dec
 
 
@@ -529,16 +538,116 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
+# ---------------------------------------------------------------- profile summaries
+
+# kernels whose HBM traffic is summarised: key -> (source file, name pattern,
+# algorithmic bytes per launch).  Template argument MODE 2 is the SwiGLU
+# epilogue, which only the gate/up projection uses.
+TRAFFIC_KERNELS = {
+    "gemm_up_7b_t2": ("gemm_bf16.hip", r"gemm_\w+_kernel<[^>]*, 2>",
+                      2 * (2048 * 4096 + 11008 * 4096 + 2048 * 5504)),
+    "gemv_up_7b_t4": ("decode.hip", r"gemv_kernel<[^>]*, 2, true>", 2 * (5504 * 4096 + 4096 + 2752)),
+}
+
+
+def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
+    """Per-launch HBM bytes of the roofline kernels from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by
+    the same counter's reading for the known-size copy (--calib-copy), and
+    a kernel-duration table from the --kernel-trace --stats run."""
+    import csv
+    import glob
+    import re
+    import statistics
+
+    def rows(d, suffix):
+        out = []
+        for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+            out.extend(csv.DictReader(open(f)))
+        return out
+
+    calib = calib_mib * 1024 * 1024
+    traffic, facts = {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rs = [r for r in rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) * 1024 for r in rs
+                  if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 > calib / 2]
+        if not copies:
+            raise SystemExit(f"no calibration copy found in {d}")
+        factor = calib / statistics.median(copies)
+        facts[counter] = factor
+        for key, (_, pat, _) in TRAFFIC_KERNELS.items():
+            vals = [float(r["Counter_Value"]) * 1024 * factor for r in rs if re.search(pat, r["Kernel_Name"])]
+            if vals:
+                traffic.setdefault(key, {})[counter] = (statistics.mean(vals), len(vals))
+    rec = {}
+    for key, (src, pat, alg) in TRAFFIC_KERNELS.items():
+        if key not in traffic or len(traffic[key]) != 2:
+            continue
+        f, nf = traffic[key]["FETCH_SIZE"]
+        w, nw = traffic[key]["WRITE_SIZE"]
+        rec[key] = {"source": src, "source_sha": source_sha(src), "bytes_per_launch": round(f + w),
+                    "fetch_bytes": round(f), "write_bytes": round(w), "algorithmic_bytes": alg,
+                    "traffic_over_algorithmic": round((f + w) / alg, 3), "launches": [nf, nw],
+                    "fetch_factor": round(facts["FETCH_SIZE"], 4), "write_factor": round(facts["WRITE_SIZE"], 4)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    # kernel durations from the trace run, next to the bench's live event timings
+    stats = rows(trace_dir, "kernel_stats.csv")
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    md = ["| kernel | calls | avg µs | min µs | max µs | % time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in stats[:24]:
+        name = r["Name"].replace("|", "/")
+        name = name if len(name) <= 110 else name[:107] + "..."
+        md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                  f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    live = []
+    for k in ("roofline",):
+        live.append(f"- prefill roofline kernel ({line[k]['kernel']}): live HIP-event average "
+                    f"{line[k]['avg_us']} µs over {line[k]['launches']} launches")
+    if "decode" in line:
+        dk = line["decode"]["kernels"].get("gemv_up")
+        if dk:
+            live.append(f"- decode roofline kernel ({line['decode']['roofline']['kernel']}): live HIP-event "
+                        f"average {dk['avg_us']} µs over {dk['launches']} launches (events add ~1 µs)")
+    with open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w") as fh:
+        fh.write("# Kernel durations of `bench.py --no-cpu` (rocprofv3 --kernel-trace --stats)\n\n")
+        fh.write("Commands: see profiles/README.md.  Bench line of the same run:\n\n")
+        fh.write("\n".join(live) + "\n\n" + "\n".join(md) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
+def calib_copy(torch, mib):
+    """A plain device copy of known size (the scale for byte counters)."""
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- main
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize, args.calib_copy or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
               "build", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.calib_copy:
+        calib_copy(torch, args.calib_copy)
     if args.sweep:
         table = run_sweep(args, torch)
         print(json.dumps({"sweep": "7B-shaped layer, rank 0 of t=2 vs t=1 (unsharded), bf16; prefill B x S tokens "
