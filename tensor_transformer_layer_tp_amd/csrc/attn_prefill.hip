@@ -41,7 +41,7 @@ __device__ __forceinline__ int kslot(int r, int c) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                            const bf16* __restrict__ V, bf16* __restrict__ O,
                                                            int hl, int kvl, int S, int ld_seq, float scale_log2) {
     constexpr int KC = D / 8;        // 16-byte chunks per K row
@@ -77,26 +77,47 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
 
     const int kv_end = min(S, qb * BQ + BQ);
     const int nkb = (kv_end + BKV - 1) / BKV;
+
+    // Block kb + 1 is fetched into registers while block kb is computed from
+    // LDS.  Rows past the sequence are clamped to row S-1 (read, never used),
+    // so every load is issued unconditionally and stays in bounds.
+    constexpr int KLD = BKV * KC / 256;         // K chunks per thread
+    constexpr int VLD = (BKV / 2) * KC / 256;   // V key pairs per thread
+    bf16x8 kreg[KLD];
+    u16x8 vreg[VLD][2];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int gk = min(k0 + idx / KC, S - 1);
+            kreg[i] = *(const bf16x8*)(Kb + (long long)gk * D + (idx % KC) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
+            const int g0 = min(k0 + 2 * a, S - 1), g1 = min(k0 + 2 * a + 1, S - 1);
+            vreg[i][0] = *(const u16x8*)(Vb + (long long)g0 * D + dc * 8);
+            vreg[i][1] = *(const u16x8*)(Vb + (long long)g1 * D + dc * 8);
+        }
+    };
+    fetch(0);
     for (int kb = 0; kb < nkb; ++kb) {
         const int k0 = kb * BKV;
         __syncthreads();
         // K block -> LDS [key][dim], chunk swizzled by key
 #pragma unroll
-        for (int i = 0; i < BKV * KC / 256; ++i) {
+        for (int i = 0; i < KLD; ++i) {
             const int idx = tid + 256 * i;
             const int key = idx / KC, dc = idx % KC;
-            const int gk = min(k0 + key, S - 1);
-            const bf16x8 v = *(const bf16x8*)(Kb + (long long)gk * D + dc * 8);
-            *(bf16x8*)(sK + key * D + (kslot<KC>(key, dc) << 3)) = v;
+            *(bf16x8*)(sK + key * D + (kslot<KC>(key, dc) << 3)) = kreg[i];
         }
         // V block -> LDS transposed [dim][permuted key], two keys per 32-bit store
 #pragma unroll
-        for (int i = 0; i < (BKV / 2) * KC / 256; ++i) {
+        for (int i = 0; i < VLD; ++i) {
             const int idx = tid + 256 * i;
             const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
-            const int g0 = min(k0 + 2 * a, S - 1), g1 = min(k0 + 2 * a + 1, S - 1);
-            const u16x8 v0 = *(const u16x8*)(Vb + (long long)g0 * D + dc * 8);
-            const u16x8 v1 = *(const u16x8*)(Vb + (long long)g1 * D + dc * 8);
+            const u16x8 v0 = vreg[i][0], v1 = vreg[i][1];
             const int p = vt_pos(2 * a);
             const bool hi = (lane >> 5) != 0;
 #pragma unroll
@@ -111,6 +132,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
             }
         }
         __syncthreads();
+        fetch(k0 + BKV);
         if (k0 > q0 + 31) continue;  // every key of this block is after every query of the wave
 
         // S^T tile: keys (32t + row) x this wave's 32 queries
@@ -125,33 +147,43 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16* __restric
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[t], 0, 0, 0);
             }
         }
+        // causal mask only where the block reaches past the wave's first query
+        const bool diag = k0 + BKV - 1 > q0;
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
                 float s = st[t][r] * scale_log2;
-                s = key > qme ? -INFINITY : s;
+                if (diag) {
+                    const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                    s = key > qme ? -INFINITY : s;
+                }
                 st[t][r] = s;
                 mx = fmaxf(mx, s);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // The running max is raised (and the output rescaled) only when a score
+        // exceeds it by more than 2^8: softmax does not depend on the reference
+        // value, so a stale max only scales P and l by the same factor <= 2^8.
+        if (__any(mx > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) oacc[i] *= alpha;
+        }
         float lsum = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(st[t][r] - m_new);
+                const float p = __builtin_amdgcn_exp2f(st[t][r] - m_run);
                 st[t][r] = p;
                 lsum += p;
             }
-        l_run = l_run * alpha + lsum;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) oacc[i] *= alpha;
+        l_run += lsum;
 
         // O^T[dim][q] += V^T[dim][key] P^T[key][q], 16 keys per MFMA
 #pragma unroll
