@@ -8,9 +8,52 @@
 // the weights from HBM with 16-byte coalesced loads, not around MFMA.
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace tp {
 
 namespace {
+
+// Stores output rows r1 and r1 + 32 (partners in one packed 64-row group) of
+// sequence b: fp32 partial, bf16 (GELU), SwiGLU of the (gate, up) pair, or
+// the rotary embedding of the (i, i + d/2) pair scattered to q and to the
+// KV cache at position pos0.
+template <int MODE>
+__device__ __forceinline__ void pair_store(const Epilogue& epi, int b, int r1, float y1, float y2) {
+    const int r2 = r1 + 32;
+    if constexpr (MODE == EPI_F32) {
+        float* o = (float*)epi.out + (long long)b * epi.ldo;
+        o[r1] = y1;
+        o[r2] = y2;
+    } else if constexpr (MODE == EPI_STORE || MODE == EPI_GELU) {
+        bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
+        o[r1] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y1) : y1);
+        o[r2] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y2) : y2);
+    } else if constexpr (MODE == EPI_SWIGLU) {
+        bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
+        o[(r1 >> 6) * 32 + (r1 & 31)] = f2bf(silu_f(y1) * y2);
+    } else {  // EPI_QKV, one token per sequence at position pos0
+        const QKVDest& q = epi.qkv;
+        const int d = q.d, half = d >> 1;
+        const int qcols = q.hl * d, kcols = q.kvl * d;
+        const int region = r1 < qcols ? 0 : (r1 < qcols + kcols ? 1 : 2);
+        const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
+        const int head = (r1 - base) / d;
+        const int i1 = 32 * (((r1 - base) % d) >> 6) + (r1 & 31);
+        float o1 = y1, o2 = y2;
+        if (region < 2 && q.rope_cos != nullptr) {
+            const float c = q.rope_cos[(long long)q.pos0 * half + i1];
+            const float sn = q.rope_sin[(long long)q.pos0 * half + i1];
+            o1 = y1 * c - y2 * sn;
+            o2 = y2 * c + y1 * sn;
+        }
+        bf16* dst = region == 0 ? (bf16*)q.q + ((long long)b * q.hl + head) * d
+                                : (bf16*)(region == 1 ? q.k : q.v) +
+                                      (((long long)b * q.kvl + head) * q.ld_seq + q.pos0) * d;
+        dst[i1] = f2bf(o1);
+        dst[i1 + half] = f2bf(o2);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // GEMV: y[b, n] = sum_k W[n, k] * in[b, k] for b < NB, optionally with the
@@ -121,40 +164,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
     const float y1 = red[0][e * NB + b] + red[1][e * NB + b] + red[2][e * NB + b] + red[3][e * NB + b];
     const int j2 = (P + e) * NB + b;
     const float y2 = red[0][j2] + red[1][j2] + red[2][j2] + red[3][j2];
-    const int r1 = rbase + e, r2 = rbase + 32 + e;
-
-    if constexpr (MODE == EPI_F32) {
-        float* o = (float*)epi.out + (long long)b * epi.ldo;
-        o[r1] = y1;
-        o[r2] = y2;
-    } else if constexpr (MODE == EPI_STORE || MODE == EPI_GELU) {
-        bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
-        o[r1] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y1) : y1);
-        o[r2] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y2) : y2);
-    } else if constexpr (MODE == EPI_SWIGLU) {
-        bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
-        o[(r1 >> 6) * 32 + (r1 & 31)] = f2bf(silu_f(y1) * y2);
-    } else {  // EPI_QKV, one token per sequence at position pos0
-        const QKVDest& q = epi.qkv;
-        const int d = q.d, half = d >> 1;
-        const int qcols = q.hl * d, kcols = q.kvl * d;
-        const int region = r1 < qcols ? 0 : (r1 < qcols + kcols ? 1 : 2);
-        const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
-        const int head = (r1 - base) / d;
-        const int i1 = 32 * (((r1 - base) % d) >> 6) + (r1 & 31);
-        float o1 = y1, o2 = y2;
-        if (region < 2 && q.rope_cos != nullptr) {
-            const float c = q.rope_cos[(long long)q.pos0 * half + i1];
-            const float sn = q.rope_sin[(long long)q.pos0 * half + i1];
-            o1 = y1 * c - y2 * sn;
-            o2 = y2 * c + y1 * sn;
-        }
-        bf16* dst = region == 0 ? (bf16*)q.q + ((long long)b * q.hl + head) * d
-                                : (bf16*)(region == 1 ? q.k : q.v) +
-                                      (((long long)b * q.kvl + head) * q.ld_seq + q.pos0) * d;
-        dst[i1] = f2bf(o1);
-        dst[i1 + half] = f2bf(o2);
-    }
+    pair_store<MODE>(epi, b, rbase + e, y1, y2);
 }
 
 // ---------------------------------------------------------------------------
@@ -307,6 +317,118 @@ __global__ __launch_bounds__(D) void attn_decode_combine(const float* __restrict
     O[((long long)b * hl + head) * D + dim] = f2bf(acc / L);
 }
 
+// ---------------------------------------------------------------------------
+// Skinny GEMM for small decode batches (2..64 sequences), split over K.
+//
+// y[b, n] = sum_k W[n, k] x[b, k] with v_mfma_f32_32x32x16_bf16: the weight
+// rows are the A operand (32 rows per tile), the batch the B operand (32
+// sequences per column tile, rows past B clamped to B-1 and discarded).
+// Work-group (g, z) owns the 64 rows of packed group g and the z-th share of
+// K; its 4 waves split that share in groups of 64 k.  Within a group each lane
+// reads 64 contiguous bytes of its row: the contraction order is free, so
+// half h of the lanes feeds k = 32 h + 8 j + [0, 8) into MFMA step j, for the
+// weights and the activations alike.  The waves' sums meet in LDS and go to
+// an fp32 scratch [z][b][n]; a second kernel sums the z shares and applies
+// the epilogue of the row pair (r, r + 32).
+constexpr int SK_ROWS = 64, SK_KG = 64;
+
+template <int NC>
+__global__ __launch_bounds__(256) void skinny_kernel(const bf16* __restrict__ x, int B, const bf16* __restrict__ W,
+                                                     int N, int K, int ks, float* __restrict__ part) {
+    __shared__ float red[4][2][NC][16][65];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * SK_ROWS, kz = blockIdx.y;
+    const int G = K / SK_KG, slot = kz * 4 + wave, nslots = ks * 4;
+    const int g0 = (int)((long long)G * slot / nslots), g1 = (int)((long long)G * (slot + 1) / nslots);
+    const int row = lane & 31, h = lane >> 5;
+    const bf16* w0 = W + (long long)(n0 + row) * K + 32 * h;
+    const bf16* w1 = w0 + 32LL * K;
+    const bf16* xr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) xr[c] = x + (long long)min(32 * c + row, B - 1) * K + 32 * h;
+
+    f32x16 acc[2][NC];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[t][c] = (f32x16){};
+    // two k-groups per iteration, all loads issued before the MFMAs; past the
+    // wave's last group the second group re-reads it (in bounds) with its
+    // activations zeroed, so no branch splits the loads from their use
+    for (int g = g0; g < g1; g += 2) {
+        const bool two = g + 1 < g1;
+        const int ka = g * SK_KG, kb = (two ? g + 1 : g) * SK_KG;
+        bf16x8 wf[2][2][4], xf[2][NC][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                wf[0][t][j] = *(const bf16x8*)((t ? w1 : w0) + ka + 8 * j);
+                wf[1][t][j] = *(const bf16x8*)((t ? w1 : w0) + kb + 8 * j);
+            }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xf[0][c][j] = *(const bf16x8*)(xr[c] + ka + 8 * j);
+                xf[1][c][j] = *(const bf16x8*)(xr[c] + kb + 8 * j);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!two) xf[1][c][j] = (bf16x8){};
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+                        acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[u][t][j], xf[u][c][j], acc[t][c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[wave][t][c][r][lane] = acc[t][c][r];
+    __syncthreads();
+    // accumulator register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32
+    for (int idx = tid; idx < SK_ROWS * B; idx += 256) {
+        const int i = idx & 63, b = idx >> 6;
+        const int t = i >> 5, rr = i & 31, c = b >> 5, col = b & 31;
+        const int ln = col + 32 * ((rr >> 2) & 1), r = 4 * (rr >> 3) + (rr & 3);
+        const float v = red[0][t][c][r][ln] + red[1][t][c][r][ln] + red[2][t][c][r][ln] + red[3][t][c][r][ln];
+        part[((long long)kz * B + b) * N + n0 + i] = v;
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void skinny_fixup(const float* __restrict__ part, int ks, int B, int N,
+                                                    Epilogue epi) {
+    const int npairs = N >> 1;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= B * npairs) return;
+    const int b = idx / npairs, p = idx - b * npairs;
+    const int r1 = (p >> 5) * 64 + (p & 31);
+    float y1 = 0.f, y2 = 0.f;
+    for (int z = 0; z < ks; ++z) {
+        const float* pz = part + ((long long)z * B + b) * N;
+        y1 += pz[r1];
+        y2 += pz[r1 + 32];
+    }
+    pair_store<MODE>(epi, b, r1, y1, y2);
+}
+
+int skinny_splits(int N, int K) {
+    const int groups = N / SK_ROWS, kgroups = K / SK_KG;
+    const int want = (512 + groups - 1) / groups;   // at least ~512 work-groups
+    return std::max(1, std::min(want, kgroups / 4));
+}
+
 template <int NB, int P, int NI, bool NORM>
 void gemv_mode(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
                hipStream_t st) {
@@ -382,6 +504,28 @@ void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W
                 }
             }
         }
+    }
+}
+
+size_t skinny_scratch_bytes(int B, int N, int K) {
+    return (size_t)skinny_splits(N, K) * B * N * sizeof(float);
+}
+
+void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,
+                 hipStream_t st) {
+    const int ks = skinny_splits(N, K);
+    const dim3 grid(N / SK_ROWS, ks);
+    if (B <= 32)
+        hipLaunchKernelGGL(skinny_kernel<1>, grid, dim3(256), 0, st, x, B, W, N, K, ks, part);
+    else
+        hipLaunchKernelGGL(skinny_kernel<2>, grid, dim3(256), 0, st, x, B, W, N, K, ks, part);
+    const dim3 fg(cdiv(B * (N >> 1), 256));
+    switch (epi.mode) {
+        case EPI_F32: hipLaunchKernelGGL(skinny_fixup<EPI_F32>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
+        case EPI_QKV: hipLaunchKernelGGL(skinny_fixup<EPI_QKV>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL(skinny_fixup<EPI_SWIGLU>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
+        case EPI_GELU: hipLaunchKernelGGL(skinny_fixup<EPI_GELU>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
+        default: hipLaunchKernelGGL(skinny_fixup<EPI_STORE>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
     }
 }
 

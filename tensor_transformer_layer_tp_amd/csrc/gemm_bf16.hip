@@ -523,6 +523,8 @@ const Cfg kCfgs[] = {
     {128, 128, 0.78f, 1},  // 6 dma 128x128 BK64 ST4
     {128, 128, 0.90f, 2},  // 7 dma 128x128 BK64 ST2
     {256, 128, 0.85f, 1},  // 8 dma 256x128 BK32 ST4
+    {128, 384, 0.95f, 1},  // 9 dma 128x384 BK32 ST4
+    {128, 384, 0.95f, 1},  // 10 dma 128x384 BK32 ST3
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -567,14 +569,16 @@ void launch_cfg(int c, const Args& a) {
         case 5: launch_pipe<256, 128, 64, 3, MODE>(a); break;
         case 6: launch_pipe<128, 128, 64, 4, MODE>(a); break;
         case 7: launch_dma<128, 128, 64, 2, MODE>(a); break;
-        default: launch_pipe<256, 128, 32, 4, MODE>(a); break;
+        case 8: launch_pipe<256, 128, 32, 4, MODE>(a); break;
+        case 9: launch_pipe<128, 384, 32, 4, MODE>(a); break;
+        default: launch_pipe<128, 384, 32, 3, MODE>(a); break;
     }
 }
 
-// Tiles of 256 rows and columns keep 256 accumulators per lane; with the
-// rotary and the erf epilogues the register-staged kernel spills them.
+// The two-stage 256x256 DMA kernel holds 256 accumulators per lane and
+// spills them with the rotary, erf and plain-store epilogues.
 bool usable(int c, int mode) {
-    return !(kCfgs[c].bm == 256 && kCfgs[c].bn == 256 && (mode == EPI_QKV || mode == EPI_GELU));
+    return !(c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE));
 }
 
 // Shape-based choice.  Large problems (at least 1.5 waves of 256x256 tiles)

@@ -56,6 +56,11 @@ void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B,
                       int hl, int kvl, int len, int ld_seq, int d, hipStream_t st);
 size_t attn_decode_scratch_bytes(int B, int hl, int len);
+// small decode batches (2..64): split-K MFMA projection + epilogue pass; part
+// is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
+void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,
+                 hipStream_t st);
+size_t skinny_scratch_bytes(int B, int N, int K);
 
 // ---- fp32 path ----
 void gemm_f32(const float* A, long long lda, const float* B, long long ldb, int M, int N, int K,

@@ -133,6 +133,12 @@ Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) 
     L.act = L.kv + al((size_t)2 * T * s->kvl * s->d * e);
     L.scr = L.act + al((size_t)T * s->fl * e);
     size_t scr = len_decode > 0 ? attn_decode_scratch_bytes(batch_decode, s->hl, len_decode) : 0;
+    if (batch_decode > 1) {
+        // split-K scratch of the small-batch decode projections
+        const int shapes[4][2] = {{s->nqkv, s->hidden}, {s->hidden, s->hl * s->d}, {s->nup, s->hidden},
+                                  {s->hidden, s->fl}};
+        for (const auto& nk : shapes) scr = std::max(scr, skinny_scratch_bytes(batch_decode, nk[0], nk[1]));
+    }
     L.total = L.scr + al(scr);
     return L;
 }
@@ -183,15 +189,29 @@ int launch_norm(tp_shard* s, const void* x, const void* g, void* out, long long 
     return TP_OK;
 }
 
-// decode projections at batch <= 8 stream the weights through the GEMV kernel,
-// whose threads hold a whole input row in registers (K <= 16384)
-constexpr int kGemvMaxBatch = 8;
+// Decode projections stream each weight once.  One sequence: the GEMV kernel,
+// whose threads hold a whole input row in registers (K <= 16384).  2..64
+// sequences: RMSNorm (if any) into the workspace, then the split-K MFMA
+// projection and its epilogue pass.  More sequences take the GEMM path.
+constexpr int kGemvMaxBatch = 1;
+constexpr int kSkinnyMaxBatch = 64;
 constexpr int kGemvMaxK = 16384;
 
 int launch_gemv(tp_shard* s, const void* x, int B, const void* gamma, const void* W, int N, int K,
-                const Epilogue& epi, hipStream_t st) {
-    gemv_bf16((const bf16*)x, B, (const bf16*)gamma, s->o.eps, (const bf16*)W, N, K, epi, st);
-    LAUNCH_CHECK("gemv");
+                const Epilogue& epi, void* nbuf, void* scratch, hipStream_t st) {
+    if (B <= kGemvMaxBatch) {
+        gemv_bf16((const bf16*)x, B, (const bf16*)gamma, s->o.eps, (const bf16*)W, N, K, epi, st);
+        LAUNCH_CHECK("gemv");
+        return TP_OK;
+    }
+    const void* xin = x;
+    if (gamma) {
+        rmsnorm_bf16((const bf16*)x, (const bf16*)gamma, (bf16*)nbuf, B, K, s->o.eps, st);
+        LAUNCH_CHECK("rmsnorm");
+        xin = nbuf;
+    }
+    skinny_bf16((const bf16*)xin, B, (const bf16*)W, N, K, (float*)scratch, epi, st);
+    LAUNCH_CHECK("skinny projection");
     return TP_OK;
 }
 
@@ -481,8 +501,9 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
     if (!s->loaded) return TP_E_STATE;
     hipStream_t st = (hipStream_t)stream;
     const bool bf = s->o.dtype == TP_BF16;
-    const bool use_gemv = bf && batch <= kGemvMaxBatch && s->hidden <= kGemvMaxK && s->hl * s->d <= kGemvMaxK &&
-                          s->fl <= kGemvMaxK;
+    const bool use_gemv = bf && (batch <= kGemvMaxBatch ? s->hidden <= kGemvMaxK && s->hl * s->d <= kGemvMaxK &&
+                                                               s->fl <= kGemvMaxK
+                                                         : batch <= kSkinnyMaxBatch);
     if (stage == TP_STAGE_ATTN) {
         if (!kv) return TP_E_ARG;
         if (kv->batch != batch || kv->dtype != s->o.dtype || kv->kvl != s->kvl) return TP_E_ARG;
@@ -506,7 +527,8 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.qkv = QKVDest{1, L, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
                               s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
             KTimer kt(s, TP_K_GEMV_QKV, st);
-            TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi, st));
+            TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi,
+                            ws + lay.n, ws + lay.scr, st));
         } else {
             const void* xin = x;
             if (s->o.rmsnorm) {
@@ -533,7 +555,8 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.out = partial;
             epi.ldo = s->hidden;
             KTimer kt(s, TP_K_GEMV_OUT, st);
-            TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, st));
+            TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, ws + lay.n,
+                            ws + lay.scr, st));
         } else {
             KTimer kt(s, TP_K_GEMM_OUT, st);
             TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
@@ -548,14 +571,16 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.ldo = s->fl;
             {
                 KTimer kt(s, TP_K_GEMV_UP, st);
-                TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi, st));
+                TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi,
+                                ws + lay.n, ws + lay.scr, st));
             }
             Epilogue e2{};
             e2.mode = EPI_F32;
             e2.out = partial;
             e2.ldo = s->hidden;
             KTimer kt(s, TP_K_GEMV_DOWN, st);
-            TRY(launch_gemv(s, ws + lay.act, batch, nullptr, s->w_down, s->hidden, s->fl, e2, st));
+            TRY(launch_gemv(s, ws + lay.act, batch, nullptr, s->w_down, s->hidden, s->fl, e2, ws + lay.n,
+                            ws + lay.scr, st));
         } else {
             const void* xin = x;
             if (s->o.rmsnorm) {

@@ -196,7 +196,9 @@ def test_decode_steps_match_oracle(B):
     (768, 6, 6, 6144, 1, 2),      # K = 768 and 6144: 1 and 3 chunks of 2048 per thread
     (512, 4, 2, 11008, 1, 4),     # K = 11008: 6 chunks (8-chunk variant, ragged)
     (256, 2, 2, 20480, 1, 1),     # FFN shard 20480 > 16384: decode falls back to the GEMM path
-    (2048, 32, 8, 2816, 2, 7),    # 16 local heads, 4 KV heads (G = 4), batch split 4 + 3
+    (2048, 32, 8, 2816, 2, 7),    # 16 local heads, 4 KV heads (G = 4)
+    (1024, 8, 4, 5504, 2, 33),    # two 32-sequence column tiles, ragged; down K = 2752 (43 groups of 64)
+    (512, 8, 8, 1536, 1, 64),     # the largest split-K batch
 ])
 def test_decode_gemv_shapes(hidden, heads, kv, ffn, tp, B):
     announce(f"bf16 decode shapes hidden={hidden} heads={heads}/{kv} ffn={ffn} t={tp} B={B}")
@@ -403,7 +405,7 @@ def test_every_gemm_config(ffn):
     ref_a = O.attn_stage(L.exact["x"], L.W, L.spec, 2, 1)
     ref_m = O.mlp_stage(h.float().numpy(), L.W, L.spec, 2, 1)
     sh = L.shard(2, 1)
-    n_cfg = 9
+    n_cfg = 11
     assert N.lib().tp_tune_set_gemm_config(n_cfg) == N.TP_E_ARG   # the table has exactly n_cfg entries
     try:
         for cfg in range(n_cfg):
