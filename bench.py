@@ -275,10 +275,9 @@ def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copie
     return layers
 
 
-def decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=None):
+def decode_step_fn(torch, layers, hidden, t, B, x0):
     """One decode token for B sequences through every layer copy: ATTN stage,
-    reduce, MLP stage, reduce (other ranks' partials are fixed stand-ins).
-    With reset_len every step decodes at that cache length."""
+    reduce, MLP stage, reduce (other ranks' partials are fixed stand-ins)."""
     from tensor_transformer_layer_tp_amd import ATTN, MLP, partial_reduce
     g = torch.Generator(device="cuda")
     g.manual_seed(98)
@@ -291,8 +290,6 @@ def decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=None):
     def step():
         x = x0
         for i, (sh, kv) in enumerate(layers):
-            if reset_len is not None:
-                kv.length = reset_len
             sh.decode(ATTN, x, kv, out=pa)
             partial_reduce([pa, *others], residual=x, out=hb)
             sh.decode(MLP, hb, out=pm)
@@ -303,14 +300,31 @@ def decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=None):
     return step
 
 
+def capture(torch, fn):
+    """fn's launches recorded in a HIP graph (fn must have run once eagerly
+    with the same shapes, so that nothing is allocated during capture)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0, roof_key):
+    """Decode through a stack of layer copies: eager calls, then the same
+    step captured once in a HIP graph and replayed (each replay appends one
+    token per layer: the kernels read and advance the device-resident cache
+    length), then a per-kernel breakdown pass with event markers."""
     wb = weight_bytes(hidden, heads, kv_heads, ffn, t)
     nl = args.decode_layers or max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
-    cap = L0 + args.warmup + 2 * args.steps + 4
+    cap = L0 + 4 * (args.warmup + args.steps) + 8
     layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, 1, L0, cap, nl, fill)
     stream = torch.cuda.current_stream()
     step = decode_step_fn(torch, layers, hidden, t, 1, x0)
     ms, dist = timed(torch, step, args.steps, args.warmup, stream)
+    g = capture(torch, step)
+    gms, gdist = timed(torch, g.replay, args.steps, args.warmup, torch.cuda.current_stream())
+    del g
     for sh, _ in layers:
         sh.timing(True)
     timed(torch, step, args.steps, 0, stream)
@@ -324,9 +338,9 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
     for sh, kv in layers:
         kv.close()
         sh.close()
-    L_avg = L0 + args.warmup + args.steps + (args.steps - 1) / 2.0   # mean cache length of the timed steps
+    L_avg = L0 + 2 * (args.warmup + args.steps)   # mean cache length over the timed passes
     nbytes, per_kernel = decode_bytes(hidden, heads, kv_heads, ffn, t, 1, int(L_avg))
-    us = 1e3 * ms / nl
+    us, us_graph = 1e3 * ms / nl, 1e3 * gms / nl
     kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in agg.items()}
     for k, b in per_kernel.items():
         if k in kern:
@@ -334,13 +348,17 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
     dom = "gemv_up"
     ach = per_kernel[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
     d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
+    best = min(us, us_graph)
     return {
         "workload": f"{name}, {nl} distinct layer copies ({nl * wb / 1e9:.2f} GB of weights)",
-        "us_per_token_layer": round(us, 3),
+        "us_per_token_layer": round(best, 3),
+        "us_per_token_layer_eager": round(us, 3),
+        "us_per_token_layer_graph": round(us_graph, 3),
         "step_ms": dist,
+        "step_ms_graph": gdist,
         "bytes_per_token_layer": nbytes,
-        "hbm_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-        "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "hbm_GBps": round(nbytes / (best * 1e-6) / 1e9, 1),
+        "hbm_frac": round(nbytes / (best * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "kernels": {k: rounded(v) for k, v in kern.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic_for(roof_key, "decode.hip"),
@@ -430,7 +448,8 @@ def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
     from tensor_transformer_layer_tp_amd import synth
     stream = torch.cuda.current_stream()
     x = synth.draw_normal_device((B, S, hidden), 1000 + B * 10000 + S)
-    sh, kv, step = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, False, kv_cap=S + 1)
+    extra = 16                                   # decode steps the caches leave room for
+    sh, kv, step = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, False, kv_cap=S + extra)
     step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -442,19 +461,21 @@ def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
     gemm, attn = prefill_flops(hidden, heads, kv_heads, ffn, t, B, S)
     pre = {"ms": ms, "median_ms": dist["median"], "tflops": (sum(gemm.values()) + attn) / (ms * 1e-3) / 1e12}
     del step
-    # decode one token per sequence at cache length S over the cache this
+    # decode one token per sequence from cache length S over the cache this
     # prefill left, through enough layer copies to span >= 1 GB of weights
     wb = weight_bytes(hidden, heads, kv_heads, ffn, t)
     nl = max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
-    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, S, S + 1, nl, lambda k: k.copy_from(kv))
+    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, S, S + extra, nl,
+                          lambda k: k.copy_from(kv))
     kv.close()
     sh.close()
     del x
     x0 = synth.draw_normal_device((B, hidden), 7)
-    dstep = decode_step_fn(torch, layers, hidden, t, B, x0, reset_len=S)
-    dms, _ = timed(torch, dstep, max(3, min(args.steps, 10)), 2, stream)
+    dstep = decode_step_fn(torch, layers, hidden, t, B, x0)
+    nd = max(3, min(args.steps, 10))
+    dms, _ = timed(torch, dstep, nd, 2, stream)
     us = 1e3 * dms / nl
-    nbytes, _ = decode_bytes(hidden, heads, kv_heads, ffn, t, B, S)
+    nbytes, _ = decode_bytes(hidden, heads, kv_heads, ffn, t, B, S + 2 + nd // 2)
     dec = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
     for s_, k_ in layers:
         k_.close()

@@ -137,7 +137,12 @@ int tp_kv_create(const tp_shard *s, int batch, int max_seq, tp_kv **out);
  * to fill a cache with synthetic content.  Either output may be NULL. */
 int tp_kv_view(tp_kv *kv, void **k, void **v);
 
-/* tp_kv_set_len / tp_kv_get_len -- number of valid positions [0, len). */
+/* tp_kv_set_len / tp_kv_get_len -- number of valid positions [0, len).
+ * The length lives in device memory, where the kernels read and advance it
+ * (so a decode call captured in a HIP graph stays correct on replay); the
+ * library also keeps a host copy for its capacity checks.  Both calls wait
+ * for the whole device first (hipDeviceSynchronize), then copy the value;
+ * get_len also refreshes the host copy.  TP_E_ARG if len > max_seq. */
 int tp_kv_set_len(tp_kv *kv, int len);
 int tp_kv_get_len(const tp_kv *kv, int *len);
 
@@ -155,11 +160,19 @@ int tp_shard_forward_prefill(tp_shard *s, int stage, const void *x,
 /* tp_shard_forward_decode -- one stage for one new token per sequence.
  *   stage TP_STAGE_ATTN: x [batch, hidden] sits at position L = the cache
  *     length; its k, v are appended at slot L, the query attends to
- *     positions 0..L, and the cache length becomes L+1 (updated on the
- *     host when the call returns).  TP_E_KV_FULL if L == max_seq; batch
- *     must equal the cache's batch.
+ *     positions 0..L, and the cache length becomes L+1.  TP_E_KV_FULL if
+ *     the host copy of L equals max_seq; batch must equal the cache's batch.
  *   stage TP_STAGE_MLP: x = reduced h [batch, hidden]; kv must be NULL.
- *   partial [batch, hidden] fp32 receives this rank's summand. */
+ *   partial [batch, hidden] fp32 receives this rank's summand.
+ * Graph capture (TP_BF16 only): the kernels take L from the cache's device
+ * length and advance it themselves, the attention grid and the workspace are
+ * sized by max_seq, so a captured sequence of decode calls may be replayed;
+ * each replay appends one token per captured ATTN call.  Make one eager call
+ * of the same shape first (it sizes the workspace and the rotary table: no
+ * allocation may happen during capture).  A replay past max_seq appends
+ * nothing and attends over the first max_seq positions; the host copy of the
+ * length is refreshed by tp_kv_get_len.  TP_F32 shards return TP_E_STATE on a
+ * capturing stream. */
 int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
                             tp_kv *kv, float *partial, void *stream);
 

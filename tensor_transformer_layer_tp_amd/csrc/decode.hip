@@ -40,16 +40,18 @@ __device__ __forceinline__ void pair_store(const Epilogue& epi, int b, int r1, f
         const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
         const int head = (r1 - base) / d;
         const int i1 = 32 * (((r1 - base) % d) >> 6) + (r1 & 31);
+        const int pos = q.pos_dev ? *q.pos_dev : q.pos0;
+        if (region > 0 && pos >= q.ld_seq) return;   // cache full: nothing to append
         float o1 = y1, o2 = y2;
         if (region < 2 && q.rope_cos != nullptr) {
-            const float c = q.rope_cos[(long long)q.pos0 * half + i1];
-            const float sn = q.rope_sin[(long long)q.pos0 * half + i1];
+            const float c = q.rope_cos[(long long)pos * half + i1];
+            const float sn = q.rope_sin[(long long)pos * half + i1];
             o1 = y1 * c - y2 * sn;
             o2 = y2 * c + y1 * sn;
         }
         bf16* dst = region == 0 ? (bf16*)q.q + ((long long)b * q.hl + head) * d
                                 : (bf16*)(region == 1 ? q.k : q.v) +
-                                      (((long long)b * q.kvl + head) * q.ld_seq + q.pos0) * d;
+                                      (((long long)b * q.kvl + head) * q.ld_seq + pos) * d;
         dst[i1] = f2bf(o1);
         dst[i1 + half] = f2bf(o2);
     }
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
     __shared__ float red[4][R * NB];
     __shared__ float rs_s[NB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (blockIdx.x == 0 && tid == 0) apply_len_update(epi.len);
     const int per_group = 32 / P;
     const int grp = blockIdx.x / per_group, sub = blockIdx.x % per_group;
     const int rbase = 64 * grp + P * sub;   // rows rbase + e and rbase + 32 + e, e < P
@@ -177,10 +180,13 @@ constexpr int CH = 64;
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict__ q, const bf16* __restrict__ K,
                                                          const bf16* __restrict__ V, float* __restrict__ scr,
-                                                         int hl, int kvl, int len, int ld_seq, float scale_log2) {
+                                                         int hl, int kvl, const int* __restrict__ len_dev,
+                                                         int ld_seq, float scale_log2) {
     const int G = hl / kvl;
     const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    const int nchunks = gridDim.x;
+    const int nchunks = gridDim.x;   // chunk stride of the scratch (sized for ld_seq positions)
+    const int len = min(*len_dev + 1, ld_seq);
+    if (chunk * CH >= len) return;   // past the cache length: no work
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     extern __shared__ float sm[];
     float* sq = sm;                 // [G][D]
@@ -280,12 +286,14 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
 // with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
-                                                         int hl, int nchunks) {
+                                                         int hl, int stride, const int* __restrict__ len_dev,
+                                                         int ld_seq) {
     constexpr int NW = D / 64, TILE = 1024;
     __shared__ float sw[TILE];
     __shared__ float sred[NW];
     const int head = blockIdx.x, b = blockIdx.y, dim = threadIdx.x, lane = dim & 63, wave = dim >> 6;
-    const float* st = scr + ((long long)b * hl + head) * nchunks * (D + 2);
+    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by attn_decode_chunk
+    const float* st = scr + ((long long)b * hl + head) * stride * (D + 2);
     float m = -INFINITY;
     for (int c = dim; c < nchunks; c += D) m = fmaxf(m, st[c * (D + 2) + D]);
     m = wave_max(m);
@@ -411,6 +419,7 @@ __global__ __launch_bounds__(256) void skinny_fixup(const float* __restrict__ pa
                                                     Epilogue epi) {
     const int npairs = N >> 1;
     const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx == 0) apply_len_update(epi.len);
     if (idx >= B * npairs) return;
     const int b = idx / npairs, p = idx - b * npairs;
     const int r1 = (p >> 5) * 64 + (p & 31);
@@ -529,25 +538,29 @@ void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part,
     }
 }
 
-size_t attn_decode_scratch_bytes(int B, int hl, int len) {
-    const int nchunks = (len + CH - 1) / CH;
+size_t attn_decode_scratch_bytes(int B, int hl, int cap) {
+    const int nchunks = (cap + CH - 1) / CH;
     return (size_t)B * hl * nchunks * (128 + 2) * sizeof(float);
 }
 
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
-                      int kvl, int len, int ld_seq, int d, hipStream_t st) {
-    const int nchunks = (len + CH - 1) / CH;
+                      int kvl, const int* len_dev, int ld_seq, int d, hipStream_t st) {
+    const int nchunks = (ld_seq + CH - 1) / CH;
     const int G = hl / kvl;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     dim3 grid(nchunks, kvl, B);
     // LDS: q [G][d], scores [G][CH], per-head partial sums [256/(d/8)][d]
     const size_t lds = ((size_t)G * d + (size_t)G * CH + (size_t)(256 / (d / 8)) * d) * sizeof(float);
     if (d == 128) {
-        hipLaunchKernelGGL(attn_decode_chunk<128>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len, ld_seq, scale_log2);
-        hipLaunchKernelGGL(attn_decode_combine<128>, dim3(hl, B), dim3(128), 0, st, scratch, O, hl, nchunks);
+        hipLaunchKernelGGL(attn_decode_chunk<128>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len_dev, ld_seq,
+                           scale_log2);
+        hipLaunchKernelGGL(attn_decode_combine<128>, dim3(hl, B), dim3(128), 0, st, scratch, O, hl, nchunks, len_dev,
+                           ld_seq);
     } else {
-        hipLaunchKernelGGL(attn_decode_chunk<64>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len, ld_seq, scale_log2);
-        hipLaunchKernelGGL(attn_decode_combine<64>, dim3(hl, B), dim3(64), 0, st, scratch, O, hl, nchunks);
+        hipLaunchKernelGGL(attn_decode_chunk<64>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len_dev, ld_seq,
+                           scale_log2);
+        hipLaunchKernelGGL(attn_decode_combine<64>, dim3(hl, B), dim3(64), 0, st, scratch, O, hl, nchunks, len_dev,
+                           ld_seq);
     }
 }
 

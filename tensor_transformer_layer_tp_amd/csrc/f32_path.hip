@@ -23,6 +23,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     __shared__ float Bs[TK][T + 1];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) apply_len_update(epi.len);
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += TK) {
         for (int i = tid; i < T * TK; i += 256) {

@@ -116,7 +116,8 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
             bf16* dbase = region == 0 ? (bf16*)q.q : (region == 1 ? (bf16*)q.k : (bf16*)q.v);
             const int nh = region == 0 ? q.hl : q.kvl;
             const int ld = region == 0 ? q.S : q.ld_seq;
-            const int poff = region == 0 ? 0 : q.pos0;   // q is stored by token index, k/v by position
+            const int base_pos = q.pos_dev ? *q.pos_dev : q.pos0;
+            const int poff = region == 0 ? 0 : base_pos;   // q is stored by token index, k/v by position
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -124,7 +125,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                     const int row = wrow0 + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
                     const int rr = min(row, M - 1);
                     const int b = rr / q.S, s = rr - b * q.S;
-                    const int pos = q.pos0 + s;
+                    const int pos = base_pos + s;
                     float y1 = acc[i][2 * p][r], y2 = acc[i][2 * p + 1][r];
                     float c = 1.f, sn = 0.f;
                     if (rot) {
@@ -134,7 +135,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                     const float o1 = y1 * c - y2 * sn;
                     const float o2 = y2 * c + y1 * sn;
                     bf16* dst = dbase + (((long long)b * nh + head) * ld + poff + s) * d;
-                    if (row < M && gcol < N) {
+                    if (row < M && gcol < N && (region == 0 || pos < q.ld_seq)) {
                         dst[i1] = f2bf(o1);
                         dst[i1 + half] = f2bf(o2);
                     }
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) apply_len_update(epi.len);
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -315,6 +317,7 @@ __global__ __launch_bounds__(256) void gemm_dma_pipe_kernel(const bf16* __restri
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA addressing scalar
     const int wm = wave >> 1, wn = wave & 1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) apply_len_update(epi.len);
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -438,6 +441,7 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const bf16* __restrict__ 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) apply_len_update(epi.len);
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;

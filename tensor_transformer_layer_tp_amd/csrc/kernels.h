@@ -17,6 +17,8 @@ enum EpiMode {
 struct QKVDest {
     int S;              // tokens per sequence in this call (1 for decode)
     int pos0;           // position of token 0 (0 for prefill, L for decode)
+    const int* pos_dev; // if set, token 0's position is read from device memory instead
+                        // (the cache length); k/v stores at positions >= ld_seq are dropped
     int hl, kvl, d;     // local query heads, local kv heads, head dim
     void* q;            // [B, hl, S, d]
     void* k;            // [B, kvl, ld_seq, d], written at slots pos0 + s
@@ -26,12 +28,31 @@ struct QKVDest {
     const float* rope_sin;
 };
 
+// Update of a device-resident cache length, done by one thread of the
+// projection that follows the last reader of the length in a stage.
+struct LenUpdate {
+    int* ptr;           // nullptr: no update
+    int value;          // >= 0: *ptr = value;  < 0: *ptr = min(*ptr + 1, cap)
+    int cap;
+};
+
 struct Epilogue {
     int mode;
     void* out;          // F32: float*, others: element-type pointer
     long long ldo;      // leading dimension of out, in elements
     QKVDest qkv;
+    LenUpdate len;
 };
+
+__device__ __forceinline__ void apply_len_update(const LenUpdate& u) {
+    if (u.ptr == nullptr) return;
+    if (u.value >= 0) {
+        *u.ptr = u.value;
+    } else {
+        const int v = *u.ptr;
+        *u.ptr = v < u.cap ? v + 1 : v;
+    }
+}
 
 // Packed column layout shared by the projection kernels: for Q/K/V heads and
 // for the gate/up pair, every 64-row group of the packed weight holds two
@@ -53,9 +74,12 @@ void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int
                        int S, int ld_seq, int d, hipStream_t st);
 void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W, int N, int K,
                const Epilogue& epi, hipStream_t st);
+// decode attention over positions [0, *len_dev + 1) (capped at ld_seq); the
+// grid and the scratch are sized for ld_seq positions so that one launch
+// stays valid while the device length grows (graph replay)
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B,
-                      int hl, int kvl, int len, int ld_seq, int d, hipStream_t st);
-size_t attn_decode_scratch_bytes(int B, int hl, int len);
+                      int hl, int kvl, const int* len_dev, int ld_seq, int d, hipStream_t st);
+size_t attn_decode_scratch_bytes(int B, int hl, int cap);
 // small decode batches (2..64): split-K MFMA projection + epilogue pass; part
 // is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
 void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,

@@ -46,7 +46,9 @@ struct tp_shard {
 };
 
 struct tp_kv {
-    int batch, max_seq, len;
+    int batch, max_seq;
+    int len;      // host copy of the cache length, advanced by every enqueued call
+    int* dlen;    // device copy, read and advanced by the kernels themselves
     int kvl, d;
     size_t esz;
     int dtype;
@@ -144,11 +146,12 @@ Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) 
 }
 
 int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void* q, void* k, void* v,
-               int ld_seq, hipStream_t st) {
+               int ld_seq, hipStream_t st, const int* pos_dev = nullptr) {
     Epilogue epi{};
     epi.mode = EPI_QKV;
     epi.qkv.S = S;
     epi.qkv.pos0 = pos0;
+    epi.qkv.pos_dev = pos_dev;
     epi.qkv.hl = s->hl;
     epi.qkv.kvl = s->kvl;
     epi.qkv.d = s->d;
@@ -167,11 +170,12 @@ int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void
 }
 
 int launch_proj(tp_shard* s, const void* A, long long M, int K, const void* W, int N, int mode, void* out,
-                long long ldo, hipStream_t st) {
+                long long ldo, hipStream_t st, LenUpdate len = LenUpdate{nullptr, 0, 0}) {
     Epilogue epi{};
     epi.mode = mode;
     epi.out = out;
     epi.ldo = ldo;
+    epi.len = len;
     if (s->o.dtype == TP_BF16)
         gemm_bf16((const bf16*)A, K, (const bf16*)W, K, (int)M, N, K, epi, st);
     else
@@ -381,14 +385,18 @@ int tp_kv_create(const tp_shard* s, int batch, int max_seq, tp_kv** out) {
     kv->esz = s->esz;
     kv->dtype = s->o.dtype;
     size_t bytes = (size_t)batch * s->kvl * max_seq * s->d * s->esz;
-    if (hipMalloc(&kv->k, bytes) != hipSuccess || hipMalloc(&kv->v, bytes) != hipSuccess) {
+    if (hipMalloc(&kv->k, bytes) != hipSuccess || hipMalloc(&kv->v, bytes) != hipSuccess ||
+        hipMalloc((void**)&kv->dlen, sizeof(int)) != hipSuccess) {
         if (kv->k) (void)hipFree(kv->k);
+        if (kv->v) (void)hipFree(kv->v);
         delete kv;
         return TP_E_NOMEM;
     }
-    if (hipMemset(kv->k, 0, bytes) != hipSuccess || hipMemset(kv->v, 0, bytes) != hipSuccess) {
+    if (hipMemset(kv->k, 0, bytes) != hipSuccess || hipMemset(kv->v, 0, bytes) != hipSuccess ||
+        hipMemset(kv->dlen, 0, sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(kv->k);
         (void)hipFree(kv->v);
+        (void)hipFree(kv->dlen);
         delete kv;
         return hip_fail(hipGetLastError(), "hipMemset(kv)");
     }
@@ -405,13 +413,19 @@ int tp_kv_view(tp_kv* kv, void** k, void** v) {
 
 int tp_kv_set_len(tp_kv* kv, int len) {
     if (!kv || len < 0 || len > kv->max_seq) return TP_E_ARG;
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(kv->dlen, &len, sizeof(int), hipMemcpyHostToDevice));
     kv->len = len;
     return TP_OK;
 }
 
 int tp_kv_get_len(const tp_kv* kv, int* len) {
     if (!kv || !len) return TP_E_ARG;
-    *len = kv->len;
+    int v = 0;
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(&v, kv->dlen, sizeof(int), hipMemcpyDeviceToHost));
+    const_cast<tp_kv*>(kv)->len = v;   // replays of captured calls advance only the device copy
+    *len = v;
     return TP_OK;
 }
 
@@ -471,7 +485,8 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         }
         {
             KTimer kt(s, TP_K_GEMM_OUT, st);
-            TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
+            TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
+                            kv ? LenUpdate{kv->dlen, seq, 0} : LenUpdate{nullptr, 0, 0}));
         }
         if (kv) kv->len = seq;
     } else {
@@ -511,20 +526,27 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
     } else if (kv) {
         return TP_E_ARG;
     }
+    // bf16 decode takes the cache length from the device copy, so a captured
+    // call stays valid on replay; the fp32 path uses the host copy
+    if (!bf) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(st, &cs));
+        if (cs != hipStreamCaptureStatusNone) return TP_E_STATE;
+    }
     const int L = stage == TP_STAGE_ATTN ? kv->len : 0;
-    Layout lay = layout(s, batch, stage == TP_STAGE_ATTN ? L + 1 : 0, batch);
+    Layout lay = layout(s, batch, stage == TP_STAGE_ATTN ? kv->max_seq : 0, batch);
     TRY(ensure_ws(s, lay.total));
     char* ws = s->ws;
     s->off_n = lay.n;
     s->off_o = lay.o;
     s->off_act = lay.act;
     if (stage == TP_STAGE_ATTN) {
-        TRY(ensure_rope(s, L + 1, st));
+        TRY(ensure_rope(s, kv->max_seq + 1, st));   // a query at position max_seq (full cache) stays in range
         void* qbuf = ws + lay.q;
         if (use_gemv) {
             Epilogue epi{};
             epi.mode = EPI_QKV;
-            epi.qkv = QKVDest{1, L, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
+            epi.qkv = QKVDest{1, L, kv->dlen, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
                               s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
             KTimer kt(s, TP_K_GEMV_QKV, st);
             TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi,
@@ -537,13 +559,13 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
                 xin = ws + lay.n;
             }
             KTimer kt(s, TP_K_GEMM_QKV, st);
-            TRY(launch_qkv(s, xin, batch, 1, L, qbuf, kv->k, kv->v, kv->max_seq, st));
+            TRY(launch_qkv(s, xin, batch, 1, L, qbuf, kv->k, kv->v, kv->max_seq, st, bf ? kv->dlen : nullptr));
         }
         {
             KTimer kt(s, TP_K_ATTN_DECODE, st);
             if (bf)
                 attn_decode_bf16((const bf16*)qbuf, (const bf16*)kv->k, (const bf16*)kv->v, (bf16*)(ws + lay.o),
-                                 (float*)(ws + lay.scr), batch, s->hl, s->kvl, L + 1, kv->max_seq, s->d, st);
+                                 (float*)(ws + lay.scr), batch, s->hl, s->kvl, kv->dlen, kv->max_seq, s->d, st);
             else
                 attn_f32((const float*)qbuf, (const float*)kv->k, (const float*)kv->v, (float*)(ws + lay.o), batch,
                          s->hl, s->kvl, 1, L, kv->max_seq, s->d, st);
@@ -554,12 +576,14 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.mode = EPI_F32;
             epi.out = partial;
             epi.ldo = s->hidden;
+            epi.len = LenUpdate{kv->dlen, -1, kv->max_seq};
             KTimer kt(s, TP_K_GEMV_OUT, st);
             TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, ws + lay.n,
                             ws + lay.scr, st));
         } else {
             KTimer kt(s, TP_K_GEMM_OUT, st);
-            TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st));
+            TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
+                            LenUpdate{kv->dlen, -1, kv->max_seq}));
         }
         kv->len = L + 1;
     } else {
@@ -682,6 +706,7 @@ void tp_kv_destroy(tp_kv* kv) {
     if (!kv) return;
     if (kv->k) (void)hipFree(kv->k);
     if (kv->v) (void)hipFree(kv->v);
+    if (kv->dlen) (void)hipFree(kv->dlen);
     delete kv;
 }
 

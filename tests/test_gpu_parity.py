@@ -244,6 +244,67 @@ def test_decode_long_cache(L_len):
     assert_close(o, ref["o"].reshape(B, -1), "decode o", "bf16")
 
 
+@pytest.mark.parametrize("B", [1, 3, 70])   # GEMV, split-K and GEMM projection paths
+def test_decode_graph_replay(B):
+    """A decode step (ATTN + MLP stage) captured in a HIP graph and replayed
+    with new inputs: every replay must equal the same step made by eager
+    calls on a twin shard, and the device-resident cache length must advance
+    by one per replay.  Eager work and synchronisations run between replays."""
+    announce(f"decode step in a HIP graph, B={B}: eager warm-up + 3 replays against eager twins")
+    S, hid = 24, 512
+    L = Layer(hid, 4, 2, 1024, batch=B, seq=S + 4, gamma_noise=True, seed=31)
+    sh_e, sh_g = L.shard(2, 1), L.shard(2, 1)
+    kv_e, kv_g = sh_e.kv_cache(B, S + 8), sh_g.kv_cache(B, S + 8)
+    pre = L.dev["x"][:, :S].contiguous()
+    sh_e.prefill(ATTN, pre, kv_e)
+    sh_g.prefill(ATTN, pre, kv_g)
+    hs = [synth.to_storage(synth.draw_normal((B, hid), 40 + i), "bf16").cuda() for i in range(4)]
+    xbuf = torch.empty((B, hid), dtype=torch.bfloat16, device="cuda")
+    hbuf = torch.empty_like(xbuf)
+    pa, pm = nan_like((B, hid)), nan_like((B, hid))
+
+    def step():
+        sh_g.decode(ATTN, xbuf, kv_g, out=pa)
+        sh_g.decode(MLP, hbuf, out=pm)
+
+    def eager(i):
+        pe = sh_e.decode(ATTN, L.dev["x"][:, S + i].contiguous(), kv_e)
+        me = sh_e.decode(MLP, hs[i])
+        return pe, me
+
+    # step 0 eagerly on both (sizes the workspace before capture)
+    xbuf.copy_(L.dev["x"][:, S])
+    hbuf.copy_(hs[0])
+    step()
+    pe, me = eager(0)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pe) and torch.equal(pm, me)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    assert kv_g.length == S + 1                      # capture executes nothing
+    for i in range(1, 4):
+        xbuf.copy_(L.dev["x"][:, S + i])
+        hbuf.copy_(hs[i])
+        g.replay()
+        pe, me = eager(i)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pe), f"replay {i}: attention partial differs from the eager call"
+        assert torch.equal(pm, me), f"replay {i}: MLP partial differs from the eager call"
+        assert kv_g.length == S + 1 + i
+    kg, vg = kv_g.read()
+    ke, ve = kv_e.read()
+    torch.cuda.synchronize()
+    assert torch.equal(kg, ke) and torch.equal(vg, ve)
+    # the eager twin itself against the oracle at the last step
+    x = L.exact["x"]
+    ref_pre = O.attn_stage(x[:, :S + 3], L.W, L.spec, 2, 1)
+    ref = O.decode_attn_stage(x[:, S + 3], ref_pre["k"], ref_pre["v"], L.W, L.spec, 2, 1)
+    assert_close(to_np(pe), ref["partial"], "last replayed step vs oracle", "bf16")
+    del g
+
+
 def test_decode_equals_prefill_row():
     """Same math both ways: decode of token L after a prefill of L tokens
     equals row L of a prefill over L+1 tokens (GPU against GPU, then both
