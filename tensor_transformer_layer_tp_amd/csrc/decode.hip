@@ -171,14 +171,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV decode attention.  Work-group (chunk, kv head, batch) scores CH
-// cached positions for every query head of the GQA group, and writes the
-// chunk's running max, sum and unnormalised output; a second kernel merges
-// the chunks.
-constexpr int CH = 64;
-
+// Split-KV decode attention.  Work-group (chunk, kv head, sequence) takes a
+// chunk of cached positions for every query head of the GQA group and
+// writes, per head, the chunk's maximum, sum and unnormalised output; a
+// second kernel merges the chunks.  Chunks at or past the device-resident
+// cache length exit at once (the grid is sized for the capacity).
+//
+// One query head per KV head (G = 1): chunks of 64 positions; thread = (key,
+// quarter of the head dim) for the scores, (8-dim chunk, key group) for P V.
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict__ q, const bf16* __restrict__ K,
+__global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restrict__ q, const bf16* __restrict__ K,
                                                          const bf16* __restrict__ V, float* __restrict__ scr,
                                                          int hl, int kvl, const int* __restrict__ len_dev,
                                                          int ld_seq, float scale_log2) {
@@ -186,12 +188,12 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int nchunks = gridDim.x;   // chunk stride of the scratch (sized for ld_seq positions)
     const int len = min(*len_dev + 1, ld_seq);
-    if (chunk * CH >= len) return;   // past the cache length: no work
+    if (chunk * 64 >= len) return;   // past the cache length: no work
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     extern __shared__ float sm[];
     float* sq = sm;                 // [G][D]
-    float* ss = sm + G * D;         // [G][CH]
-    const int k0 = chunk * CH;
+    float* ss = sm + G * D;         // [G][64]
+    const int k0 = chunk * 64;
 
     for (int i = tid; i < G * D; i += 256) {
         const int g = i / D, dd = i % D;
@@ -219,18 +221,18 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
             for (int e = 0; e < QD; ++e) s += kf[e] * sq[g * D + seg * QD + e];
             s += __shfl_xor(s, 1, 64);
             s += __shfl_xor(s, 2, 64);
-            if (seg == 0) ss[g * CH + key] = (k0 + key < len) ? s * scale_log2 : -INFINITY;
+            if (seg == 0) ss[g * 64 + key] = (k0 + key < len) ? s * scale_log2 : -INFINITY;
         }
     }
     __syncthreads();
     // softmax pieces per head: wave w handles heads w, w+4, ...
     float* stat = scr + ((long long)b * hl + kvh * G) * nchunks * (D + 2);
     for (int g = wave; g < G; g += 4) {
-        const float s = ss[g * CH + lane];
+        const float s = ss[g * 64 + lane];
         const float m = wave_max(s);
         const float p = exp2f(s - m);
         const float l = wave_sum(p);
-        ss[g * CH + lane] = p;
+        ss[g * 64 + lane] = p;
         if (lane == 0) {
             float* st = stat + ((long long)g * nchunks + chunk) * (D + 2);
             st[D] = m;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     {
         constexpr int DC = D / 8;               // dim chunks
         constexpr int KG = 256 / DC;            // key groups
-        constexpr int KPG = CH / KG;            // keys per group
+        constexpr int KPG = 64 / KG;            // keys per group
         const int dc = tid % DC, kg = tid / DC;
         float vf[KPG][8];
 #pragma unroll
@@ -261,12 +263,12 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
             for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
             for (int i = 0; i < KPG; ++i) {
-                const float p = ss[g * CH + kg * KPG + i];
+                const float p = ss[g * 64 + kg * KPG + i];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] += p * vf[i][e];
             }
             // sum over key groups: thread (dc, kg) -> part[kg][dc*8+e]
-            float* pg = part + G * D + G * CH;  // scratch after sq and ss
+            float* pg = part + G * D + G * 64;  // scratch after sq and ss
 #pragma unroll
             for (int e = 0; e < 8; ++e) pg[kg * D + dc * 8 + e] = o[e];
             __syncthreads();
@@ -280,22 +282,155 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     }
 }
 
-// Merge the chunks of one (batch, query head).  The chunk maxima are reduced
-// in parallel; the chunk weights exp2(m_c - M) go to LDS a tile of 1024
-// chunks at a time, and each thread (one head dim) sums the chunks' outputs
-// with independent loads.
-template <int D>
-__global__ __launch_bounds__(D) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
-                                                         int hl, int stride, const int* __restrict__ len_dev,
-                                                         int ld_seq) {
-    constexpr int NW = D / 64, TILE = 1024;
+// Query groups (G >= 2): chunks of CH positions and every pass covers all G
+// heads at once, so a work-group has three barriers whatever G is:
+//  * scores: thread (key, segment) dots its D/SEG dims of the key with every
+//    head's query (from LDS) and the SEG threads of a key sum by shuffles;
+//  * softmax: wave w takes heads w, w+4, ... (one lane per key);
+//  * P V: item (head, 8-dim chunk, key split) sums its keys from the V chunk
+//    in LDS; the KS splits of one output are adjacent lanes, summed by
+//    shuffles.
+template <int D, int CH>
+__global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict__ q, const bf16* __restrict__ K,
+                                                         const bf16* __restrict__ V, float* __restrict__ scr,
+                                                         int hl, int kvl, const int* __restrict__ len_dev,
+                                                         int ld_seq, float scale_log2) {
+    constexpr int SEG = 256 / CH, SD = D / SEG, DC = D / 8;
+    static_assert(SD % 8 == 0, "score segment");
+    const int G = hl / kvl;
+    const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int nchunks = gridDim.x;   // chunk stride of the scratch (sized for ld_seq positions)
+    const int k0 = chunk * CH;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    extern __shared__ float sm[];
+    float* sq = sm;                              // [G][D] queries
+    float* sp = sm + G * D;                      // [G][CH] scores, then probabilities
+    bf16* sv = (bf16*)(sp + G * CH);             // [CH][D] values
+
+    // The loads are issued before the cache length arrives: rows are clamped
+    // to the capacity (always addressable) and rows at or past the length are
+    // masked once it is known.
+    const int lenp = *len_dev;
+    const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
+    const bf16* Vb = V + ((long long)b * kvl + kvh) * ld_seq * D;
+    const bf16* qg = q + ((long long)b * hl + kvh * G) * D;   // the group's heads are adjacent
+    const int key = tid / SEG, seg = tid % SEG;
+    // every load first (fixed trip counts, clamped addresses), then the LDS writes
+    constexpr int VCH = CH * DC / 256;           // 16-byte V chunks per thread
+    static_assert(VCH >= 1 && CH * DC % 256 == 0, "V chunk split");
+    u16x8 kraw[SD / 8], vraw[VCH], qraw[2];
+    {
+        const int gk = min(k0 + key, ld_seq - 1);
+#pragma unroll
+        for (int c = 0; c < SD / 8; ++c) kraw[c] = *(const u16x8*)(Kb + (long long)gk * D + seg * SD + c * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+        const int i = tid + 256 * j, kk = i / DC, c = i % DC;
+        vraw[j] = *(const u16x8*)(Vb + (long long)min(k0 + kk, ld_seq - 1) * D + c * 8);
+    }
+    const int nq8 = G * D / 8;                   // two chunks per thread cover G * D <= 4096
+#pragma unroll
+    for (int j = 0; j < 2; ++j) qraw[j] = *(const u16x8*)(qg + 8 * min(tid + 256 * j, nq8 - 1));
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+        const int i = tid + 256 * j, kk = i / DC, c = i % DC;
+        *(u16x8*)(sv + kk * D + c * 8) = vraw[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = tid + 256 * j;
+        if (i < nq8)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq[8 * i + e] = bfbits2f(qraw[j][e]);
+    }
+    for (int i = tid + 512; i < nq8; i += 256) {   // larger query groups
+        const u16x8 v = *(const u16x8*)(qg + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq[8 * i + e] = bfbits2f(v[e]);
+    }
+    const int len = min(lenp + 1, ld_seq);
+    if (k0 >= len) return;           // past the cache length: no work (uniform per work-group)
+    float kf[SD];
+#pragma unroll
+    for (int c = 0; c < SD / 8; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[c * 8 + e] = bfbits2f(kraw[c][e]);
+    __syncthreads();
+    const bool kvalid = k0 + key < len;
+    for (int g = 0; g < G; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < SD; ++e) s += kf[e] * sq[g * D + seg * SD + e];
+#pragma unroll
+        for (int off = 1; off < SEG; off <<= 1) s += __shfl_xor(s, off, 64);
+        if (seg == 0) sp[g * CH + key] = kvalid ? s * scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    float* stat = scr + ((long long)b * hl + kvh * G) * nchunks * (D + 2);
+    for (int g = wave; g < G; g += 4) {
+        const float s = lane < CH ? sp[g * CH + lane] : -INFINITY;
+        const float m = wave_max(s);
+        const float p = lane < CH ? __builtin_amdgcn_exp2f(s - m) : 0.f;
+        const float l = wave_sum(p);
+        if (lane < CH) sp[g * CH + lane] = p;
+        if (lane == 0) {
+            float* st = stat + ((long long)g * nchunks + chunk) * (D + 2);
+            st[D] = m;
+            st[D + 1] = l;
+        }
+    }
+    __syncthreads();
+    int KS = 1;   // key splits: the largest power of two with G * DC * KS <= 256, at most CH
+    while (KS < CH && G * DC * KS * 2 <= 256) KS <<= 1;
+    const int kper = CH / KS, total = G * DC * KS;
+    for (int base = 0; base < total; base += 256) {
+        const int item = base + tid;
+        const bool valid = item < total;
+        const int ks = item % KS, dc = (item / KS) % DC, g = min(item / (KS * DC), G - 1);
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        if (valid) {
+            const int kend = min(kper, len - k0 - ks * kper);   // keys past the length hold no value
+            for (int i = 0; i < kend; ++i) {
+                const int kk = ks * kper + i;
+                const float p = sp[g * CH + kk];
+                const u16x8 v = *(const u16x8*)(sv + kk * D + dc * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += p * bfbits2f(v[e]);
+            }
+        }
+        for (int off = 1; off < KS; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
+        if (valid && ks == 0) {
+            float* st = stat + ((long long)g * nchunks + chunk) * (D + 2) + dc * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st[e] = o[e];
+        }
+    }
+}
+
+// Merge the chunks of one (batch, query head) with NT threads.  The chunk
+// maxima are reduced by all threads; the chunk weights exp2(m_c - M) go to
+// LDS a tile of 1024 chunks at a time; thread (dim, part) sums the weighted
+// outputs of a contiguous share (one of NT / D) of the chunks with eight
+// loads in flight, and the parts meet in LDS.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
+                                                          int hl, int stride, const int* __restrict__ len_dev,
+                                                          int ld_seq, int CH) {
+    constexpr int NW = NT / 64, P = NT / D, TILE = 1024;
     __shared__ float sw[TILE];
     __shared__ float sred[NW];
-    const int head = blockIdx.x, b = blockIdx.y, dim = threadIdx.x, lane = dim & 63, wave = dim >> 6;
-    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by attn_decode_chunk
+    __shared__ float spart[P][D];
+    const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int dim = tid % D, part = tid / D;
+    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by the chunk kernel
     const float* st = scr + ((long long)b * hl + head) * stride * (D + 2);
     float m = -INFINITY;
-    for (int c = dim; c < nchunks; c += D) m = fmaxf(m, st[c * (D + 2) + D]);
+    for (int c = tid; c < nchunks; c += NT) m = fmaxf(m, st[(long long)c * (D + 2) + D]);
     m = wave_max(m);
     if (lane == 0) sred[wave] = m;
     __syncthreads();
@@ -306,23 +441,35 @@ __global__ __launch_bounds__(D) void attn_decode_combine(const float* __restrict
     for (int c0 = 0; c0 < nchunks; c0 += TILE) {
         const int n = min(TILE, nchunks - c0);
         __syncthreads();
-        for (int c = dim; c < n; c += D) {
-            const float* sc = st + (c0 + c) * (D + 2);
+        for (int c = tid; c < n; c += NT) {
+            const float* sc = st + (long long)(c0 + c) * (D + 2);
             const float w = __builtin_amdgcn_exp2f(sc[D] - M);
             sw[c] = w;
             l += w * sc[D + 1];
         }
         __syncthreads();
-        for (int c = 0; c < n; ++c) acc += sw[c] * st[(c0 + c) * (D + 2) + dim];
+        const int lo = part * n / P, hi = (part + 1) * n / P;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int c = lo;
+        for (; c + 8 <= hi; c += 8)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[u] += sw[c + u] * st[(long long)(c0 + c + u) * (D + 2) + dim];
+        for (; c < hi; ++c) a[0] += sw[c] * st[(long long)(c0 + c) * (D + 2) + dim];
+        acc += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
+    spart[part][dim] = acc;
     l = wave_sum(l);
     __syncthreads();
     if (lane == 0) sred[wave] = l;
     __syncthreads();
-    float L = 0.f;
+    if (tid < D) {
+        float L = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) L += sred[w];
-    O[((long long)b * hl + head) * D + dim] = f2bf(acc / L);
+        for (int w = 0; w < NW; ++w) L += sred[w];
+#pragma unroll
+        for (int p = 0; p < P; ++p) o += spart[p][tid];
+        O[((long long)b * hl + head) * D + tid] = f2bf(o / L);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -538,29 +685,59 @@ void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part,
     }
 }
 
-size_t attn_decode_scratch_bytes(int B, int hl, int cap) {
-    const int nchunks = (cap + CH - 1) / CH;
-    return (size_t)B * hl * nchunks * (128 + 2) * sizeof(float);
+// Positions per chunk: 64; query groups take fewer when 64 leaves fewer
+// than 128 chunk work-groups (few KV heads and sequences), down to 16 (32
+// for d = 64).
+int decode_chunk(int B, int hl, int kvl, int cap, int d) {
+    int ch = 64;
+    if (hl == kvl) return ch;
+    const int lo = d == 128 ? 16 : 32;
+    while (ch > lo && (long long)((cap + ch - 1) / ch) * kvl * B < 128) ch >>= 1;
+    return ch;
+}
+
+size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d) {
+    const int ch = decode_chunk(B, hl, kvl, cap, d);
+    const int nchunks = (cap + ch - 1) / ch;
+    return (size_t)B * hl * nchunks * (d + 2) * sizeof(float);
+}
+
+template <int D, int CHT>
+void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
+                        int kvl, const int* len_dev, int ld_seq, hipStream_t st) {
+    const int nchunks = (ld_seq + CHT - 1) / CHT;
+    const int G = hl / kvl;
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    if (G == 1) {
+        // LDS: q [D], scores [64], per-head partial sums [256/(D/8)][D]
+        const size_t lds = ((size_t)D + 64 + (size_t)(256 / (D / 8)) * D) * sizeof(float);
+        hipLaunchKernelGGL(attn_decode_chunk_mha<D>, dim3(nchunks, kvl, B), dim3(256), lds, st, q, K, V, scratch, hl,
+                           kvl, len_dev, ld_seq, scale_log2);
+    } else {
+        // LDS: queries [G][D] and scores [G][CH] fp32, values [CH][D] bf16
+        const size_t lds = ((size_t)G * D + (size_t)G * CHT) * sizeof(float) + (size_t)CHT * D * sizeof(bf16);
+        hipLaunchKernelGGL((attn_decode_chunk<D, CHT>), dim3(nchunks, kvl, B), dim3(256), lds, st, q, K, V, scratch,
+                           hl, kvl, len_dev, ld_seq, scale_log2);
+    }
+    // long chunk lists are summed by more threads
+    if (nchunks > 32)
+        hipLaunchKernelGGL((attn_decode_combine<D, 512>), dim3(hl, B), dim3(512), 0, st, scratch, O, hl, nchunks,
+                           len_dev, ld_seq, CHT);
+    else
+        hipLaunchKernelGGL((attn_decode_combine<D, D>), dim3(hl, B), dim3(D), 0, st, scratch, O, hl, nchunks, len_dev,
+                           ld_seq, CHT);
 }
 
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
                       int kvl, const int* len_dev, int ld_seq, int d, hipStream_t st) {
-    const int nchunks = (ld_seq + CH - 1) / CH;
-    const int G = hl / kvl;
-    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
-    dim3 grid(nchunks, kvl, B);
-    // LDS: q [G][d], scores [G][CH], per-head partial sums [256/(d/8)][d]
-    const size_t lds = ((size_t)G * d + (size_t)G * CH + (size_t)(256 / (d / 8)) * d) * sizeof(float);
+    const int ch = decode_chunk(B, hl, kvl, ld_seq, d);
     if (d == 128) {
-        hipLaunchKernelGGL(attn_decode_chunk<128>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len_dev, ld_seq,
-                           scale_log2);
-        hipLaunchKernelGGL(attn_decode_combine<128>, dim3(hl, B), dim3(128), 0, st, scratch, O, hl, nchunks, len_dev,
-                           ld_seq);
+        if (ch == 64) launch_decode_attn<128, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
+        else if (ch == 32) launch_decode_attn<128, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
+        else launch_decode_attn<128, 16>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
     } else {
-        hipLaunchKernelGGL(attn_decode_chunk<64>, grid, dim3(256), lds, st, q, K, V, scratch, hl, kvl, len_dev, ld_seq,
-                           scale_log2);
-        hipLaunchKernelGGL(attn_decode_combine<64>, dim3(hl, B), dim3(64), 0, st, scratch, O, hl, nchunks, len_dev,
-                           ld_seq);
+        if (ch == 64) launch_decode_attn<64, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
+        else launch_decode_attn<64, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
     }
 }
 

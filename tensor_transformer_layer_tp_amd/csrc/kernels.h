@@ -79,7 +79,7 @@ void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W
 // stays valid while the device length grows (graph replay)
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B,
                       int hl, int kvl, const int* len_dev, int ld_seq, int d, hipStream_t st);
-size_t attn_decode_scratch_bytes(int B, int hl, int cap);
+size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d);
 // small decode batches (2..64): split-K MFMA projection + epilogue pass; part
 // is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
 void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,

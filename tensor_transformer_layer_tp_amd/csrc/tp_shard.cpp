@@ -134,7 +134,7 @@ Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) 
     L.kv = L.o + al((size_t)T * s->hl * s->d * e);
     L.act = L.kv + al((size_t)2 * T * s->kvl * s->d * e);
     L.scr = L.act + al((size_t)T * s->fl * e);
-    size_t scr = len_decode > 0 ? attn_decode_scratch_bytes(batch_decode, s->hl, len_decode) : 0;
+    size_t scr = len_decode > 0 ? attn_decode_scratch_bytes(batch_decode, s->hl, s->kvl, len_decode, s->d) : 0;
     if (batch_decode > 1) {
         // split-K scratch of the small-batch decode projections
         const int shapes[4][2] = {{s->nqkv, s->hidden}, {s->hidden, s->hl * s->d}, {s->nup, s->hidden},
