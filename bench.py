@@ -86,26 +86,33 @@ def prefill_flops(hidden, heads, kv_heads, ffn, t, B, S):
     return gemm, attn
 
 
-def weight_bytes(hidden, heads, kv_heads, ffn, t):
+def weight_bytes(hidden, heads, kv_heads, ffn, t, fp8=False):
+    """Bytes of a rank's four projection weights as decode reads them: bf16,
+    or E4M3 codes plus one fp32 scale per row."""
     d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
-    return 2 * ((hl + 2 * kvl) * d * hidden + hidden * hl * d + 2 * fl * hidden + hidden * fl)
+    shapes = [((hl + 2 * kvl) * d, hidden), (hidden, hl * d), (2 * fl, hidden), (hidden, fl)]
+    if fp8:
+        return sum(n * k + 4 * n for n, k in shapes)
+    return sum(2 * n * k for n, k in shapes)
 
 
-def decode_bytes(hidden, heads, kv_heads, ffn, t, B, L):
+def decode_bytes(hidden, heads, kv_heads, ffn, t, B, L, fp8=False):
     """Algorithmic HBM bytes of one decode step (one token for each of B
-    sequences) on one rank at cache length L: the rank's bf16 weights once,
-    K/V of positions 0..L read, one K/V position written per sequence
-    (activations are a few KB per sequence and left out)."""
+    sequences) on one rank at cache length L: the rank's weights once (bf16,
+    or E4M3 codes + row scales), K/V of positions 0..L read, one K/V position
+    written per sequence (activations are a few KB per sequence and left
+    out)."""
     d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
     kv_read = B * 2 * 2 * kvl * d * (L + 1)
+    wb = (lambda n, k: n * k + 4 * n) if fp8 else (lambda n, k: 2 * n * k)
     per_kernel = {
-        "gemv_qkv": 2 * (hl + 2 * kvl) * d * hidden,
-        "gemv_out": 2 * hidden * hl * d,
-        "gemv_up": 2 * 2 * fl * hidden,
-        "gemv_down": 2 * hidden * fl,
+        "gemv_qkv": wb((hl + 2 * kvl) * d, hidden),
+        "gemv_out": wb(hidden, hl * d),
+        "gemv_up": wb(2 * fl, hidden),
+        "gemv_down": wb(hidden, fl),
         "attn_decode": kv_read,
     }
-    return weight_bytes(hidden, heads, kv_heads, ffn, t) + kv_read + B * 2 * 2 * kvl * d, per_kernel
+    return weight_bytes(hidden, heads, kv_heads, ffn, t, fp8) + kv_read + B * 2 * 2 * kvl * d, per_kernel
 
 
 # ---------------------------------------------------------------- timing
@@ -255,14 +262,14 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
 
 # ---------------------------------------------------------------- decode
 
-def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copies, fill):
+def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copies, fill, fp8=False):
     """`copies` distinct rank-0 shards (their weights rotate through HBM)
     with caches at length L0; fill(kv) writes the first copy's cache
     content, the others copy it."""
     from tensor_transformer_layer_tp_amd import Shard
     layers = []
     for i in range(copies):
-        sh = Shard(hidden, heads, kv_heads, ffn, t, 0)
+        sh = Shard(hidden, heads, kv_heads, ffn, t, 0, decode_fp8=fp8)
         sh.load_weights(wdev)
         kv = sh.kv_cache(B, cap)
         if i == 0:
@@ -310,15 +317,15 @@ def capture(torch, fn):
     return g
 
 
-def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0, roof_key):
+def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0, roof_key, fp8=False):
     """Decode through a stack of layer copies: eager calls, then the same
     step captured once in a HIP graph and replayed (each replay appends one
     token per layer: the kernels read and advance the device-resident cache
     length), then a per-kernel breakdown pass with event markers."""
-    wb = weight_bytes(hidden, heads, kv_heads, ffn, t)
+    wb = weight_bytes(hidden, heads, kv_heads, ffn, t, fp8)
     nl = args.decode_layers or max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
     cap = L0 + 4 * (args.warmup + args.steps) + 8
-    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, 1, L0, cap, nl, fill)
+    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, 1, L0, cap, nl, fill, fp8)
     stream = torch.cuda.current_stream()
     step = decode_step_fn(torch, layers, hidden, t, 1, x0)
     ms, dist = timed(torch, step, args.steps, args.warmup, stream)
@@ -339,7 +346,7 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
         kv.close()
         sh.close()
     L_avg = L0 + 2 * (args.warmup + args.steps)   # mean cache length over the timed passes
-    nbytes, per_kernel = decode_bytes(hidden, heads, kv_heads, ffn, t, 1, int(L_avg))
+    nbytes, per_kernel = decode_bytes(hidden, heads, kv_heads, ffn, t, 1, int(L_avg), fp8)
     us, us_graph = 1e3 * ms / nl, 1e3 * gms / nl
     kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in agg.items()}
     for k, b in per_kernel.items():
@@ -350,7 +357,8 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
     d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
     best = min(us, us_graph)
     return {
-        "workload": f"{name}, {nl} distinct layer copies ({nl * wb / 1e9:.2f} GB of weights)",
+        "workload": f"{name}{', E4M3 weights (per-row scales)' if fp8 else ''}, {nl} distinct layer copies "
+                    f"({nl * wb / 1e9:.2f} GB of weights)",
         "us_per_token_layer": round(best, 3),
         "us_per_token_layer_eager": round(us, 3),
         "us_per_token_layer_graph": round(us_graph, 3),
@@ -361,8 +369,10 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
         "hbm_frac": round(nbytes / (best * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "kernels": {k: rounded(v) for k, v in kern.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic_for(roof_key, "decode.hip"),
-                     "kernel": f"gemv_kernel (gate/up + SwiGLU, fused RMSNorm), N={2 * fl} K={hidden}",
+                     "frac": round(ach / PEAK_HBM_GBPS, 4),
+                     "traffic": None if fp8 else traffic_for(roof_key, "decode.hip"),
+                     "kernel": f"gemv_kernel ({'E4M3' if fp8 else 'bf16'} gate/up + SwiGLU, fused RMSNorm), "
+                               f"N={2 * fl} K={hidden}",
                      "bytes_per_launch": per_kernel[dom]},
     }
 
@@ -398,8 +408,11 @@ def run_7b_decode(args, torch):
 
     name = ("7b-t4-decode: hidden 4096, rank 0 of t=4 (8 of 32 heads x 128, SwiGLU 2752 of 11008), bf16, batch 1, "
             f"cache {w.kv_len}+ positions")
-    return bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill,
-                        dev["x_dec"], "gemv_up_7b_t4")
+    dec = bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill,
+                       dev["x_dec"], "gemv_up_7b_t4")
+    dec8 = bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill,
+                        dev["x_dec"], "gemv8_up_7b_t4", fp8=True)
+    return dec, dec8
 
 
 def run_70b(args, torch):
@@ -428,11 +441,12 @@ def run_70b(args, torch):
             kv.write(kf, vf)
 
         x0 = synth.draw_normal_device((1, wd.hidden), 4)
-        dec = bench_decode(args, torch,
-                           "70b-t8-decode: rank 0 of t=8 (8 query heads on 1 KV head x 128, SwiGLU 3584 of 28672), "
-                           f"bf16, batch 1, cache {wd.kv_len}+ positions",
-                           wd.hidden, wd.heads, wd.kv_heads, wd.ffn, wd.tp, wdev, wd.kv_len, fill, x0,
-                           "gemv_up_70b_t8")
+        name = ("70b-t8-decode: rank 0 of t=8 (8 query heads on 1 KV head x 128, SwiGLU 3584 of 28672), "
+                f"bf16, batch 1, cache {wd.kv_len}+ positions")
+        dec = (bench_decode(args, torch, name, wd.hidden, wd.heads, wd.kv_heads, wd.ffn, wd.tp, wdev, wd.kv_len,
+                            fill, x0, "gemv_up_70b_t8"),
+               bench_decode(args, torch, name, wd.hidden, wd.heads, wd.kv_heads, wd.ffn, wd.tp, wdev, wd.kv_len,
+                            fill, x0, "gemv8_up_70b_t8", fp8=True))
     return pre, dec
 
 
@@ -705,11 +719,11 @@ def main():
               "ms_per_step_all_kernels_bracketed", "kernels", "roofline"):
         line[k] = pre[k]
     if dec is not None:
-        line["decode"] = dec
+        line["decode"], line["decode_fp8"] = dec
     if big is not None:
         line["prefill_70b"] = big[0]
         if big[1] is not None:
-            line["decode_70b"] = big[1]
+            line["decode_70b"], line["decode_70b_fp8"] = big[1]
     if not args.no_cpu:
         steps, secs, threads = cpu_baseline(state)
         line["cpu_baseline"] = {

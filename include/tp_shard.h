@@ -85,6 +85,9 @@ typedef struct {
     float eps;          /* RMSNorm epsilon                                    */
     int   rope;         /* 1: rotate-half RoPE on q and k; 0: none            */
     float rope_theta;   /* RoPE base                                          */
+    int   decode_fp8;   /* 1 (TP_BF16 only): also keep OCP E4M3 copies of the
+                           four projection weights, one fp32 scale per row,
+                           and decode one sequence (batch 1) from them      */
 } tp_opts;
 
 /* Full, unsharded layer weights (device pointers, element type = dtype):
@@ -108,7 +111,7 @@ typedef struct {
  * heads % kv_heads == 0, head_dim = hidden/heads in {64, 128},
  * hidden % 64 == 0, (ffn / degree) % 64 == 0.
  * opts == NULL selects {TP_BF16, TP_ACT_SWIGLU, rmsnorm 1, eps 1e-5, rope 1,
- * theta 10000}.  *out receives the handle (host memory owned by the library). */
+ * theta 10000, decode_fp8 0}.  decode_fp8 with TP_F32 returns TP_E_ARG.  *out receives the handle (host memory owned by the library). */
 int tp_shard_create(int hidden, int heads, int kv_heads, int ffn,
                     int tp_degree, int rank, const tp_opts *opts,
                     tp_shard **out);
@@ -118,7 +121,13 @@ int tp_shard_create(int hidden, int heads, int kv_heads, int ffn,
  * of the rank's heads; gate/up rows of the rank's FFN columns interleaved
  * in 32-row blocks; the matching column blocks of wo and w_down).  Enqueued
  * on `stream`; the caller's weights may be freed once the stream has
- * drained.  May be called again to replace the weights. */
+ * drained.  May be called again to replace the weights.
+ * With decode_fp8 it also quantises each packed matrix row by row: scale =
+ * max|w| / 448 (1 for a zero row), code = the E4M3 value nearest to the
+ * fp32 quotient w / scale (clamped to +-448), ties to the even code.  The
+ * pages leave any quantisation open (netray glossary "What Is Tensor
+ * Parallelism?", "In Practice": quantising as the alternative to
+ * sharding); this per-row scheme is the library's. */
 int tp_shard_load_weights(tp_shard *s, const tp_weights *full, void *stream);
 
 /* tp_shard_reserve -- pre-size the workspace for calls of up to
@@ -187,6 +196,14 @@ int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
 int tp_partial_reduce(const float *const *partials, int t,
                       const void *residual, void *out, long long n,
                       int out_dtype, void *stream);
+
+/* tp_shard_fp8_view -- device addresses of the E4M3 copy of a packed weight
+ * (which = 0 Q/K/V [(heads+2 kv_heads)/t * d, hidden], 1 W_o block
+ * [hidden, heads/t * d], 2 gate/up [2 ffn/t (ffn/t for GELU), hidden],
+ * 3 W_down block [hidden, ffn/t]; rows in the packed order described at
+ * tp_shard_load_weights), its per-row fp32 scales and its shape.
+ * TP_E_STATE without decode_fp8 or before tp_shard_load_weights. */
+int tp_shard_fp8_view(tp_shard *s, int which, void **codes, float **scales, int *rows, int *cols);
 
 /* tp_shard_debug_view -- device address of a workspace tensor from the last
  * forward call, for diagnostics: which = 0 attention output o

@@ -132,21 +132,21 @@ class Shard:
 
     def __init__(self, hidden: int, heads: int, kv_heads: int, ffn: int, tp: int = 1, rank: int = 0, *,
                  dtype: str = "bf16", act: str = "swiglu", rmsnorm: bool = True, eps: float = 1e-5,
-                 rope: bool = True, rope_theta: float = 10000.0):
+                 rope: bool = True, rope_theta: float = 10000.0, decode_fp8: bool = False):
         if dtype not in _DT:
             raise ValueError("dtype must be 'bf16' or 'f32'")
         if act not in ("swiglu", "gelu"):
             raise ValueError("act must be 'swiglu' or 'gelu'")
         code, tdt = _DT[dtype]
         opts = N.tp_opts(code, N.TP_ACT_SWIGLU if act == "swiglu" else N.TP_ACT_GELU, int(rmsnorm), eps,
-                         int(rope), rope_theta)
+                         int(rope), rope_theta, int(decode_fp8))
         h = C.c_void_p()
         N.check(N.lib().tp_shard_create(hidden, heads, kv_heads, ffn, tp, rank, C.byref(opts), C.byref(h)),
                 "tp_shard_create")
         self._h = h
         self.hidden, self.heads, self.kv_heads, self.ffn, self.tp, self.rank = hidden, heads, kv_heads, ffn, tp, rank
         self.dtype, self.torch_dtype, self.elem_size = dtype, tdt, (2 if dtype == "bf16" else 4)
-        self.act, self.rmsnorm, self.rope = act, rmsnorm, rope
+        self.act, self.rmsnorm, self.rope, self.decode_fp8 = act, rmsnorm, rope, decode_fp8
         self.head_dim = hidden // heads
         self.heads_local = heads // tp
         self.kv_local = kv_heads // tp
@@ -205,6 +205,19 @@ class Shard:
             self._h, stage, _dev(x, "x", self.torch_dtype), B, kv._h if kv is not None else None,
             _dev(out, "partial", torch.float32, (B, self.hidden)), _stream(stream)), "tp_shard_forward_decode")
         return out
+
+    def fp8_weights(self, which: str, stream=None):
+        """Copies of the E4M3 codes (uint8 [rows, cols], packed row order) and
+        row scales (fp32 [rows]) of 'qkv', 'o', 'up' or 'down'."""
+        code = {"qkv": 0, "o": 1, "up": 2, "down": 3}[which]
+        q, sc, r, c = C.c_void_p(), C.c_void_p(), C.c_int(), C.c_int()
+        N.check(N.lib().tp_shard_fp8_view(self._h, code, C.byref(q), C.byref(sc), C.byref(r), C.byref(c)),
+                "tp_shard_fp8_view")
+        codes = torch.empty((r.value, c.value), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((r.value,), dtype=torch.float32, device="cuda")
+        _memcpy_d2d(codes.data_ptr(), q.value, codes.numel(), stream)
+        _memcpy_d2d(scales.data_ptr(), sc.value, scales.numel() * 4, stream)
+        return codes, scales
 
     def debug_tensor(self, which: str, shape, stream=None) -> torch.Tensor:
         """Copy of a workspace tensor of the last call: 'o' [tokens, heads/t*d],

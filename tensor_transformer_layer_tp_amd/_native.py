@@ -23,7 +23,7 @@ KERNEL_KINDS = ["rmsnorm", "gemm_qkv", "attn_prefill", "gemm_out", "gemm_up", "g
 
 class tp_opts(C.Structure):
     _fields_ = [("dtype", C.c_int), ("act", C.c_int), ("rmsnorm", C.c_int), ("eps", C.c_float),
-                ("rope", C.c_int), ("rope_theta", C.c_float)]
+                ("rope", C.c_int), ("rope_theta", C.c_float), ("decode_fp8", C.c_int)]
 
 
 class tp_weights(C.Structure):
@@ -47,6 +47,8 @@ SIGNATURES = [
     ("tp_partial_reduce", C.c_int, [C.POINTER(C.c_void_p), C.c_int, C.c_void_p, C.c_void_p, C.c_longlong, C.c_int,
                                     C.c_void_p]),
     ("tp_shard_debug_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),
+    ("tp_shard_fp8_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
+                                    C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     ("tp_tune_set_gemm_config", C.c_int, [C.c_int]),
     ("tp_shard_timing", C.c_int, [C.c_void_p, C.c_int]),
     ("tp_shard_timing_read", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),

@@ -61,68 +61,88 @@ __device__ __forceinline__ void pair_store(const Epilogue& epi, int b, int r1, f
 // GEMV: y[b, n] = sum_k W[n, k] * in[b, k] for b < NB, optionally with the
 // RMSNorm of x fused in front (in = bf16(x * rsqrt(mean x^2 + eps) * gamma)).
 //
-// A work-group owns P row pairs (rows r and r + 32 of one 64-row group of the
-// packed weight; see packed_to_dim) so that the RoPE / SwiGLU partners meet in
-// one work-group.  Thread t owns the 16-byte K-chunks t + 256 i (i < NI), so
-// the 256 threads sweep each row in contiguous 4 KB bursts.  Every weight load
-// of the thread is issued first; the norm's sum of squares comes from the same
-// x chunks while those loads are in flight (the thread chunks together cover
-// all of K, so one work-group reduction gives the whole row's sum).
-template <int NB, int P, int NI, int MODE, bool NORM>
-__global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, const bf16* __restrict__ gamma,
-                                                   float eps, const bf16* __restrict__ W, int N, int K,
-                                                   Epilogue epi) {
-    constexpr int R = 2 * P;
-    __shared__ float red[4][R * NB];
+// A work-group of T threads owns P row pairs (rows r and r + 32 of one 64-row
+// group of the packed weight; see packed_to_dim) so that the RoPE / SwiGLU
+// partners meet in one work-group.  Thread t owns the 16-byte K-chunks
+// t + T i (i < NI), so the threads sweep each row in contiguous bursts; T is
+// the smallest of 64, 128, 256 that covers a row's chunks.  Every weight load
+// of the thread is issued first; the norm's sum of squares comes from the
+// same x chunks while those loads are in flight (the thread chunks together
+// cover all of K, so one work-group reduction gives the whole row's sum).
+//
+// Weights are bf16 (8 per chunk) or, with W8, OCP E4M3 codes (16 per chunk,
+// decoded exactly by the hardware conversion, two per instruction) with one
+// fp32 scale per row applied to the finished dot product.
+template <int NB, int P, int NI, int MODE, bool NORM, bool W8, int T>
+__global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, const bf16* __restrict__ gamma,
+                                                 float eps, const void* __restrict__ Wv,
+                                                 const float* __restrict__ wscale, int N, int K, Epilogue epi) {
+    constexpr int R = 2 * P, NW = T / 64;
+    constexpr int CW = W8 ? 16 : 8;      // weights per 16-byte chunk
+    constexpr int XC = CW / 8;           // 16-byte activation chunks per weight chunk
+    __shared__ float red[NW][R * NB];
     __shared__ float rs_s[NB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (blockIdx.x == 0 && tid == 0) apply_len_update(epi.len);
     const int per_group = 32 / P;
     const int grp = blockIdx.x / per_group, sub = blockIdx.x % per_group;
     const int rbase = 64 * grp + P * sub;   // rows rbase + e and rbase + 32 + e, e < P
-    const int KC = K >> 3;
+    const int KC = K / CW;
+    const char* W = (const char*)Wv;
+    const long long row_bytes = (long long)K * (W8 ? 1 : 2);
 
     int cofs[NI];
     bool valid[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int c = tid + 256 * i;
+        const int c = tid + T * i;
         valid[i] = c < KC;
-        cofs[i] = min(c, KC - 1) * 8;   // clamped: every load is issued and in bounds
+        cofs[i] = min(c, KC - 1);   // clamped: every load is issued and in bounds
     }
-    u16x8 wv[R][NI];
+    u32x4 wv[R][NI];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const bf16* wrow = W + (long long)(rbase + (r < P ? r : 32 + r - P)) * K;
+        const char* wrow = W + (long long)(rbase + (r < P ? r : 32 + r - P)) * row_bytes;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) wv[r][i] = *(const u16x8*)(wrow + cofs[i]);
+        for (int i = 0; i < NI; ++i) wv[r][i] = *(const u32x4*)(wrow + 16LL * cofs[i]);
     }
-    u16x8 xv[NB][NI];
+    u16x8 xv[NB][NI][XC];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < NI; ++i) xv[b][i] = *(const u16x8*)(x + (long long)b * K + cofs[i]);
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int h = 0; h < XC; ++h) xv[b][i][h] = *(const u16x8*)(x + (long long)b * K + cofs[i] * CW + 8 * h);
 
     float rs[NB];
-    u16x8 gv[NI];
+    u16x8 gv[NI][XC];
     if constexpr (NORM) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) gv[i] = *(const u16x8*)(gamma + cofs[i]);
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int h = 0; h < XC; ++h) gv[i][h] = *(const u16x8*)(gamma + cofs[i] * CW + 8 * h);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = bfbits2f(xv[b][i][e]);
-                    ss += valid[i] ? f * f : 0.f;
-                }
+                for (int h = 0; h < XC; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float f = bfbits2f(xv[b][i][h][e]);
+                        ss += valid[i] ? f * f : 0.f;
+                    }
             ss = wave_sum(ss);
             if (lane == 0) red[wave][b] = ss;
         }
         __syncthreads();
-        if (tid < NB) rs_s[tid] = rsqrtf((red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) / (float)K + eps);
+        if (tid < NB) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += red[w][tid];
+            rs_s[tid] = rsqrtf(t / (float)K + eps);
+        }
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < NB; ++b) rs[b] = rs_s[b];
@@ -136,23 +156,46 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         if (!valid[i]) continue;
+        float wf[R][CW];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if constexpr (W8) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[r][i][j], false);
+                    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[r][i][j], true);
+                    wf[r][4 * j] = lo[0];
+                    wf[r][4 * j + 1] = lo[1];
+                    wf[r][4 * j + 2] = hi[0];
+                    wf[r][4 * j + 3] = hi[1];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wf[r][2 * j] = __uint_as_float(wv[r][i][j] << 16);
+                    wf[r][2 * j + 1] = __uint_as_float(wv[r][i][j] & 0xFFFF0000u);
+                }
+            }
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            float xin[8];
+            float xin[CW];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float f = bfbits2f(xv[b][i][e]);
-                if constexpr (NORM) f = round_bf(f * rs[b] * bfbits2f(gv[i][e]));
-                xin[e] = f;
-            }
+            for (int h = 0; h < XC; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float f = bfbits2f(xv[b][i][h][e]);
+                    if constexpr (NORM) f = round_bf(f * rs[b] * bfbits2f(gv[i][h][e]));
+                    xin[8 * h + e] = f;
+                }
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[r][b] += bfbits2f(wv[r][i][e]) * xin[e];
+                for (int e = 0; e < CW; ++e) acc[r][b] += wf[r][e] * xin[e];
         }
     }
 
-    // reduce: wave sums, then across the 4 waves
+    // reduce: wave sums, then across the waves
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -164,10 +207,60 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16* __restrict__ x, c
     __syncthreads();
     if (tid >= P * NB) return;
     const int e = tid / NB, b = tid % NB;
-    const float y1 = red[0][e * NB + b] + red[1][e * NB + b] + red[2][e * NB + b] + red[3][e * NB + b];
     const int j2 = (P + e) * NB + b;
-    const float y2 = red[0][j2] + red[1][j2] + red[2][j2] + red[3][j2];
+    float y1 = 0.f, y2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        y1 += red[w][e * NB + b];
+        y2 += red[w][j2];
+    }
+    if constexpr (W8) {
+        y1 *= wscale[rbase + e];
+        y2 *= wscale[rbase + 32 + e];
+    }
     pair_store<MODE>(epi, b, rbase + e, y1, y2);
+}
+
+// Per-row E4M3 quantisation of a bf16 matrix [N, K]: one work-group per
+// row; scale = max|w| / 448 (1 for a zero row); code = nearest E4M3 value of
+// the fp32 quotient w / scale clamped to +-448, ties to the even code.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fminf(fabsf(v), 448.f);
+    uint32_t code;
+    if (a < 0.015625f) {                       // below 2^-6: subnormal spacing 2^-9
+        code = (uint32_t)__builtin_rintf(a * 512.f);   // 0..8; 8 is the smallest normal
+    } else {
+        const uint32_t ab = __float_as_uint(a);
+        uint32_t e = (ab >> 23) - 120;         // biased E4M3 exponent 1..15
+        uint32_t m = (ab >> 20) & 7u;
+        const uint32_t rem = ab & 0xFFFFFu;
+        if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
+            if (++m == 8u) {
+                m = 0;
+                ++e;
+            }
+        }
+        code = (e << 3) | m;
+    }
+    return code | sign;
+}
+
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16* __restrict__ W, int K, uint8_t* __restrict__ Q,
+                                                         float* __restrict__ scale) {
+    __shared__ float red[4];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bf16* w = W + (long long)row * K;
+    float amax = 0.f;
+    for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf(bf2f(w[k])));
+    amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax > 0.f ? amax / 448.f : 1.f;
+    if (tid == 0) scale[row] = s;
+    uint8_t* q = Q + (long long)row * K;
+    for (int k = tid; k < K; k += 256) q[k] = (uint8_t)e4m3_code(bf2f(w[k]) / s);
 }
 
 // ---------------------------------------------------------------------------
@@ -585,45 +678,47 @@ int skinny_splits(int N, int K) {
     return std::max(1, std::min(want, kgroups / 4));
 }
 
-template <int NB, int P, int NI, bool NORM>
-void gemv_mode(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
-               hipStream_t st) {
-    dim3 g(N / (2 * P)), b(256);
+template <int NB, int P, int NI, bool NORM, bool W8, int T>
+void gemv_mode(const bf16* x, const bf16* gamma, float eps, const void* W, const float* ws, int N, int K,
+               const Epilogue& epi, hipStream_t st) {
+    dim3 g(N / (2 * P)), b(T);
     switch (epi.mode) {
-        case EPI_F32: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_F32, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_QKV, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_SWIGLU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        case EPI_GELU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_GELU, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
-        default: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_STORE, NORM>), g, b, 0, st, x, gamma, eps, W, N, K, epi); break;
+        case EPI_F32: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_F32, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
+        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_QKV, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_SWIGLU, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
+        case EPI_GELU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_GELU, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
+        default: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_STORE, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
     }
 }
 
-template <int NB, int NI>
-void gemv_ni(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
-             hipStream_t st) {
+template <int NB, int NI, bool W8, int T>
+void gemv_ni(const bf16* x, const bf16* gamma, float eps, const void* W, const float* ws, int N, int K,
+             const Epilogue& epi, hipStream_t st) {
     // 8 rows per work-group keep 8 x NI loads in flight per thread; 4 rows when
     // 8 would leave the GPU short of work-groups or the thread short of registers
     if constexpr (NI <= 2) {
         if (N / 8 >= 512) {
-            if (gamma) gemv_mode<NB, 4, NI, true>(x, gamma, eps, W, N, K, epi, st);
-            else gemv_mode<NB, 4, NI, false>(x, gamma, eps, W, N, K, epi, st);
+            if (gamma) gemv_mode<NB, 4, NI, true, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
+            else gemv_mode<NB, 4, NI, false, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
             return;
         }
     }
-    if (gamma) gemv_mode<NB, 2, NI, true>(x, gamma, eps, W, N, K, epi, st);
-    else gemv_mode<NB, 2, NI, false>(x, gamma, eps, W, N, K, epi, st);
+    if (gamma) gemv_mode<NB, 2, NI, true, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
+    else gemv_mode<NB, 2, NI, false, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
 }
 
-template <int NB>
-void gemv_nb(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, int K, const Epilogue& epi,
-             hipStream_t st) {
-    const int ni = ((K >> 3) + 255) / 256;   // 16-byte chunks per thread (K <= 16384)
-    switch (ni) {
-        case 1: gemv_ni<NB, 1>(x, gamma, eps, W, N, K, epi, st); break;
-        case 2: gemv_ni<NB, 2>(x, gamma, eps, W, N, K, epi, st); break;
-        case 3: gemv_ni<NB, 3>(x, gamma, eps, W, N, K, epi, st); break;
-        case 4: gemv_ni<NB, 4>(x, gamma, eps, W, N, K, epi, st); break;
-        default: gemv_ni<NB, 8>(x, gamma, eps, W, N, K, epi, st); break;
+template <int NB, bool W8>
+void gemv_nb(const bf16* x, const bf16* gamma, float eps, const void* W, const float* ws, int N, int K,
+             const Epilogue& epi, hipStream_t st) {
+    const int kc = K / (W8 ? 16 : 8);   // 16-byte chunks per row (K <= 16384)
+    if (kc <= 64) return gemv_ni<NB, 1, W8, 64>(x, gamma, eps, W, ws, N, K, epi, st);
+    if (kc <= 128) return gemv_ni<NB, 1, W8, 128>(x, gamma, eps, W, ws, N, K, epi, st);
+    switch ((kc + 255) / 256) {
+        case 1: gemv_ni<NB, 1, W8, 256>(x, gamma, eps, W, ws, N, K, epi, st); break;
+        case 2: gemv_ni<NB, 2, W8, 256>(x, gamma, eps, W, ws, N, K, epi, st); break;
+        case 3: gemv_ni<NB, 3, W8, 256>(x, gamma, eps, W, ws, N, K, epi, st); break;
+        case 4: gemv_ni<NB, 4, W8, 256>(x, gamma, eps, W, ws, N, K, epi, st); break;
+        default: gemv_ni<NB, 8, W8, 256>(x, gamma, eps, W, ws, N, K, epi, st); break;
     }
 }
 
@@ -632,35 +727,20 @@ void gemv_nb(const bf16* x, const bf16* gamma, float eps, const bf16* W, int N, 
 void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W, int N, int K,
                const Epilogue& epi, hipStream_t st) {
     switch (B) {
-        case 1: gemv_nb<1>(x, gamma, eps, W, N, K, epi, st); break;
-        case 2: gemv_nb<2>(x, gamma, eps, W, N, K, epi, st); break;
-        case 3: gemv_nb<3>(x, gamma, eps, W, N, K, epi, st); break;
-        case 4: gemv_nb<4>(x, gamma, eps, W, N, K, epi, st); break;
-        default: {
-            // batches above 4 run in slices of 4 rows (the caller keeps B <= 8)
-            for (int b0 = 0; b0 < B; b0 += 4) {
-                const int nb = B - b0 < 4 ? B - b0 : 4;
-                Epilogue e = epi;
-                if (epi.mode == EPI_QKV) {
-                    // slices of the batch: shift the q and cache bases by b0 sequences
-                    e.qkv.q = (bf16*)epi.qkv.q + (long long)b0 * epi.qkv.hl * epi.qkv.d;
-                    e.qkv.k = (bf16*)epi.qkv.k + (long long)b0 * epi.qkv.kvl * epi.qkv.ld_seq * epi.qkv.d;
-                    e.qkv.v = (bf16*)epi.qkv.v + (long long)b0 * epi.qkv.kvl * epi.qkv.ld_seq * epi.qkv.d;
-                } else if (epi.mode == EPI_F32) {
-                    e.out = (float*)epi.out + (long long)b0 * epi.ldo;
-                } else {
-                    e.out = (bf16*)epi.out + (long long)b0 * epi.ldo;
-                }
-                const bf16* xb = x + (long long)b0 * K;
-                switch (nb) {
-                    case 1: gemv_nb<1>(xb, gamma, eps, W, N, K, e, st); break;
-                    case 2: gemv_nb<2>(xb, gamma, eps, W, N, K, e, st); break;
-                    case 3: gemv_nb<3>(xb, gamma, eps, W, N, K, e, st); break;
-                    default: gemv_nb<4>(xb, gamma, eps, W, N, K, e, st); break;
-                }
-            }
-        }
+        case 1: gemv_nb<1, false>(x, gamma, eps, W, nullptr, N, K, epi, st); break;
+        case 2: gemv_nb<2, false>(x, gamma, eps, W, nullptr, N, K, epi, st); break;
+        case 3: gemv_nb<3, false>(x, gamma, eps, W, nullptr, N, K, epi, st); break;
+        default: gemv_nb<4, false>(x, gamma, eps, W, nullptr, N, K, epi, st); break;
     }
+}
+
+void gemv_fp8(const bf16* x, const bf16* gamma, float eps, const uint8_t* W, const float* scale, int N, int K,
+              const Epilogue& epi, hipStream_t st) {
+    gemv_nb<1, true>(x, gamma, eps, W, scale, N, K, epi, st);
+}
+
+void quant_rows_e4m3(const bf16* W, int N, int K, uint8_t* Q, float* scale, hipStream_t st) {
+    hipLaunchKernelGGL(quant_rows_kernel, dim3(N), dim3(256), 0, st, W, K, Q, scale);
 }
 
 size_t skinny_scratch_bytes(int B, int N, int K) {

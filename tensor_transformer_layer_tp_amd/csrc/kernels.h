@@ -72,8 +72,14 @@ void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st);
 void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl,
                        int S, int ld_seq, int d, hipStream_t st);
+// decode GEMV for B <= 4 sequences (K <= 16384, N a multiple of 64)
 void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W, int N, int K,
                const Epilogue& epi, hipStream_t st);
+// one sequence, E4M3 weights [N, K] with one fp32 scale per row
+void gemv_fp8(const bf16* x, const bf16* gamma, float eps, const uint8_t* W, const float* scale, int N, int K,
+              const Epilogue& epi, hipStream_t st);
+// per-row E4M3 quantisation: Q [N, K] codes, scale [N]
+void quant_rows_e4m3(const bf16* W, int N, int K, uint8_t* Q, float* scale, hipStream_t st);
 // decode attention over positions [0, *len_dev + 1) (capped at ld_seq); the
 // grid and the scratch are sized for ld_seq positions so that one launch
 // stays valid while the device length grows (graph replay)

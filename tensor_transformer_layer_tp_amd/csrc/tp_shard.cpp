@@ -31,6 +31,9 @@ struct tp_shard {
     int device;
     bool loaded;
     void *w_qkv, *w_o, *w_up, *w_down, *g1, *g2;
+    // E4M3 copies of the four packed projections (decode_fp8) and their row scales
+    uint8_t* q8[4];
+    float* s8[4];
     char* ws;
     size_t ws_bytes;
     float *rcos, *rsin;
@@ -145,6 +148,14 @@ Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) 
     return L;
 }
 
+// rows x cols of packed projection i (0 Q/K/V, 1 W_o block, 2 gate/up, 3 W_down block)
+void fp8_shape(const tp_shard* s, int i, int* rows, int* cols) {
+    const int R[4] = {s->nqkv, s->hidden, s->nup, s->hidden};
+    const int C[4] = {s->hidden, s->hl * s->d, s->hidden, s->fl};
+    *rows = R[i];
+    *cols = C[i];
+}
+
 int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void* q, void* k, void* v,
                int ld_seq, hipStream_t st, const int* pos_dev = nullptr) {
     Epilogue epi{};
@@ -202,7 +213,12 @@ constexpr int kSkinnyMaxBatch = 64;
 constexpr int kGemvMaxK = 16384;
 
 int launch_gemv(tp_shard* s, const void* x, int B, const void* gamma, const void* W, int N, int K,
-                const Epilogue& epi, void* nbuf, void* scratch, hipStream_t st) {
+                const Epilogue& epi, void* nbuf, void* scratch, hipStream_t st, int fp8_index) {
+    if (B == 1 && s->o.decode_fp8) {
+        gemv_fp8((const bf16*)x, (const bf16*)gamma, s->o.eps, s->q8[fp8_index], s->s8[fp8_index], N, K, epi, st);
+        LAUNCH_CHECK("fp8 gemv");
+        return TP_OK;
+    }
     if (B <= kGemvMaxBatch) {
         gemv_bf16((const bf16*)x, B, (const bf16*)gamma, s->o.eps, (const bf16*)W, N, K, epi, st);
         LAUNCH_CHECK("gemv");
@@ -269,8 +285,10 @@ int tp_shard_create(int hidden, int heads, int kv_heads, int ffn, int tp_degree,
     if (!out) return TP_E_ARG;
     *out = nullptr;
     if (hidden <= 0 || heads <= 0 || kv_heads <= 0 || ffn <= 0 || tp_degree <= 0) return TP_E_ARG;
-    tp_opts o = {TP_BF16, TP_ACT_SWIGLU, 1, 1e-5f, 1, 10000.0f};
+    tp_opts o = {TP_BF16, TP_ACT_SWIGLU, 1, 1e-5f, 1, 10000.0f, 0};
     if (opts) o = *opts;
+    if (o.decode_fp8 != 0 && o.decode_fp8 != 1) return TP_E_ARG;
+    if (o.decode_fp8 && o.dtype != TP_BF16) return TP_E_ARG;
     if (o.dtype != TP_BF16 && o.dtype != TP_F32) return TP_E_ARG;
     if (o.act != TP_ACT_SWIGLU && o.act != TP_ACT_GELU) return TP_E_ARG;
     if (o.rmsnorm && !(o.eps >= 0.f)) return TP_E_ARG;
@@ -361,7 +379,33 @@ int tp_shard_load_weights(tp_shard* s, const tp_weights* W, void* stream) {
         HIP_TRY(hipMemcpyAsync(s->g1, W->g1, (size_t)h * e, hipMemcpyDeviceToDevice, st));
         HIP_TRY(hipMemcpyAsync(s->g2, W->g2, (size_t)h * e, hipMemcpyDeviceToDevice, st));
     }
+    if (s->o.decode_fp8) {
+        const void* src[4] = {s->w_qkv, s->w_o, s->w_up, s->w_down};
+        for (int i = 0; i < 4; ++i) {
+            int rows, cols;
+            fp8_shape(s, i, &rows, &cols);
+            if (!s->q8[i]) {
+                if (hipMalloc((void**)&s->q8[i], (size_t)rows * cols) != hipSuccess ||
+                    hipMalloc((void**)&s->s8[i], (size_t)rows * sizeof(float)) != hipSuccess)
+                    return TP_E_NOMEM;
+            }
+            quant_rows_e4m3((const bf16*)src[i], rows, cols, s->q8[i], s->s8[i], st);
+            LAUNCH_CHECK("fp8 quantisation");
+        }
+    }
     s->loaded = true;
+    return TP_OK;
+}
+
+int tp_shard_fp8_view(tp_shard* s, int which, void** codes, float** scales, int* rows, int* cols) {
+    if (!s || which < 0 || which > 3) return TP_E_ARG;
+    if (!s->o.decode_fp8 || !s->loaded || !s->q8[which]) return TP_E_STATE;
+    int r, c;
+    fp8_shape(s, which, &r, &c);
+    if (codes) *codes = s->q8[which];
+    if (scales) *scales = s->s8[which];
+    if (rows) *rows = r;
+    if (cols) *cols = c;
     return TP_OK;
 }
 
@@ -516,8 +560,8 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
     if (!s->loaded) return TP_E_STATE;
     hipStream_t st = (hipStream_t)stream;
     const bool bf = s->o.dtype == TP_BF16;
-    const bool use_gemv = bf && (batch <= kGemvMaxBatch ? s->hidden <= kGemvMaxK && s->hl * s->d <= kGemvMaxK &&
-                                                               s->fl <= kGemvMaxK
+    const int kmax = batch == 1 && s->o.decode_fp8 ? 2 * kGemvMaxK : kGemvMaxK;   // E4M3 rows are half as long
+    const bool use_gemv = bf && (batch <= kGemvMaxBatch ? s->hidden <= kmax && s->hl * s->d <= kmax && s->fl <= kmax
                                                          : batch <= kSkinnyMaxBatch);
     if (stage == TP_STAGE_ATTN) {
         if (!kv) return TP_E_ARG;
@@ -550,7 +594,7 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
                               s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
             KTimer kt(s, TP_K_GEMV_QKV, st);
             TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi,
-                            ws + lay.n, ws + lay.scr, st));
+                            ws + lay.n, ws + lay.scr, st, 0));
         } else {
             const void* xin = x;
             if (s->o.rmsnorm) {
@@ -579,7 +623,7 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.len = LenUpdate{kv->dlen, -1, kv->max_seq};
             KTimer kt(s, TP_K_GEMV_OUT, st);
             TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, ws + lay.n,
-                            ws + lay.scr, st));
+                            ws + lay.scr, st, 1));
         } else {
             KTimer kt(s, TP_K_GEMM_OUT, st);
             TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
@@ -596,7 +640,7 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             {
                 KTimer kt(s, TP_K_GEMV_UP, st);
                 TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi,
-                                ws + lay.n, ws + lay.scr, st));
+                                ws + lay.n, ws + lay.scr, st, 2));
             }
             Epilogue e2{};
             e2.mode = EPI_F32;
@@ -604,7 +648,7 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             e2.ldo = s->hidden;
             KTimer kt(s, TP_K_GEMV_DOWN, st);
             TRY(launch_gemv(s, ws + lay.act, batch, nullptr, s->w_down, s->hidden, s->fl, e2, ws + lay.n,
-                            ws + lay.scr, st));
+                            ws + lay.scr, st, 3));
         } else {
             const void* xin = x;
             if (s->o.rmsnorm) {
@@ -696,7 +740,8 @@ void tp_shard_destroy(tp_shard* s) {
     if (!s) return;
     for (hipEvent_t e : s->ev)
         if (e) (void)hipEventDestroy(e);
-    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin};
+    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin,
+                    s->q8[0], s->q8[1], s->q8[2], s->q8[3], s->s8[0], s->s8[1], s->s8[2], s->s8[3]};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     delete s;

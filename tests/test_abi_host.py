@@ -140,3 +140,19 @@ def test_tune_hook_range():
     lib = N.lib()
     assert lib.tp_tune_set_gemm_config(99) == N.TP_E_ARG
     assert lib.tp_tune_set_gemm_config(-1) == N.TP_OK
+
+
+def test_fp8_option_rules():
+    """decode_fp8 needs the bf16 shard; the fp8 view needs loaded weights."""
+    lib = N.lib()
+    h = C.c_void_p()
+    bad = N.tp_opts(N.TP_F32, N.TP_ACT_SWIGLU, 1, 1e-5, 1, 10000.0, 1)
+    assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, C.byref(bad), C.byref(h)) == N.TP_E_ARG
+    bad2 = N.tp_opts(N.TP_BF16, N.TP_ACT_SWIGLU, 1, 1e-5, 1, 10000.0, 2)
+    assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, C.byref(bad2), C.byref(h)) == N.TP_E_ARG
+    ok = N.tp_opts(N.TP_BF16, N.TP_ACT_SWIGLU, 1, 1e-5, 1, 10000.0, 1)
+    assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, C.byref(ok), C.byref(h)) == N.TP_OK
+    q, sc, r, c = C.c_void_p(), C.c_void_p(), C.c_int(), C.c_int()
+    assert lib.tp_shard_fp8_view(h, 0, C.byref(q), C.byref(sc), C.byref(r), C.byref(c)) == N.TP_E_STATE
+    assert lib.tp_shard_fp8_view(h, 4, C.byref(q), C.byref(sc), C.byref(r), C.byref(c)) == N.TP_E_ARG
+    lib.tp_shard_destroy(h)

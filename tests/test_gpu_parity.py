@@ -305,6 +305,99 @@ def test_decode_graph_replay(B):
     del g
 
 
+def packed_qkv_rows(spec, tp, r):
+    """Original row index (into the concatenation [W_q; W_k; W_v]) of every
+    packed Q/K/V row of rank r: the rank's q heads, then its k heads, then
+    its v heads; inside a head, packed row p holds dim 32 g + w (w < 32) or
+    d/2 + 32 g + w - 32 (w >= 32), g = p // 64, w = p % 64."""
+    hb, kb, _ = O.rank_blocks(spec, tp, r)
+    d = spec.head_dim
+    dims = [32 * (p // 64) + (p % 64) if p % 64 < 32 else d // 2 + 32 * (p // 64) + (p % 64) - 32
+            for p in range(d)]
+    rows = []
+    for base, block in ((0, hb), (spec.heads * d, kb), (spec.heads * d + spec.kv_heads * d, kb)):
+        for hd in block:
+            rows += [base + hd * d + dm for dm in dims]
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("hidden,heads,kv,ffn,tp,r", [(1024, 8, 4, 2816, 2, 1), (512, 8, 8, 1536, 1, 0)])
+def test_fp8_codes_bit_exact(hidden, heads, kv, ffn, tp, r):
+    """The E4M3 codes and row scales the library computes at load time equal
+    the oracle's, byte for byte, for all four packed projections."""
+    from oracle import fp8
+    announce(f"fp8 weight codes, hidden={hidden} heads={heads}/{kv} ffn={ffn} t={tp} r={r}")
+    L = Layer(hidden, heads, kv, ffn, seed=51)
+    from tensor_transformer_layer_tp_amd import Shard
+    sh = Shard(hidden, heads, kv, ffn, tp, r, decode_fp8=True)
+    sh.load_weights({k: v for k, v in L.dev.items()})
+    spec, W = L.spec, L.exact
+    _, _, fb = O.rank_blocks(spec, tp, r)
+    hb, _, _ = O.rank_blocks(spec, tp, r)
+    d, fl = spec.head_dim, ffn // tp
+    qkv_all = np.concatenate([W["wq"], W["wk"], W["wv"]])
+    up_rows = []
+    for j in range(fl // 32):
+        up_rows.append(W["w_gate"][fb.start + 32 * j: fb.start + 32 * j + 32])
+        up_rows.append(W["w_up"][fb.start + 32 * j: fb.start + 32 * j + 32])
+    expect = {
+        "qkv": qkv_all[packed_qkv_rows(spec, tp, r)],
+        "o": W["wo"][:, hb.start * d: hb.stop * d],
+        "up": np.concatenate(up_rows),
+        "down": W["w_down"][:, fb.start: fb.stop],
+    }
+    for name, w in expect.items():
+        codes, scales = sh.fp8_weights(name)
+        torch.cuda.synchronize()
+        ref_codes, ref_scales = fp8.quantize_rows(w)
+        assert np.array_equal(scales.cpu().numpy(), ref_scales), f"{name}: row scales differ"
+        got = codes.cpu().numpy()
+        bad = np.count_nonzero(got != ref_codes)
+        assert bad == 0, f"{name}: {bad} of {got.size} codes differ"
+
+
+@pytest.mark.parametrize("hidden,heads,kv,ffn,tp,r", [
+    (1024, 8, 4, 2816, 2, 1),     # fp8 chunks per row: 64 (hidden), 32 (o), 88 (down)
+    (4096, 32, 8, 5632, 4, 3),    # 256 chunks per row; GQA 8 heads on 2 KV heads
+    (512, 8, 8, 1536, 1, 0),      # head_dim 64
+])
+def test_fp8_decode_matches_oracle(hidden, heads, kv, ffn, tp, r):
+    """Batch-1 decode on the fp8 shard against the oracle with the rank's
+    weights replaced by their E4M3 values; batch 3 on the same shard takes
+    the bf16 weights and matches the unquantised oracle."""
+    from oracle import fp8
+    from tensor_transformer_layer_tp_amd import Shard
+    announce(f"fp8 decode hidden={hidden} heads={heads}/{kv} ffn={ffn} t={tp} r={r}")
+    S = 40
+    L = Layer(hidden, heads, kv, ffn, batch=3, seq=S + 1, gamma_noise=True, seed=52)
+    sh = Shard(hidden, heads, kv, ffn, tp, r, decode_fp8=True)
+    sh.load_weights({k: v for k, v in L.dev.items() if k != "x"})
+    spec, x = L.spec, L.exact["x"]
+    Wq = fp8.rank_weights(L.W, spec, tp, r)
+    kvc = sh.kv_cache(1, S + 1)
+    sh.prefill(ATTN, L.dev["x"][:1, :S].contiguous(), kvc)
+    p = sh.decode(ATTN, L.dev["x"][:1, S].contiguous(), kvc, out=nan_like((1, hidden)))
+    h = synth.to_storage(synth.draw_normal((1, hidden), 53), "bf16")
+    pm = sh.decode(MLP, h.cuda(), out=nan_like((1, hidden)))
+    torch.cuda.synchronize()
+    pre = O.attn_stage(x[:1, :S], L.W, spec, tp, r)            # the cache came from bf16 prefill
+    ref = O.decode_attn_stage(x[:1, S], pre["k"], pre["v"], Wq, spec, tp, r)
+    assert_close(to_np(p), ref["partial"], "fp8 decode attn partial", "bf16")
+    refm = O.mlp_stage(h.float().numpy()[:, None], Wq, spec, tp, r)
+    assert_close(to_np(pm), refm["partial"][:, 0], "fp8 decode mlp partial", "bf16")
+    # the quantisation is visible: the unquantised oracle differs by more than rounding
+    ref_bf = O.mlp_stage(h.float().numpy()[:, None], L.W, spec, tp, r)
+    assert np.abs(ref_bf["partial"][:, 0] - refm["partial"][:, 0]).max() > 1e-3
+    # batch 3 on the same shard: bf16 weights
+    kv3 = sh.kv_cache(3, S + 1)
+    sh.prefill(ATTN, L.dev["x"][:, :S].contiguous(), kv3)
+    p3 = sh.decode(ATTN, L.dev["x"][:, S].contiguous(), kv3, out=nan_like((3, hidden)))
+    torch.cuda.synchronize()
+    pre3 = O.attn_stage(x[:, :S], L.W, spec, tp, r)
+    ref3 = O.decode_attn_stage(x[:, S], pre3["k"], pre3["v"], L.W, spec, tp, r)
+    assert_close(to_np(p3), ref3["partial"], "batch-3 decode on the fp8 shard", "bf16")
+
+
 def test_decode_equals_prefill_row():
     """Same math both ways: decode of token L after a prefill of L tokens
     equals row L of a prefill over L+1 tokens (GPU against GPU, then both
