@@ -12,8 +12,10 @@ Independent implementations live here:
   separately, used only to pin ``oracle.layer``.
 * ``oracle.fp8``    -- E4M3 encoding from the format definition and the
   per-row weight quantisation of the fp8 decode shard.
+* ``oracle.sp``     -- the sequence-parallel variant: reduce-scatter over
+  token rows, per-rank norms, all-gather of the normalised rows.
 
 None of them shares any code with the GPU path.
 """
 
-from . import layer, brute, fp8  # noqa: F401
+from . import layer, brute, fp8, sp  # noqa: F401

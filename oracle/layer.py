@@ -245,9 +245,16 @@ def attn_stage(x, W, spec: Spec, t: int = 1, r: int = 0):
     """Prefill ATTN stage of rank r over x [B, S, hidden]: norm, own-head
     Q/K/V, causal attention over positions 0..S-1, row-parallel partial."""
     x = np.asarray(x, np.float64)
-    S = x.shape[1]
+    return attn_from_n1(norm1(x, W, spec), W, spec, t, r)
+
+
+def attn_from_n1(n1, W, spec: Spec, t: int = 1, r: int = 0):
+    """The ATTN stage after its norm: n1 [B, S, hidden] is the normalised
+    stage input (computed by this rank, or gathered from the ranks'
+    sequence shards)."""
+    n1 = np.asarray(n1, np.float64)
+    S = n1.shape[1]
     pos = np.arange(S)
-    n1 = norm1(x, W, spec)
     q, k, v = qkv_rank(n1, W, spec, t, r, pos)
     o = _store(spec, attention(q, k, v, pos, pos))
     partial = out_proj_rank(o, W, spec, t, r)
@@ -259,9 +266,15 @@ def mlp_stage(h, W, spec: Spec, t: int = 1, r: int = 0):
     column-parallel up (and gate) projection of the rank's FFN columns with
     the activation, then the row-parallel down projection's partial."""
     h = np.asarray(h, np.float64)
+    return mlp_from_n2(norm2(h, W, spec), W, spec, t, r)
+
+
+def mlp_from_n2(n2, W, spec: Spec, t: int = 1, r: int = 0):
+    """The FFN stage after its norm: n2 [B, S, hidden] is the normalised
+    stage input."""
+    n2 = np.asarray(n2, np.float64)
     _, _, fb = rank_blocks(spec, t, r)
     cols = slice(fb.start, fb.stop)
-    n2 = norm2(h, W, spec)
     if spec.swiglu:
         g = n2 @ np.asarray(W["w_gate"], np.float64)[cols].T
         u = n2 @ np.asarray(W["w_up"], np.float64)[cols].T
