@@ -260,6 +260,50 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
     }
 
 
+def bench_sp(args, torch, hidden, heads, kv_heads, ffn, t, wdev, x):
+    """The sequence-parallel step of rank 0: norm of its T/t token rows,
+    all-gather of the ranks' normalised rows, ATTN stage without its norm,
+    reduce-scatter, the same for the MLP stage.  The other ranks'
+    contributions are seeded stand-ins (timing only)."""
+    from tensor_transformer_layer_tp_amd import (ATTN, MLP, PRENORM, Shard, all_gather,
+                                                 partial_reduce_scatter)
+    B, S = int(x.shape[0]), int(x.shape[1])
+    T, n = B * S, B * S // t
+    sh = Shard(hidden, heads, kv_heads, ffn, t, 0)
+    sh.load_weights(wdev)
+    sh.reserve(T)
+    kv = sh.kv_cache(B, S)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(97)
+    x0 = x.reshape(T, hidden)[:n].contiguous()
+    others_n = [torch.randn((n, hidden), device="cuda", generator=g).to(torch.bfloat16) for _ in range(t - 1)]
+    pa = [torch.randn((B, S, hidden), device="cuda", generator=g) * 0.1 for _ in range(t)]
+    pm = [torch.randn((B, S, hidden), device="cuda", generator=g) * 0.1 for _ in range(t)]
+    n1r, n2r = torch.empty_like(x0), torch.empty_like(x0)
+    n1 = torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda")
+    n2 = torch.empty_like(n1)
+    hr, yr = torch.empty_like(x0), torch.empty_like(x0)
+
+    def step():
+        sh.norm(1, x0, out=n1r)
+        all_gather([n1r, *others_n], out=n1)
+        sh.prefill(ATTN | PRENORM, n1.reshape(B, S, hidden), kv, out=pa[0])
+        partial_reduce_scatter(pa, 0, x0, out=hr)
+        sh.norm(2, hr, out=n2r)
+        all_gather([n2r, *others_n], out=n2)
+        sh.prefill(MLP | PRENORM, n2.reshape(B, S, hidden), out=pm[0])
+        partial_reduce_scatter(pm, 0, hr, out=yr)
+
+    ms, dist = timed(torch, step, args.steps, args.warmup, torch.cuda.current_stream())
+    kv.close()
+    sh.close()
+    gemm, attn = prefill_flops(hidden, heads, kv_heads, ffn, t, B, S)
+    return {"workload": "sequence-parallel step of the same 7B t=2 rank-0 shard: norms on its 1024 token rows, "
+                        "all-gather, stages without their norms, reduce-scatter",
+            "ms_per_step": round(ms, 4), "step_ms": dist,
+            "tflops": round((sum(gemm.values()) + attn) / (ms * 1e-3) / 1e12, 2)}
+
+
 # ---------------------------------------------------------------- decode
 
 def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copies, fill, fp8=False):
@@ -387,6 +431,7 @@ def run_7b(args, torch):
     wdev = {k: v for k, v in dev.items() if k != "x"}
     pre = bench_prefill(args, torch, "7b-t2-prefill", w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, dev["x"],
                         True, "gemm_up_7b_t2")
+    pre["sequence_parallel"] = bench_sp(args, torch, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, dev["x"])
     del dev, wdev
     return pre, (w, raw)
 
@@ -716,7 +761,7 @@ def main():
         },
     }
     for k in ("step_ms", "mfma_frac", "flops_per_step", "gemm_tflops", "gemm_mfma_frac",
-              "ms_per_step_all_kernels_bracketed", "kernels", "roofline"):
+              "ms_per_step_all_kernels_bracketed", "kernels", "roofline", "sequence_parallel"):
         line[k] = pre[k]
     if dec is not None:
         line["decode"], line["decode_fp8"] = dec

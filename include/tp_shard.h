@@ -70,6 +70,10 @@ extern "C" {
 /* stages of a shard's forward pass */
 #define TP_STAGE_ATTN  0
 #define TP_STAGE_MLP   1
+/* OR'ed into a stage: x is the already normalised stage input (the
+ * sequence-parallel flow gathers the ranks' normalised rows, see
+ * tp_shard_norm / tp_all_gather), so the stage skips its RMSNorm */
+#define TP_STAGE_PRENORM 0x10
 
 /* FFN activation */
 #define TP_ACT_SWIGLU  0   /* act = SiLU(n W_gate^T) * (n W_up^T); three FFN matrices */
@@ -204,6 +208,29 @@ int tp_partial_reduce(const float *const *partials, int t,
  * tp_shard_load_weights), its per-row fp32 scales and its shape.
  * TP_E_STATE without decode_fp8 or before tp_shard_load_weights. */
 int tp_shard_fp8_view(tp_shard *s, int which, void **codes, float **scales, int *rows, int *cols);
+
+/* Sequence-parallel variant (undercodenews post 110319, "What Undercode
+ * Say": tensor parallelism is paired with sequence parallelism).  Between
+ * the stages the activations are split by token: rank r holds rows
+ * [r T/t, (r+1) T/t) of the flattened [T = batch*seq, hidden] tensor.
+ *
+ * tp_partial_reduce_scatter -- rank `rank`'s rows of the reduce:
+ *   out_rows[i] = (sum_{r<t} partials[r][rank * n + i]) + residual_rows[i],
+ *   n = rows / t * cols, summed in fp32 in rank order, stored as out_dtype.
+ *   partials: HOST array of t device pointers to [rows, cols] fp32;
+ *   residual_rows (may be NULL) and out_rows: [rows / t, cols] of out_dtype.
+ *   rows % t != 0 returns TP_E_DIVIDE; cols must be a multiple of 8.
+ * tp_all_gather -- out [t * rows_per_rank, cols] = the t pieces (HOST array
+ *   of device pointers, each [rows_per_rank, cols] of dtype) in rank order.
+ *   cols * element size must be a multiple of 16.
+ * tp_shard_norm -- out = RMSNorm(x) with the shard's gain g1 (which = 1) or
+ *   g2 (which = 2) over `rows` rows of hidden values (a copy of x if the
+ *   shard has no norm).  All pointers 16-byte aligned; enqueued on stream. */
+int tp_partial_reduce_scatter(const float *const *partials, int t, int rank, const void *residual_rows,
+                              void *out_rows, long long rows, int cols, int out_dtype, void *stream);
+int tp_all_gather(const void *const *pieces, int t, long long rows_per_rank, int cols, int dtype, void *out,
+                  void *stream);
+int tp_shard_norm(tp_shard *s, int which, const void *x, long long rows, void *out, void *stream);
 
 /* tp_shard_debug_view -- device address of a workspace tensor from the last
  * forward call, for diagnostics: which = 0 attention output o

@@ -25,6 +25,7 @@ from ._native import (TP_ACT_GELU, TP_ACT_SWIGLU, TP_BF16, TP_F32, TPError, TP_E
 
 ATTN = N.TP_STAGE_ATTN
 MLP = N.TP_STAGE_MLP
+PRENORM = N.TP_STAGE_PRENORM   # OR into a stage whose input is already normalised
 
 _DT = {"bf16": (N.TP_BF16, torch.bfloat16), "f32": (N.TP_F32, torch.float32)}
 
@@ -206,6 +207,19 @@ class Shard:
             _dev(out, "partial", torch.float32, (B, self.hidden)), _stream(stream)), "tp_shard_forward_decode")
         return out
 
+    def norm(self, which: int, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """RMSNorm of rows of x [..., hidden] with the shard's gain g1 (which=1)
+        or g2 (which=2): the per-rank norm of the sequence-parallel flow."""
+        if x.shape[-1] != self.hidden:
+            raise ValueError("x must end in hidden")
+        if out is None:
+            out = torch.empty_like(x)
+        rows = x.numel() // self.hidden
+        N.check(N.lib().tp_shard_norm(self._h, which, _dev(x, "x", self.torch_dtype),
+                                      rows, _dev(out, "out", self.torch_dtype, tuple(x.shape)), _stream(stream)),
+                "tp_shard_norm")
+        return out
+
     def fp8_weights(self, which: str, stream=None):
         """Copies of the E4M3 codes (uint8 [rows, cols], packed row order) and
         row scales (fp32 [rows]) of 'qkv', 'o', 'up' or 'down'."""
@@ -282,6 +296,53 @@ def partial_reduce(partials, residual: torch.Tensor | None = None, out: torch.Te
     N.check(N.lib().tp_partial_reduce(ptrs, len(partials), C.c_void_p(residual.data_ptr()) if residual is not None
                                       else None, _dev(out, "out", tdt), n, code, _stream(stream)),
             "tp_partial_reduce")
+    return out
+
+
+def partial_reduce_scatter(partials, rank: int, residual_rows: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, dtype: str | None = None, stream=None) -> torch.Tensor:
+    """Rank ``rank``'s token rows of (sum of the fp32 partials in rank order)
+    + residual_rows.  partials: t tensors [..., hidden] flattening to [T, hidden];
+    returns [T/t, hidden]."""
+    partials = list(partials)
+    t = len(partials)
+    if t == 0:
+        raise ValueError("need at least one partial")
+    shape = tuple(partials[0].shape)
+    cols = shape[-1]
+    rows = partials[0].numel() // cols
+    ptrs = (C.c_void_p * t)(*[_dev(p, f"partial[{i}]", torch.float32, shape).value for i, p in enumerate(partials)])
+    if dtype is None:
+        dtype = "bf16" if residual_rows is None or residual_rows.dtype == torch.bfloat16 else "f32"
+    code, tdt = _DT[dtype]
+    if rows % t:
+        raise ValueError("the token count must divide by the number of partials")
+    if residual_rows is not None:
+        _dev(residual_rows, "residual_rows", tdt)
+        if residual_rows.numel() != rows // t * cols:
+            raise ValueError("residual_rows must hold T/t rows")
+    if out is None:
+        out = torch.empty((rows // t, cols), dtype=tdt, device=partials[0].device)
+    N.check(N.lib().tp_partial_reduce_scatter(ptrs, t, rank,
+                                              C.c_void_p(residual_rows.data_ptr()) if residual_rows is not None
+                                              else None, _dev(out, "out", tdt), rows, cols, code, _stream(stream)),
+            "tp_partial_reduce_scatter")
+    return out
+
+
+def all_gather(pieces, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Rank-order concatenation of t equal [rows, cols] pieces into [t * rows, cols]."""
+    pieces = list(pieces)
+    t = len(pieces)
+    shape = tuple(pieces[0].shape)
+    dt = pieces[0].dtype
+    code = N.TP_BF16 if dt == torch.bfloat16 else N.TP_F32
+    cols = shape[-1]
+    rows = pieces[0].numel() // cols
+    ptrs = (C.c_void_p * t)(*[_dev(p, f"piece[{i}]", dt, shape).value for i, p in enumerate(pieces)])
+    if out is None:
+        out = torch.empty((t * rows, cols), dtype=dt, device=pieces[0].device)
+    N.check(N.lib().tp_all_gather(ptrs, t, rows, cols, code, _dev(out, "out", dt), _stream(stream)), "tp_all_gather")
     return out
 
 

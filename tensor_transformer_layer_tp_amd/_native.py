@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libtpshard.so")
 
 TP_OK, TP_E_ARG, TP_E_DIVIDE, TP_E_RANK, TP_E_NOMEM, TP_E_HIP, TP_E_KV_FULL, TP_E_STATE = 0, -1, -2, -3, -4, -5, -6, -7
 TP_F32, TP_BF16 = 0, 1
-TP_STAGE_ATTN, TP_STAGE_MLP = 0, 1
+TP_STAGE_ATTN, TP_STAGE_MLP, TP_STAGE_PRENORM = 0, 1, 0x10
 TP_ACT_SWIGLU, TP_ACT_GELU = 0, 1
 # kernel kinds of the shard's event timer (TP_K_*)
 KERNEL_KINDS = ["rmsnorm", "gemm_qkv", "attn_prefill", "gemm_out", "gemm_up", "gemm_down", "gemv_qkv",
@@ -47,6 +47,10 @@ SIGNATURES = [
     ("tp_partial_reduce", C.c_int, [C.POINTER(C.c_void_p), C.c_int, C.c_void_p, C.c_void_p, C.c_longlong, C.c_int,
                                     C.c_void_p]),
     ("tp_shard_debug_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),
+    ("tp_partial_reduce_scatter", C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_longlong,
+                                            C.c_int, C.c_int, C.c_void_p]),
+    ("tp_all_gather", C.c_int, [C.c_void_p, C.c_int, C.c_longlong, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
+    ("tp_shard_norm", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_longlong, C.c_void_p, C.c_void_p]),
     ("tp_shard_fp8_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                     C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     ("tp_tune_set_gemm_config", C.c_int, [C.c_int]),

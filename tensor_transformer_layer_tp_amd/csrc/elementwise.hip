@@ -100,6 +100,21 @@ __global__ __launch_bounds__(256) void reduce_kernel(Parts parts, int t, const v
     }
 }
 
+// All-gather on one device: out = rank-order concatenation of t pieces of
+// `units` 16-byte vectors each (pieces and out 16-byte aligned).
+struct Pieces {
+    const u32x4* p[64];
+};
+
+__global__ __launch_bounds__(256) void gather_kernel(Pieces pieces, int t, long long units, u32x4* __restrict__ out) {
+    const long long total = units * t;
+    const long long stride = (long long)gridDim.x * 256;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < total; i += stride) {
+        const int r = (int)(i / units);
+        out[i] = pieces.p[r][i - (long long)r * units];
+    }
+}
+
 // cos/sin of p * theta^(-2i/d) for p < npos, i < d/2, evaluated in double.
 __global__ void rope_table_kernel(float* cos_t, float* sin_t, int npos, int d, double theta) {
     const int half = d / 2;
@@ -123,6 +138,15 @@ void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, floa
 void rmsnorm_f32(const float* x, const float* g, float* out, int rows, int n, float eps, hipStream_t st) {
     if (rows <= 0) return;
     hipLaunchKernelGGL(rmsnorm_f32_kernel, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
+}
+
+void all_gather(const void* const* pieces, int t, long long piece_bytes, void* out, hipStream_t st) {
+    if (piece_bytes <= 0) return;
+    Pieces P;
+    for (int r = 0; r < 64; ++r) P.p[r] = r < t ? (const u32x4*)pieces[r] : nullptr;
+    const long long units = piece_bytes / 16;
+    const int blocks = (int)std::min<long long>(std::max<long long>((units * t + 255) / 256, 1), 256LL * 8);
+    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, st, P, t, units, (u32x4*)out);
 }
 
 void partial_reduce(const float* const* parts, int t, const void* residual, void* out, long long n,

@@ -56,6 +56,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                                          int wcol0, int M, int N) {
     const int col_in = lane & 31;
     const int row_in = 4 * (lane >> 5);
+    const int cb = epi.col0;   // this launch's first output column (bounds stay launch-relative)
     // Stores are predicated per element (no early exits): divergent control
     // flow around the accumulator tile makes the compiler spill it.
     if constexpr (MODE == EPI_F32) {
@@ -68,7 +69,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                 for (int r = 0; r < 16; ++r) {
                     const int row = wrow0 + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
                     const int col = wcol0 + j * 32 + col_in;
-                    if (row < M && col < N) o[(long long)row * epi.ldo + col] = acc[i][j][r];
+                    if (row < M && col < N) o[(long long)row * epi.ldo + cb + col] = acc[i][j][r];
                 }
     } else if constexpr (MODE == EPI_STORE || MODE == EPI_GELU) {
         bf16* o = (bf16*)epi.out;
@@ -83,7 +84,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                     const int col = wcol0 + j * 32 + col_in;
                     float v = acc[i][j][r];
                     if constexpr (gelu) v = gelu_erf_f(v);
-                    if (row < M && col < N) o[(long long)row * epi.ldo + col] = f2bf(v);
+                    if (row < M && col < N) o[(long long)row * epi.ldo + cb + col] = f2bf(v);
                 }
     } else if constexpr (MODE == EPI_SWIGLU) {
         bf16* o = (bf16*)epi.out;
@@ -96,7 +97,8 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                     const int row = wrow0 + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
                     const int gcol = wcol0 + p * 64;  // 64-aligned group: [gate 32 | up 32]
                     const float g = acc[i][2 * p][r], u = acc[i][2 * p + 1][r];
-                    if (row < M && gcol < N) o[(long long)row * epi.ldo + (gcol >> 1) + col_in] = f2bf(silu_f(g) * u);
+                    if (row < M && gcol < N)
+                        o[(long long)row * epi.ldo + ((cb + gcol) >> 1) + col_in] = f2bf(silu_f(g) * u);
                 }
     } else {  // MODE == EPI_QKV
         // EPI_QKV: the 64-column group at gcol holds dims (i1, i1 + d/2) of one
@@ -107,11 +109,12 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
         const int qcols = q.hl * d, kcols = q.kvl * d;
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
-            const int gcol = wcol0 + p * 64;
-            const int region = gcol < qcols ? 0 : (gcol < qcols + kcols ? 1 : 2);
+            const int gcol = wcol0 + p * 64;          // launch-relative (bounds)
+            const int acol = cb + gcol;               // absolute packed column
+            const int region = acol < qcols ? 0 : (acol < qcols + kcols ? 1 : 2);
             const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
-            const int head = (gcol - base) / d;
-            const int i1 = 32 * (((gcol - base) % d) >> 6) + col_in;
+            const int head = (acol - base) / d;
+            const int i1 = 32 * (((acol - base) % d) >> 6) + col_in;
             const bool rot = region < 2 && q.rope_cos != nullptr;
             bf16* dbase = region == 0 ? (bf16*)q.q : (region == 1 ? (bf16*)q.k : (bf16*)q.v);
             const int nh = region == 0 ? q.hl : q.kvl;
@@ -585,25 +588,59 @@ bool usable(int c, int mode) {
     return !(c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE));
 }
 
-// Shape-based choice.  Large problems (at least 1.5 waves of 256x256 tiles)
-// take the 4-stage 256x256 DMA ring, which has the highest per-CU efficiency.
-// Otherwise the modelled time of a configuration is the number of tiles the
-// busiest CU runs times the tile's work over its efficiency; the DMA rings
-// lose 20% with the rotary epilogue (measured on the 7B Q/K/V projection).
-int pick(int M, int N, int mode) {
-    if (g_forced_cfg >= 0 && g_forced_cfg < kNumCfg && usable(g_forced_cfg, mode)) return g_forced_cfg;
-    if (usable(4, mode) && (long long)cdiv(M, 256) * cdiv(N, 256) >= 384) return 4;
-    int best = 1;
+// Modelled time of one launch: rounds of 256 tiles (one per CU), each the
+// tile's FLOPs at the configuration's per-CU rate, plus a launch.  The DMA
+// rings lose 20% with the rotary epilogue (measured on the 7B Q/K/V shape).
+constexpr double kCuFlopPerUs = 4.7e6;   // per-CU bf16 rate of a configuration with eff = 1
+constexpr double kLaunchUs = 3.0;
+
+double model_us(int c, int mode, int M, int N, int K) {
+    const Cfg& f = kCfgs[c];
+    const long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
+    const double eff = f.eff * ((c >= 3 && mode == EPI_QKV) ? 0.8 : 1.0);
+    return kLaunchUs + (double)((tiles + 255) / 256) * 2.0 * f.bm * f.bn * K / (eff * kCuFlopPerUs);
+}
+
+// A GEMM runs as one launch, or as two over column ranges: the first covers
+// whole rounds of a large tile, the second the remaining columns with a
+// smaller tile, so that the last round is not mostly idle (the tile count of
+// a shape like 2048 x 11008 leaves 88 of 344 tiles for a second round).
+struct Plan {
+    int parts;
+    int cfg[2];
+    int c0[2], ncols[2];
+};
+
+Plan plan(int M, int N, int K, int mode) {
+    Plan best{1, {1, 1}, {0, 0}, {N, 0}};
+    if (g_forced_cfg >= 0 && g_forced_cfg < kNumCfg && usable(g_forced_cfg, mode)) {
+        best.cfg[0] = g_forced_cfg;
+        return best;
+    }
     double best_t = 1e30;
     for (int c = 0; c < kNumCfg; ++c) {
         if (!usable(c, mode)) continue;
-        const Cfg& f = kCfgs[c];
-        const long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
-        const double eff = f.eff * ((c >= 3 && mode == EPI_QKV) ? 0.8 : 1.0);
-        const double t = (double)((tiles + 255) / 256) * f.bm * f.bn / eff;
+        const double t = model_us(c, mode, M, N, K);
         if (t < best_t * 0.999) {
             best_t = t;
-            best = c;
+            best = Plan{1, {c, c}, {0, 0}, {N, 0}};
+        }
+    }
+    for (int b = 0; b < kNumCfg; ++b) {
+        if (!usable(b, mode) || kCfgs[b].occ != 1) continue;
+        const int tiles_m = cdiv(M, kCfgs[b].bm);
+        if (tiles_m > 256) continue;
+        const int round_cols = (256 / tiles_m) * kCfgs[b].bn;
+        const int n_big = (N / round_cols) * round_cols;
+        if (n_big == 0 || n_big == N) continue;
+        const double t_big = model_us(b, mode, M, n_big, K);
+        for (int c = 0; c < kNumCfg; ++c) {
+            if (!usable(c, mode)) continue;
+            const double t = t_big + model_us(c, mode, M, N - n_big, K);
+            if (t < best_t * 0.97) {   // a second launch must clearly pay for itself
+                best_t = t;
+                best = Plan{2, {b, c}, {0, n_big}, {n_big, N - n_big}};
+            }
         }
     }
     return best;
@@ -616,14 +653,19 @@ int gemm_config_count() { return kNumCfg; }
 
 void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M, int N, int K,
                const Epilogue& epi, hipStream_t st) {
-    const Args a{A, lda, B, ldb, M, N, K, epi, st};
-    const int c = pick(M, N, epi.mode);
-    switch (epi.mode) {
-        case EPI_F32: launch_cfg<EPI_F32>(c, a); break;
-        case EPI_QKV: launch_cfg<EPI_QKV>(c, a); break;
-        case EPI_SWIGLU: launch_cfg<EPI_SWIGLU>(c, a); break;
-        case EPI_GELU: launch_cfg<EPI_GELU>(c, a); break;
-        default: launch_cfg<EPI_STORE>(c, a); break;
+    const Plan p = plan(M, N, K, epi.mode);
+    for (int i = 0; i < p.parts; ++i) {
+        Epilogue e = epi;
+        e.col0 = epi.col0 + p.c0[i];
+        if (i > 0) e.len = LenUpdate{nullptr, 0, 0};   // one launch updates the cache length
+        const Args a{A, lda, B + (long long)p.c0[i] * ldb, ldb, M, p.ncols[i], K, e, st};
+        switch (epi.mode) {
+            case EPI_F32: launch_cfg<EPI_F32>(p.cfg[i], a); break;
+            case EPI_QKV: launch_cfg<EPI_QKV>(p.cfg[i], a); break;
+            case EPI_SWIGLU: launch_cfg<EPI_SWIGLU>(p.cfg[i], a); break;
+            case EPI_GELU: launch_cfg<EPI_GELU>(p.cfg[i], a); break;
+            default: launch_cfg<EPI_STORE>(p.cfg[i], a); break;
+        }
     }
 }
 

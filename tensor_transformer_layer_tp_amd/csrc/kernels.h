@@ -42,6 +42,7 @@ struct Epilogue {
     long long ldo;      // leading dimension of out, in elements
     QKVDest qkv;
     LenUpdate len;
+    int col0;           // GEMM launches over a column range: its first column (multiple of 64)
 };
 
 __device__ __forceinline__ void apply_len_update(const LenUpdate& u) {
@@ -103,6 +104,8 @@ void attn_f32(const float* Q, const float* K, const float* V, float* O, int B, i
 void partial_reduce(const float* const* parts, int t, const void* residual, void* out, long long n,
                     int bf16_out, hipStream_t st);
 void rope_table(float* cos_t, float* sin_t, int npos, int d, float theta, hipStream_t st);
+// out = rank-order concatenation of t pieces of piece_bytes each (multiple of 16, 16-byte aligned)
+void all_gather(const void* const* pieces, int t, long long piece_bytes, void* out, hipStream_t st);
 
 // tuning: -1 = heuristic, otherwise a fixed GEMM tile configuration index
 void set_gemm_config(int cfg);

@@ -475,6 +475,8 @@ int tp_kv_get_len(const tp_kv* kv, int* len) {
 
 int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv, float* partial,
                              void* stream) {
+    const bool prenorm = (stage & TP_STAGE_PRENORM) != 0;
+    stage &= ~TP_STAGE_PRENORM;
     if (!s || !x || !partial || batch <= 0 || seq <= 0) return TP_E_ARG;
     if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return TP_E_ARG;
     if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
@@ -497,7 +499,7 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
     const void* xin = x;
     if (stage == TP_STAGE_ATTN) {
         TRY(ensure_rope(s, seq, st));
-        if (s->o.rmsnorm) {
+        if (s->o.rmsnorm && !prenorm) {
             KTimer kt(s, TP_K_RMSNORM, st);
             TRY(launch_norm(s, x, s->g1, ws + L.n, T, st));
             xin = ws + L.n;
@@ -534,7 +536,7 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         }
         if (kv) kv->len = seq;
     } else {
-        if (s->o.rmsnorm) {
+        if (s->o.rmsnorm && !prenorm) {
             KTimer kt(s, TP_K_RMSNORM, st);
             TRY(launch_norm(s, x, s->g2, ws + L.n, T, st));
             xin = ws + L.n;
@@ -554,6 +556,8 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
 
 int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial,
                             void* stream) {
+    const bool prenorm = (stage & TP_STAGE_PRENORM) != 0;
+    stage &= ~TP_STAGE_PRENORM;
     if (!s || !x || !partial || batch <= 0) return TP_E_ARG;
     if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return TP_E_ARG;
     if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
@@ -593,11 +597,11 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.qkv = QKVDest{1, L, kv->dlen, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
                               s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
             KTimer kt(s, TP_K_GEMV_QKV, st);
-            TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g1 : nullptr, s->w_qkv, s->nqkv, s->hidden, epi,
-                            ws + lay.n, ws + lay.scr, st, 0));
+            const void* g1 = s->o.rmsnorm && !prenorm ? s->g1 : nullptr;
+            TRY(launch_gemv(s, x, batch, g1, s->w_qkv, s->nqkv, s->hidden, epi, ws + lay.n, ws + lay.scr, st, 0));
         } else {
             const void* xin = x;
-            if (s->o.rmsnorm) {
+            if (s->o.rmsnorm && !prenorm) {
                 KTimer kt(s, TP_K_RMSNORM, st);
                 TRY(launch_norm(s, x, s->g1, ws + lay.n, batch, st));
                 xin = ws + lay.n;
@@ -639,8 +643,8 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.ldo = s->fl;
             {
                 KTimer kt(s, TP_K_GEMV_UP, st);
-                TRY(launch_gemv(s, x, batch, s->o.rmsnorm ? s->g2 : nullptr, s->w_up, s->nup, s->hidden, epi,
-                                ws + lay.n, ws + lay.scr, st, 2));
+                const void* g2 = s->o.rmsnorm && !prenorm ? s->g2 : nullptr;
+                TRY(launch_gemv(s, x, batch, g2, s->w_up, s->nup, s->hidden, epi, ws + lay.n, ws + lay.scr, st, 2));
             }
             Epilogue e2{};
             e2.mode = EPI_F32;
@@ -651,7 +655,7 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
                             ws + lay.scr, st, 3));
         } else {
             const void* xin = x;
-            if (s->o.rmsnorm) {
+            if (s->o.rmsnorm && !prenorm) {
                 KTimer kt(s, TP_K_RMSNORM, st);
                 TRY(launch_norm(s, x, s->g2, ws + lay.n, batch, st));
                 xin = ws + lay.n;
@@ -679,6 +683,54 @@ int tp_partial_reduce(const float* const* partials, int t, const void* residual,
     partial_reduce(partials, t, residual, out, n, out_dtype == TP_BF16, (hipStream_t)stream);
     LAUNCH_CHECK("partial_reduce");
     return TP_OK;
+}
+
+int tp_partial_reduce_scatter(const float* const* partials, int t, int rank, const void* residual_rows,
+                              void* out_rows, long long rows, int cols, int out_dtype, void* stream) {
+    if (!partials || t < 1 || t > 64 || rows < 0 || cols <= 0 || cols % 8) return TP_E_ARG;
+    if (rank < 0 || rank >= t) return TP_E_RANK;
+    if (rows % t) return TP_E_DIVIDE;
+    if (out_dtype != TP_BF16 && out_dtype != TP_F32) return TP_E_ARG;
+    const long long n = rows / t * (long long)cols;
+    if (n == 0) return TP_OK;
+    if (!out_rows || !aligned16(out_rows) || (residual_rows && !aligned16(residual_rows))) return TP_E_ARG;
+    std::vector<const float*> mine(t);
+    for (int r = 0; r < t; ++r) {
+        if (!partials[r] || !aligned16(partials[r])) return TP_E_ARG;
+        mine[r] = partials[r] + (long long)rank * n;   // this rank's rows of every partial
+    }
+    partial_reduce(mine.data(), t, residual_rows, out_rows, n, out_dtype == TP_BF16, (hipStream_t)stream);
+    LAUNCH_CHECK("partial_reduce_scatter");
+    return TP_OK;
+}
+
+int tp_all_gather(const void* const* pieces, int t, long long rows_per_rank, int cols, int dtype, void* out,
+                  void* stream) {
+    if (!pieces || t < 1 || t > 64 || rows_per_rank < 0 || cols <= 0) return TP_E_ARG;
+    if (dtype != TP_BF16 && dtype != TP_F32) return TP_E_ARG;
+    const long long row_bytes = (long long)cols * (dtype == TP_BF16 ? 2 : 4);
+    if (row_bytes % 16) return TP_E_ARG;
+    if (rows_per_rank == 0) return TP_OK;
+    if (!out || !aligned16(out)) return TP_E_ARG;
+    for (int r = 0; r < t; ++r)
+        if (!pieces[r] || !aligned16(pieces[r])) return TP_E_ARG;
+    all_gather(pieces, t, rows_per_rank * row_bytes, out, (hipStream_t)stream);
+    LAUNCH_CHECK("all_gather");
+    return TP_OK;
+}
+
+int tp_shard_norm(tp_shard* s, int which, const void* x, long long rows, void* out, void* stream) {
+    if (!s || (which != 1 && which != 2) || rows < 0) return TP_E_ARG;
+    if (rows == 0) return TP_OK;
+    if (!x || !out || !aligned16(x) || !aligned16(out) || rows > INT32_MAX) return TP_E_ARG;
+    if (!s->loaded) return TP_E_STATE;
+    hipStream_t st = (hipStream_t)stream;
+    if (!s->o.rmsnorm) {
+        HIP_TRY(hipMemcpyAsync(out, x, (size_t)rows * s->hidden * s->esz, hipMemcpyDeviceToDevice, st));
+        return TP_OK;
+    }
+    KTimer kt(s, TP_K_RMSNORM, st);
+    return launch_norm(s, x, which == 1 ? s->g1 : s->g2, out, rows, st);
 }
 
 int tp_shard_debug_view(tp_shard* s, int which, void** ptr) {

@@ -156,3 +156,26 @@ def test_fp8_option_rules():
     assert lib.tp_shard_fp8_view(h, 0, C.byref(q), C.byref(sc), C.byref(r), C.byref(c)) == N.TP_E_STATE
     assert lib.tp_shard_fp8_view(h, 4, C.byref(q), C.byref(sc), C.byref(r), C.byref(c)) == N.TP_E_ARG
     lib.tp_shard_destroy(h)
+
+
+def test_sequence_parallel_argument_rules():
+    """Argument checks of the reduce-scatter, all-gather and norm entry points
+    (all detected on the host before any device work)."""
+    lib = N.lib()
+    fake = C.c_void_p(1 << 20)            # 16-byte aligned, never dereferenced
+    parts = (C.c_void_p * 2)(fake, fake)
+    rs = lib.tp_partial_reduce_scatter
+    assert rs(parts, 2, 0, None, fake, 11, 64, N.TP_BF16, None) == N.TP_E_DIVIDE    # rows % t
+    assert rs(parts, 2, 0, None, fake, 10, 60, N.TP_BF16, None) == N.TP_E_ARG       # cols % 8
+    assert rs(parts, 2, 2, None, fake, 10, 64, N.TP_BF16, None) == N.TP_E_RANK      # rank >= t
+    assert rs(parts, 2, 0, None, fake, 10, 64, 7, None) == N.TP_E_ARG               # dtype
+    assert rs(parts, 2, 0, None, fake, 0, 64, N.TP_BF16, None) == N.TP_OK           # nothing to do
+    ag = lib.tp_all_gather
+    assert ag(parts, 2, 4, 4, N.TP_BF16, fake, None) == N.TP_E_ARG                  # 8-byte rows
+    assert ag(parts, 2, 0, 64, N.TP_BF16, fake, None) == N.TP_OK
+    assert ag(parts, 0, 4, 64, N.TP_BF16, fake, None) == N.TP_E_ARG
+    h = C.c_void_p()
+    assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, None, C.byref(h)) == N.TP_OK
+    assert lib.tp_shard_norm(h, 3, fake, 4, fake, None) == N.TP_E_ARG
+    assert lib.tp_shard_norm(h, 1, fake, 4, fake, None) == N.TP_E_STATE             # no weights yet
+    lib.tp_shard_destroy(h)

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 from oracle import layer as O
-from tensor_transformer_layer_tp_amd import ATTN, MLP, Shard, TPError, TP_E_KV_FULL, partial_reduce, synth
+from tensor_transformer_layer_tp_amd import (ATTN, MLP, PRENORM, Shard, TPError, TP_E_KV_FULL, all_gather,
+                                             partial_reduce, partial_reduce_scatter, synth)
 
 from helpers import Layer, assert_close, rank_cache, sum_magnitude, to_np
 
@@ -444,6 +445,49 @@ def test_kv_full_and_errors():
     with pytest.raises(TPError):
         sh.decode(ATTN, L.dev["x"][:, 4].expand(2, 512).contiguous(), kv)   # batch mismatch
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- sequence-parallel variant
+
+@pytest.mark.parametrize("tp,B,S", [(2, 2, 64), (4, 1, 96)])
+def test_sequence_parallel_chain(tp, B, S):
+    """All ranks of the sequence-parallel flow: per-rank norms of token rows,
+    all-gather, stages without their norm, reduce-scatter.  Against the
+    oracle's sequence-parallel layer, and bit for bit against the plain GPU
+    path (the same kernels on the same values)."""
+    from oracle import sp
+    announce(f"sequence-parallel chain t={tp} B={B} S={S}")
+    hid = 1024
+    L = Layer(hid, 8, 4, 2816, batch=B, seq=S, gamma_noise=True, seed=61)
+    T, n = B * S, B * S // tp
+    shards = [L.shard(tp, r) for r in range(tp)]
+    xf = L.dev["x"].reshape(T, hid)
+    xs = [xf[r * n:(r + 1) * n].contiguous() for r in range(tp)]
+    n1 = all_gather([shards[r].norm(1, xs[r]) for r in range(tp)]).reshape(B, S, hid)
+    pa = [sh.prefill(ATTN | PRENORM, n1, out=nan_like((B, S, hid))) for sh in shards]
+    hs = [partial_reduce_scatter(pa, r, xs[r]) for r in range(tp)]
+    n2 = all_gather([shards[r].norm(2, hs[r]) for r in range(tp)]).reshape(B, S, hid)
+    pm = [sh.prefill(MLP | PRENORM, n2, out=nan_like((B, S, hid))) for sh in shards]
+    ys = [partial_reduce_scatter(pm, r, hs[r]) for r in range(tp)]
+    torch.cuda.synchronize()
+    ref = sp.layer_sp(L.exact["x"], L.W, L.spec, tp)
+    x_rows = [L.exact["x"].reshape(T, hid)[r * n:(r + 1) * n] for r in range(tp)]
+    for r in range(tp):
+        assert_close(to_np(n1).reshape(T, hid)[r * n:(r + 1) * n], ref["n1"][r], f"n1 rows r{r}", "bf16")
+        assert_close(to_np(pa[r]), ref["attn"][r]["partial"], f"attn partial r{r}", "bf16")
+        assert_close(to_np(hs[r]), ref["h"][r], f"h rows r{r}", "bf16",
+                     sum_magnitude(x_rows[r], [a["partial"].reshape(T, hid)[r * n:(r + 1) * n] for a in ref["attn"]]))
+    y = np.concatenate([to_np(v) for v in ys])
+    rel = np.linalg.norm(y - np.concatenate(ref["y"])) / np.linalg.norm(np.concatenate(ref["y"]))
+    assert rel <= 1e-2, f"sequence-parallel y: relative Frobenius error {rel:.3g}"
+    # the plain flow on the GPU gives the same bits
+    pa_plain = [sh.prefill(ATTN, L.dev["x"], out=nan_like((B, S, hid))) for sh in shards]
+    h_plain = partial_reduce(pa_plain, residual=L.dev["x"])
+    pm_plain = [sh.prefill(MLP, h_plain, out=nan_like((B, S, hid))) for sh in shards]
+    y_plain = partial_reduce(pm_plain, residual=h_plain)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(hs), h_plain.reshape(T, hid))
+    assert torch.equal(torch.cat(ys), y_plain.reshape(T, hid))
 
 
 # ---------------------------------------------------------------- full-size workloads
