@@ -306,16 +306,23 @@ def bench_sp(args, torch, hidden, heads, kv_heads, ffn, t, wdev, x):
 
 # ---------------------------------------------------------------- decode
 
-def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copies, fill, fp8=False):
+def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copies, fill, fp8=False, block=0):
     """`copies` distinct rank-0 shards (their weights rotate through HBM)
     with caches at length L0; fill(kv) writes the first copy's cache
-    content, the others copy it."""
+    content, the others copy it.  block > 0: paged caches of that block
+    size with a scrambled block table."""
+    import numpy as np
     from tensor_transformer_layer_tp_amd import Shard
     layers = []
     for i in range(copies):
         sh = Shard(hidden, heads, kv_heads, ffn, t, 0, decode_fp8=fp8)
         sh.load_weights(wdev)
-        kv = sh.kv_cache(B, cap)
+        if block:
+            mb = -(-cap // block)
+            kv = sh.kv_cache_paged(B, cap, block, B * mb)
+            kv.set_block_table(np.random.default_rng(5).permutation(B * mb).reshape(B, mb))
+        else:
+            kv = sh.kv_cache(B, cap)
         if i == 0:
             fill(kv)
         else:
@@ -361,7 +368,8 @@ def capture(torch, fn):
     return g
 
 
-def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0, roof_key, fp8=False):
+def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, fill, x0, roof_key, fp8=False,
+                 block=0):
     """Decode through a stack of layer copies: eager calls, then the same
     step captured once in a HIP graph and replayed (each replay appends one
     token per layer: the kernels read and advance the device-resident cache
@@ -369,7 +377,7 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
     wb = weight_bytes(hidden, heads, kv_heads, ffn, t, fp8)
     nl = args.decode_layers or max(2, -(-int(MIN_DECODE_FOOTPRINT) // wb))
     cap = L0 + 4 * (args.warmup + args.steps) + 8
-    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, 1, L0, cap, nl, fill, fp8)
+    layers = decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, 1, L0, cap, nl, fill, fp8, block)
     stream = torch.cuda.current_stream()
     step = decode_step_fn(torch, layers, hidden, t, 1, x0)
     ms, dist = timed(torch, step, args.steps, args.warmup, stream)
@@ -401,8 +409,9 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
     d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
     best = min(us, us_graph)
     return {
-        "workload": f"{name}{', E4M3 weights (per-row scales)' if fp8 else ''}, {nl} distinct layer copies "
-                    f"({nl * wb / 1e9:.2f} GB of weights)",
+        "workload": f"{name}{', E4M3 weights (per-row scales)' if fp8 else ''}"
+                    f"{f', paged cache ({block}-position blocks, scrambled table)' if block else ''}, "
+                    f"{nl} distinct layer copies ({nl * wb / 1e9:.2f} GB of weights)",
         "us_per_token_layer": round(best, 3),
         "us_per_token_layer_eager": round(us, 3),
         "us_per_token_layer_graph": round(us_graph, 3),
@@ -457,7 +466,16 @@ def run_7b_decode(args, torch):
                        dev["x_dec"], "gemv_up_7b_t4")
     dec8 = bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill,
                         dev["x_dec"], "gemv8_up_7b_t4", fp8=True)
-    return dec, dec8
+
+    def fill_pages(kv):   # the pool holds N(0,1) rows (timing only)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(6)
+        kv.write(torch.randn(kv.shape, generator=g, device="cuda").to(torch.bfloat16),
+                 torch.randn(kv.shape, generator=g, device="cuda").to(torch.bfloat16))
+
+    decp = bench_decode(args, torch, name, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, w.kv_len, fill_pages,
+                        dev["x_dec"], "gemv_up_7b_t4_paged", block=16)
+    return dec, dec8, decp
 
 
 def run_70b(args, torch):
@@ -764,7 +782,7 @@ def main():
               "ms_per_step_all_kernels_bracketed", "kernels", "roofline", "sequence_parallel"):
         line[k] = pre[k]
     if dec is not None:
-        line["decode"], line["decode_fp8"] = dec
+        line["decode"], line["decode_fp8"], line["decode_paged"] = dec
     if big is not None:
         line["prefill_70b"] = big[0]
         if big[1] is not None:

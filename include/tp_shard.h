@@ -146,8 +146,30 @@ int tp_shard_reserve(tp_shard *s, long long max_tokens);
  * zero-filled, length 0.  TP_F32 caches hold at most 16000 positions. */
 int tp_kv_create(const tp_shard *s, int batch, int max_seq, tp_kv **out);
 
-/* tp_kv_view -- device pointers to the K and V arrays (layout above), e.g.
- * to fill a cache with synthetic content.  Either output may be NULL. */
+/* tp_kv_create_paged -- paged KV cache (TP_BF16 shards): K and V are pools
+ * of `num_blocks` blocks, each [kv_heads/t, block_size, head_dim], and a
+ * block table [batch, ceil(max_seq / block_size)] of block ids maps
+ * position p of sequence b to block table[b][p / block_size], row
+ * p % block_size.  The pages' serving context names paged attention as the
+ * memory structure a tensor-parallel split applies to (byteledger "Tensor
+ * Parallelism: Splitting One Layer Across GPUs", "Interaction with the rest
+ * of serving"); this layout is the library's.  block_size is a power of two
+ * in [16, 1024].  Until tp_kv_set_block_table, sequence b uses blocks
+ * b * max_blocks + i (block 0 where that exceeds the pool).  Prefill writes
+ * the prompt's K/V rows into the pages; decode appends and attends through
+ * the table.  Zero-filled, length 0. */
+int tp_kv_create_paged(const tp_shard *s, int batch, int max_seq, int block_size, int num_blocks,
+                       tp_kv **out);
+
+/* tp_kv_set_block_table -- copy a HOST table [batch, ceil(max_seq / block_size)]
+ * of block ids in [0, num_blocks) to the cache (waits for the device first).
+ * Sequences may share no block they write to.  TP_E_ARG for an id out of
+ * range, TP_E_STATE for a contiguous cache. */
+int tp_kv_set_block_table(tp_kv *kv, const int *host_table);
+
+/* tp_kv_view -- device pointers to the K and V arrays (layout above; the
+ * pools of a paged cache), e.g. to fill a cache with synthetic content.
+ * Either output may be NULL. */
 int tp_kv_view(tp_kv *kv, void **k, void **v);
 
 /* tp_kv_set_len / tp_kv_get_len -- number of valid positions [0, len).

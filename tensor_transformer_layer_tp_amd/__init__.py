@@ -64,18 +64,33 @@ def _memcpy_d2d(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
 
 
 class KVCache:
-    """K/V cache of one rank's KV heads: K and V [batch, kv_heads/t, max_seq, d]."""
+    """K/V cache of one rank's KV heads: K and V [batch, kv_heads/t, max_seq, d],
+    or (paged) pools [num_blocks, kv_heads/t, block_size, d] with a block table."""
 
-    def __init__(self, shard: "Shard", batch: int, max_seq: int):
+    def __init__(self, shard: "Shard", batch: int, max_seq: int, block_size: int = 0, num_blocks: int = 0):
         h = C.c_void_p()
-        N.check(N.lib().tp_kv_create(shard._h, batch, max_seq, C.byref(h)), "tp_kv_create")
+        if block_size:
+            N.check(N.lib().tp_kv_create_paged(shard._h, batch, max_seq, block_size, num_blocks, C.byref(h)),
+                    "tp_kv_create_paged")
+            self.shape = (num_blocks, shard.kv_local, block_size, shard.head_dim)
+            self.max_blocks = -(-max_seq // block_size)
+        else:
+            N.check(N.lib().tp_kv_create(shard._h, batch, max_seq, C.byref(h)), "tp_kv_create")
+            self.shape = (batch, shard.kv_local, max_seq, shard.head_dim)
         self._h = h
         self.shard = shard
-        self.batch, self.max_seq = batch, max_seq
-        self.shape = (batch, shard.kv_local, max_seq, shard.head_dim)
+        self.batch, self.max_seq, self.block_size = batch, max_seq, block_size
         k, v = C.c_void_p(), C.c_void_p()
         N.check(N.lib().tp_kv_view(h, C.byref(k), C.byref(v)), "tp_kv_view")
         self._k, self._v = k.value, v.value
+
+    def set_block_table(self, table) -> None:
+        """Block ids [batch, ceil(max_seq / block_size)] (paged caches)."""
+        import numpy as np
+        t = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+        if t.shape != (self.batch, self.max_blocks):
+            raise ValueError(f"block table must be {(self.batch, self.max_blocks)}")
+        N.check(N.lib().tp_kv_set_block_table(self._h, t.ctypes.data_as(C.c_void_p)), "tp_kv_set_block_table")
 
     @property
     def nbytes(self) -> int:
@@ -175,6 +190,9 @@ class Shard:
 
     def reserve(self, max_tokens: int) -> None:
         N.check(N.lib().tp_shard_reserve(self._h, int(max_tokens)), "tp_shard_reserve")
+
+    def kv_cache_paged(self, batch: int, max_seq: int, block_size: int, num_blocks: int) -> KVCache:
+        return KVCache(self, batch, max_seq, block_size, num_blocks)
 
     def kv_cache(self, batch: int, max_seq: int) -> KVCache:
         return KVCache(self, batch, max_seq)

@@ -51,7 +51,7 @@ __device__ __forceinline__ void pair_store(const Epilogue& epi, int b, int r1, f
         }
         bf16* dst = region == 0 ? (bf16*)q.q + ((long long)b * q.hl + head) * d
                                 : (bf16*)(region == 1 ? q.k : q.v) +
-                                      (((long long)b * q.kvl + head) * q.ld_seq + pos) * d;
+                                      kv_row(b, head, pos, q.kvl, q.ld_seq, d, q.table, q.bsz, q.max_blocks);
         dst[i1] = f2bf(o1);
         dst[i1 + half] = f2bf(o2);
     }
@@ -276,7 +276,8 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restrict__ q, const bf16* __restrict__ K,
                                                          const bf16* __restrict__ V, float* __restrict__ scr,
                                                          int hl, int kvl, const int* __restrict__ len_dev,
-                                                         int ld_seq, float scale_log2) {
+                                                         int ld_seq, float scale_log2, const int* __restrict__ table,
+                                                         int bsz, int max_blocks) {
     const int G = hl / kvl;
     const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int nchunks = gridDim.x;   // chunk stride of the scratch (sized for ld_seq positions)
@@ -294,8 +295,6 @@ __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restr
     }
     __syncthreads();
 
-    const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
-    const bf16* Vb = V + ((long long)b * kvl + kvh) * ld_seq * D;
     // scores: thread = (key, quarter of the head dim)
     {
         constexpr int QD = D / 4;
@@ -304,7 +303,8 @@ __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restr
         float kf[QD];
 #pragma unroll
         for (int c = 0; c < QD / 8; ++c) {
-            const u16x8 v = *(const u16x8*)(Kb + (long long)gk * D + seg * QD + c * 8);
+            const u16x8 v = *(const u16x8*)(K + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks) +
+                                            seg * QD + c * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) kf[c * 8 + e] = bfbits2f(v[e]);
         }
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restr
         for (int i = 0; i < KPG; ++i) {
             const int key = kg * KPG + i;
             const int gk = min(k0 + key, len - 1);
-            const u16x8 v = *(const u16x8*)(Vb + (long long)gk * D + dc * 8);
+            const u16x8 v = *(const u16x8*)(V + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks) + dc * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) vf[i][e] = bfbits2f(v[e]);
         }
@@ -387,7 +387,8 @@ template <int D, int CH>
 __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict__ q, const bf16* __restrict__ K,
                                                          const bf16* __restrict__ V, float* __restrict__ scr,
                                                          int hl, int kvl, const int* __restrict__ len_dev,
-                                                         int ld_seq, float scale_log2) {
+                                                         int ld_seq, float scale_log2, const int* __restrict__ table,
+                                                         int bsz, int max_blocks) {
     constexpr int SEG = 256 / CH, SD = D / SEG, DC = D / 8;
     static_assert(SD % 8 == 0, "score segment");
     const int G = hl / kvl;
@@ -404,8 +405,6 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     // to the capacity (always addressable) and rows at or past the length are
     // masked once it is known.
     const int lenp = *len_dev;
-    const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
-    const bf16* Vb = V + ((long long)b * kvl + kvh) * ld_seq * D;
     const bf16* qg = q + ((long long)b * hl + kvh * G) * D;   // the group's heads are adjacent
     const int key = tid / SEG, seg = tid % SEG;
     // every load first (fixed trip counts, clamped addresses), then the LDS writes
@@ -414,13 +413,15 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     u16x8 kraw[SD / 8], vraw[VCH], qraw[2];
     {
         const int gk = min(k0 + key, ld_seq - 1);
+        const bf16* krow = K + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks);
 #pragma unroll
-        for (int c = 0; c < SD / 8; ++c) kraw[c] = *(const u16x8*)(Kb + (long long)gk * D + seg * SD + c * 8);
+        for (int c = 0; c < SD / 8; ++c) kraw[c] = *(const u16x8*)(krow + seg * SD + c * 8);
     }
 #pragma unroll
     for (int j = 0; j < VCH; ++j) {
         const int i = tid + 256 * j, kk = i / DC, c = i % DC;
-        vraw[j] = *(const u16x8*)(Vb + (long long)min(k0 + kk, ld_seq - 1) * D + c * 8);
+        vraw[j] = *(const u16x8*)(V + kv_row(b, kvh, min(k0 + kk, ld_seq - 1), kvl, ld_seq, D, table, bsz, max_blocks) +
+                                  c * 8);
     }
     const int nq8 = G * D / 8;                   // two chunks per thread cover G * D <= 4096
 #pragma unroll
@@ -502,6 +503,23 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
 #pragma unroll
             for (int e = 0; e < 8; ++e) st[e] = o[e];
         }
+    }
+}
+
+// Copies prefill K/V rows [B, kvl, S, d] into the pages of a paged pool.
+__global__ __launch_bounds__(256) void pages_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                    bf16* __restrict__ kpool, bf16* __restrict__ vpool, int B,
+                                                    int kvl, int S, int d, const int* __restrict__ table, int bsz,
+                                                    int max_blocks) {
+    const int dc = d / 8;
+    const long long total = (long long)B * kvl * S * dc;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+        const int c = (int)(i % dc);
+        const long long row = i / dc;                 // (b, h, p) row of the contiguous layout
+        const int p = (int)(row % S), h = (int)((row / S) % kvl), b = (int)(row / ((long long)S * kvl));
+        const long long dst = kv_row(b, h, p, kvl, 0, d, table, bsz, max_blocks) + c * 8;
+        *(u16x8*)(kpool + dst) = *(const u16x8*)(k + row * d + c * 8);
+        *(u16x8*)(vpool + dst) = *(const u16x8*)(v + row * d + c * 8);
     }
 }
 
@@ -784,7 +802,7 @@ size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d) {
 
 template <int D, int CHT>
 void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
-                        int kvl, const int* len_dev, int ld_seq, hipStream_t st) {
+                        int kvl, const int* len_dev, int ld_seq, const int* table, int bsz, int mb, hipStream_t st) {
     const int nchunks = (ld_seq + CHT - 1) / CHT;
     const int G = hl / kvl;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -792,12 +810,12 @@ void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, fl
         // LDS: q [D], scores [64], per-head partial sums [256/(D/8)][D]
         const size_t lds = ((size_t)D + 64 + (size_t)(256 / (D / 8)) * D) * sizeof(float);
         hipLaunchKernelGGL(attn_decode_chunk_mha<D>, dim3(nchunks, kvl, B), dim3(256), lds, st, q, K, V, scratch, hl,
-                           kvl, len_dev, ld_seq, scale_log2);
+                           kvl, len_dev, ld_seq, scale_log2, table, bsz, mb);
     } else {
         // LDS: queries [G][D] and scores [G][CH] fp32, values [CH][D] bf16
         const size_t lds = ((size_t)G * D + (size_t)G * CHT) * sizeof(float) + (size_t)CHT * D * sizeof(bf16);
         hipLaunchKernelGGL((attn_decode_chunk<D, CHT>), dim3(nchunks, kvl, B), dim3(256), lds, st, q, K, V, scratch,
-                           hl, kvl, len_dev, ld_seq, scale_log2);
+                           hl, kvl, len_dev, ld_seq, scale_log2, table, bsz, mb);
     }
     // long chunk lists are summed by more threads
     if (nchunks > 32)
@@ -809,16 +827,25 @@ void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, fl
 }
 
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
-                      int kvl, const int* len_dev, int ld_seq, int d, hipStream_t st) {
+                      int kvl, const int* len_dev, int ld_seq, int d, const int* table, int bsz, int mb,
+                      hipStream_t st) {
     const int ch = decode_chunk(B, hl, kvl, ld_seq, d);
     if (d == 128) {
-        if (ch == 64) launch_decode_attn<128, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
-        else if (ch == 32) launch_decode_attn<128, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
-        else launch_decode_attn<128, 16>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
+        if (ch == 64) launch_decode_attn<128, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
+        else if (ch == 32) launch_decode_attn<128, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
+        else launch_decode_attn<128, 16>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
     } else {
-        if (ch == 64) launch_decode_attn<64, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
-        else launch_decode_attn<64, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, st);
+        if (ch == 64) launch_decode_attn<64, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
+        else launch_decode_attn<64, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
     }
+}
+
+void kv_to_pages(const bf16* k, const bf16* v, bf16* kpool, bf16* vpool, int B, int kvl, int S, int d,
+                 const int* table, int bsz, int max_blocks, hipStream_t st) {
+    const long long rows = (long long)B * kvl * S;
+    const int blocks = (int)std::min<long long>((rows * (d / 8) + 255) / 256, 256LL * 8);
+    hipLaunchKernelGGL(pages_kernel, dim3(blocks), dim3(256), 0, st, k, v, kpool, vpool, B, kvl, S, d, table, bsz,
+                       max_blocks);
 }
 
 }  // namespace tp

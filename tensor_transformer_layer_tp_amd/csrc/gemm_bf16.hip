@@ -137,7 +137,9 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                     }
                     const float o1 = y1 * c - y2 * sn;
                     const float o2 = y2 * c + y1 * sn;
-                    bf16* dst = dbase + (((long long)b * nh + head) * ld + poff + s) * d;
+                    bf16* dst = dbase + (region == 0 || q.table == nullptr
+                                             ? (((long long)b * nh + head) * ld + poff + s) * d
+                                             : kv_row(b, head, pos, q.kvl, q.ld_seq, d, q.table, q.bsz, q.max_blocks));
                     if (row < M && gcol < N && (region == 0 || pos < q.ld_seq)) {
                         dst[i1] = f2bf(o1);
                         dst[i1 + half] = f2bf(o2);

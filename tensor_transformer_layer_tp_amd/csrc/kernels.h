@@ -26,7 +26,20 @@ struct QKVDest {
     int ld_seq;         // cache capacity (positions)
     const float* rope_cos;  // [max_pos, d/2] or nullptr (no rotary embedding)
     const float* rope_sin;
+    // paged cache: k/v are pools [blocks, kvl, bsz, d]; position p of sequence
+    // b lives in block table[b * max_blocks + p / bsz] at row p % bsz
+    const int* table;   // nullptr: contiguous [B, kvl, ld_seq, d]
+    int bsz, max_blocks;
 };
+
+// Address of cache row (sequence b, kv head h, position p) in a contiguous
+// cache [B, kvl, ld_seq, d] or, with a block table, in a paged pool.
+__device__ __forceinline__ long long kv_row(int b, int h, int p, int kvl, int ld_seq, int d, const int* table,
+                                            int bsz, int max_blocks) {
+    if (table == nullptr) return (((long long)b * kvl + h) * ld_seq + p) * d;
+    const int blk = table[(long long)b * max_blocks + min(p / bsz, max_blocks - 1)];   // clamped: in bounds
+    return (((long long)blk * kvl + h) * bsz + (p % bsz)) * d;
+}
 
 // Update of a device-resident cache length, done by one thread of the
 // projection that follows the last reader of the length in a stage.
@@ -85,7 +98,11 @@ void quant_rows_e4m3(const bf16* W, int N, int K, uint8_t* Q, float* scale, hipS
 // grid and the scratch are sized for ld_seq positions so that one launch
 // stays valid while the device length grows (graph replay)
 void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B,
-                      int hl, int kvl, const int* len_dev, int ld_seq, int d, hipStream_t st);
+                      int hl, int kvl, const int* len_dev, int ld_seq, int d, const int* table, int bsz,
+                      int max_blocks, hipStream_t st);
+// copy K and V [B, kvl, S, d] (contiguous) into a paged pool at positions 0..S-1
+void kv_to_pages(const bf16* k, const bf16* v, bf16* kpool, bf16* vpool, int B, int kvl, int S, int d,
+                 const int* table, int bsz, int max_blocks, hipStream_t st);
 size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d);
 // small decode batches (2..64): split-K MFMA projection + epilogue pass; part
 // is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64

@@ -56,6 +56,9 @@ struct tp_kv {
     size_t esz;
     int dtype;
     void *k, *v;
+    // paged layout: k/v are pools [num_blocks, kvl, block_size, d]; table [batch, max_blocks]
+    int* table;
+    int block_size, num_blocks, max_blocks;
 };
 
 namespace {
@@ -157,12 +160,17 @@ void fp8_shape(const tp_shard* s, int i, int* rows, int* cols) {
 }
 
 int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void* q, void* k, void* v,
-               int ld_seq, hipStream_t st, const int* pos_dev = nullptr) {
+               int ld_seq, hipStream_t st, const int* pos_dev = nullptr, const tp_kv* paged = nullptr) {
     Epilogue epi{};
     epi.mode = EPI_QKV;
     epi.qkv.S = S;
     epi.qkv.pos0 = pos0;
     epi.qkv.pos_dev = pos_dev;
+    if (paged && paged->table) {
+        epi.qkv.table = paged->table;
+        epi.qkv.bsz = paged->block_size;
+        epi.qkv.max_blocks = paged->max_blocks;
+    }
     epi.qkv.hl = s->hl;
     epi.qkv.kvl = s->kvl;
     epi.qkv.d = s->d;
@@ -448,6 +456,55 @@ int tp_kv_create(const tp_shard* s, int batch, int max_seq, tp_kv** out) {
     return TP_OK;
 }
 
+int tp_kv_create_paged(const tp_shard* s, int batch, int max_seq, int block_size, int num_blocks, tp_kv** out) {
+    if (!s || !out || batch <= 0 || max_seq <= 0 || num_blocks <= 0) return TP_E_ARG;
+    if (s->o.dtype != TP_BF16) return TP_E_ARG;
+    if (block_size < 16 || block_size > 1024 || (block_size & (block_size - 1))) return TP_E_ARG;
+    *out = nullptr;
+    tp_kv* kv = new (std::nothrow) tp_kv();
+    if (!kv) return TP_E_NOMEM;
+    kv->batch = batch;
+    kv->max_seq = max_seq;
+    kv->kvl = s->kvl;
+    kv->d = s->d;
+    kv->esz = s->esz;
+    kv->dtype = s->o.dtype;
+    kv->block_size = block_size;
+    kv->num_blocks = num_blocks;
+    kv->max_blocks = (max_seq + block_size - 1) / block_size;
+    const size_t pool = (size_t)num_blocks * s->kvl * block_size * s->d * s->esz;
+    const size_t tbytes = (size_t)batch * kv->max_blocks * sizeof(int);
+    if (hipMalloc(&kv->k, pool) != hipSuccess || hipMalloc(&kv->v, pool) != hipSuccess ||
+        hipMalloc((void**)&kv->dlen, sizeof(int)) != hipSuccess || hipMalloc((void**)&kv->table, tbytes) != hipSuccess) {
+        tp_kv_destroy(kv);
+        return TP_E_NOMEM;
+    }
+    // until a table is set, sequence b uses blocks b * max_blocks + i (block 0 past the pool)
+    std::vector<int> t0((size_t)batch * kv->max_blocks);
+    for (size_t i = 0; i < t0.size(); ++i) t0[i] = (int)(i < (size_t)num_blocks ? i : 0);
+    if (hipMemset(kv->k, 0, pool) != hipSuccess || hipMemset(kv->v, 0, pool) != hipSuccess ||
+        hipMemset(kv->dlen, 0, sizeof(int)) != hipSuccess ||
+        hipMemcpy(kv->table, t0.data(), tbytes, hipMemcpyHostToDevice) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        const int rc = hip_fail(hipGetLastError(), "paged kv init");
+        tp_kv_destroy(kv);
+        return rc;
+    }
+    *out = kv;
+    return TP_OK;
+}
+
+int tp_kv_set_block_table(tp_kv* kv, const int* host_table) {
+    if (!kv || !host_table) return TP_E_ARG;
+    if (!kv->table) return TP_E_STATE;
+    const size_t n = (size_t)kv->batch * kv->max_blocks;
+    for (size_t i = 0; i < n; ++i)
+        if (host_table[i] < 0 || host_table[i] >= kv->num_blocks) return TP_E_ARG;
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(kv->table, host_table, n * sizeof(int), hipMemcpyHostToDevice));
+    return TP_OK;
+}
+
 int tp_kv_view(tp_kv* kv, void** k, void** v) {
     if (!kv) return TP_E_ARG;
     if (k) *k = kv->k;
@@ -506,11 +563,12 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         }
         void *kd, *vd;
         int ld_seq;
-        if (kv) {
+        const bool paged = kv && kv->table;
+        if (kv && !paged) {
             kd = kv->k;
             vd = kv->v;
             ld_seq = kv->max_seq;
-        } else {
+        } else {   // no cache, or a paged one (filled from the contiguous rows below)
             kd = ws + L.kv;
             vd = ws + L.kv + (size_t)T * s->kvl * s->d * s->esz;
             ld_seq = seq;
@@ -518,6 +576,11 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         {
             KTimer kt(s, TP_K_GEMM_QKV, st);
             TRY(launch_qkv(s, xin, T, seq, 0, ws + L.q, kd, vd, ld_seq, st));
+        }
+        if (paged) {
+            kv_to_pages((const bf16*)kd, (const bf16*)vd, (bf16*)kv->k, (bf16*)kv->v, batch, s->kvl, seq, s->d,
+                        kv->table, kv->block_size, kv->max_blocks, st);
+            LAUNCH_CHECK("kv pages");
         }
         {
             KTimer kt(s, TP_K_ATTN_PREFILL, st);
@@ -595,7 +658,8 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             Epilogue epi{};
             epi.mode = EPI_QKV;
             epi.qkv = QKVDest{1, L, kv->dlen, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
-                              s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr};
+                              s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr,
+                              kv->table, kv->block_size, kv->max_blocks};
             KTimer kt(s, TP_K_GEMV_QKV, st);
             const void* g1 = s->o.rmsnorm && !prenorm ? s->g1 : nullptr;
             TRY(launch_gemv(s, x, batch, g1, s->w_qkv, s->nqkv, s->hidden, epi, ws + lay.n, ws + lay.scr, st, 0));
@@ -607,13 +671,14 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
                 xin = ws + lay.n;
             }
             KTimer kt(s, TP_K_GEMM_QKV, st);
-            TRY(launch_qkv(s, xin, batch, 1, L, qbuf, kv->k, kv->v, kv->max_seq, st, bf ? kv->dlen : nullptr));
+            TRY(launch_qkv(s, xin, batch, 1, L, qbuf, kv->k, kv->v, kv->max_seq, st, bf ? kv->dlen : nullptr, kv));
         }
         {
             KTimer kt(s, TP_K_ATTN_DECODE, st);
             if (bf)
                 attn_decode_bf16((const bf16*)qbuf, (const bf16*)kv->k, (const bf16*)kv->v, (bf16*)(ws + lay.o),
-                                 (float*)(ws + lay.scr), batch, s->hl, s->kvl, kv->dlen, kv->max_seq, s->d, st);
+                                 (float*)(ws + lay.scr), batch, s->hl, s->kvl, kv->dlen, kv->max_seq, s->d, kv->table,
+                                 kv->block_size, kv->max_blocks, st);
             else
                 attn_f32((const float*)qbuf, (const float*)kv->k, (const float*)kv->v, (float*)(ws + lay.o), batch,
                          s->hl, s->kvl, 1, L, kv->max_seq, s->d, st);
@@ -804,6 +869,7 @@ void tp_kv_destroy(tp_kv* kv) {
     if (kv->k) (void)hipFree(kv->k);
     if (kv->v) (void)hipFree(kv->v);
     if (kv->dlen) (void)hipFree(kv->dlen);
+    if (kv->table) (void)hipFree(kv->table);
     delete kv;
 }
 

@@ -179,3 +179,19 @@ def test_sequence_parallel_argument_rules():
     assert lib.tp_shard_norm(h, 3, fake, 4, fake, None) == N.TP_E_ARG
     assert lib.tp_shard_norm(h, 1, fake, 4, fake, None) == N.TP_E_STATE             # no weights yet
     lib.tp_shard_destroy(h)
+
+
+def test_paged_cache_argument_rules():
+    """Paged caches need a bf16 shard and a power-of-two block size in [16, 1024]."""
+    lib = N.lib()
+    h, kv = C.c_void_p(), C.c_void_p()
+    assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, None, C.byref(h)) == N.TP_OK
+    for bs in (0, 8, 24, 2048):
+        assert lib.tp_kv_create_paged(h, 1, 64, bs, 16, C.byref(kv)) == N.TP_E_ARG
+    assert lib.tp_kv_create_paged(h, 1, 64, 16, 0, C.byref(kv)) == N.TP_E_ARG
+    assert lib.tp_kv_set_block_table(None, None) == N.TP_E_ARG
+    lib.tp_shard_destroy(h)
+    f32 = N.tp_opts(N.TP_F32, N.TP_ACT_SWIGLU, 1, 1e-5, 1, 10000.0, 0)
+    assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, C.byref(f32), C.byref(h)) == N.TP_OK
+    assert lib.tp_kv_create_paged(h, 1, 64, 16, 16, C.byref(kv)) == N.TP_E_ARG
+    lib.tp_shard_destroy(h)

@@ -399,6 +399,53 @@ def test_fp8_decode_matches_oracle(hidden, heads, kv, ffn, tp, r):
     assert_close(to_np(p3), ref3["partial"], "batch-3 decode on the fp8 shard", "bf16")
 
 
+@pytest.mark.parametrize("hidden,heads,kv,ffn,B,bs", [
+    (1024, 8, 4, 2816, 3, 16),    # split-K projections, GQA (G = 2), 16-position blocks
+    (1024, 8, 8, 2816, 1, 32),    # GEMV, one query head per KV head
+    (512, 8, 4, 1536, 70, 64),    # GEMM projection path, head_dim 64
+])
+def test_paged_cache_matches_contiguous(hidden, heads, kv, ffn, B, bs):
+    """Prefill into a paged cache with a scrambled block table, then decode
+    steps: every partial equals the contiguous cache's bit for bit, and the
+    pages gathered through the table hold the contiguous cache's rows."""
+    announce(f"paged KV cache B={B} block {bs}, heads {heads}/{kv}")
+    S, steps, tp, r = 40, 3, 2, 1
+    L = Layer(hidden, heads, kv, ffn, batch=B, seq=S + steps, gamma_noise=True, seed=71)
+    sh = L.shard(tp, r)
+    cap = S + steps + 5
+    mb = -(-cap // bs)
+    nblocks = B * mb + 7
+    perm = np.random.default_rng(72).permutation(nblocks)[:B * mb].reshape(B, mb)
+    kvc = sh.kv_cache(B, cap)
+    kvp = sh.kv_cache_paged(B, cap, bs, nblocks)
+    kvp.set_block_table(perm)
+    pre = L.dev["x"][:, :S].contiguous()
+    a = sh.prefill(ATTN, pre, kvc).clone()
+    b = sh.prefill(ATTN, pre, kvp).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for i in range(steps):
+        xi = L.dev["x"][:, S + i].contiguous()
+        pc = sh.decode(ATTN, xi, kvc).clone()
+        pp = sh.decode(ATTN, xi, kvp).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(pc, pp), f"decode step {i}: paged partial differs"
+    assert kvp.length == S + steps
+    kc, vc = kvc.read()
+    kp, vp = kvp.read()
+    torch.cuda.synchronize()
+    n = S + steps
+    for bb in range(B):
+        for p in sorted({0, min(bs - 1, n - 1), min(bs, n - 1), n - 1}):
+            blk, off = perm[bb, p // bs], p % bs
+            assert torch.equal(kp[blk, :, off], kc[bb, :, p]) and torch.equal(vp[blk, :, off], vc[bb, :, p])
+    # the contiguous twin against the oracle at the last step
+    x = L.exact["x"]
+    ref_pre = O.attn_stage(x[:, :S + steps - 1], L.W, L.spec, tp, r)
+    ref = O.decode_attn_stage(x[:, S + steps - 1], ref_pre["k"], ref_pre["v"], L.W, L.spec, tp, r)
+    assert_close(to_np(pp), ref["partial"], "paged decode vs oracle", "bf16")
+
+
 def test_decode_equals_prefill_row():
     """Same math both ways: decode of token L after a prefill of L tokens
     equals row L of a prefill over L+1 tokens (GPU against GPU, then both
