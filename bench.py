@@ -644,7 +644,8 @@ def cpu_model():
 TRAFFIC_KERNELS = {
     "gemm_up_7b_t2": ("gemm_bf16.hip", r"gemm_\w+_kernel<[^>]*, 2>",
                       2 * (2048 * 4096 + 11008 * 4096 + 2048 * 5504)),
-    "gemv_up_7b_t4": ("decode.hip", r"gemv_kernel<[^>]*, 2, true>", 2 * (5504 * 4096 + 4096 + 2752)),
+    "gemv_up_7b_t4": ("decode.hip", r"gemv_kernel<1, \d+, \d+, 2, true, false, \d+>",
+                      2 * (5504 * 4096 + 4096 + 2752)),
 }
 
 
@@ -675,9 +676,15 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
         factor = calib / statistics.median(copies)
         facts[counter] = factor
         for key, (_, pat, _) in TRAFFIC_KERNELS.items():
-            vals = [float(r["Counter_Value"]) * 1024 * factor for r in rs if re.search(pat, r["Kernel_Name"])]
-            if vals:
-                traffic.setdefault(key, {})[counter] = (statistics.mean(vals), len(vals))
+            # one projection may run as several launches (a column split): bytes per
+            # projection = all matching dispatches / dispatches of one launch kind
+            names = {}
+            for r in rs:
+                if re.search(pat, r["Kernel_Name"]):
+                    names.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024 * factor)
+            if names:
+                calls = max(len(v) for v in names.values())
+                traffic.setdefault(key, {})[counter] = (sum(sum(v) for v in names.values()) / calls, calls)
     rec = {}
     for key, (src, pat, alg) in TRAFFIC_KERNELS.items():
         if key not in traffic or len(traffic[key]) != 2:
@@ -702,16 +709,23 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
         md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     live = []
-    for k in ("roofline",):
-        live.append(f"- prefill roofline kernel ({line[k]['kernel']}): live HIP-event average "
-                    f"{line[k]['avg_us']} µs over {line[k]['launches']} launches")
+    up = [r for r in stats if re.search(TRAFFIC_KERNELS["gemm_up_7b_t2"][1], r["Name"])]
+    rocprof_up = sum(float(r["AverageNs"]) for r in up) / 1e3
+    kinds = [re.search(r"gemm_\w+_kernel<[^>]*>", r["Name"]).group(0) for r in up]
+    live.append(f"- prefill roofline kernel ({line['roofline']['kernel']}): live HIP-event average "
+                f"{line['roofline']['avg_us']} µs over {line['roofline']['launches']} projections; rocprof: "
+                f"{rocprof_up:.1f} µs, the sum of the averages of its {len(up)} launch kind(s) "
+                f"({', '.join(kinds)})")
     if "decode" in line:
         dk = line["decode"]["kernels"].get("gemv_up")
-        if dk:
+        gv = [r for r in stats if re.search(TRAFFIC_KERNELS["gemv_up_7b_t4"][1], r["Name"])]
+        if dk and gv:
             live.append(f"- decode roofline kernel ({line['decode']['roofline']['kernel']}): live HIP-event "
-                        f"average {dk['avg_us']} µs over {dk['launches']} launches (events add ~1 µs)")
+                        f"average {dk['avg_us']} µs over {dk['launches']} launches; rocprof "
+                        f"{float(gv[0]['AverageNs']) / 1e3:.1f} µs (events bracketing every short kernel "
+                        f"under the tracer inflate the live figure)")
     with open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w") as fh:
-        fh.write("# Kernel durations of `bench.py --no-cpu` (rocprofv3 --kernel-trace --stats)\n\n")
+        fh.write("# Kernel durations of `bench.py --no-cpu --no-70b` (rocprofv3 --kernel-trace --stats)\n\n")
         fh.write("Commands: see profiles/README.md.  Bench line of the same run:\n\n")
         fh.write("\n".join(live) + "\n\n" + "\n".join(md) + "\n")
     print(json.dumps(rec, indent=1))
