@@ -49,7 +49,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--decode-layers", type=int, default=0,
                     help="layer copies in the decode stack (0: enough for >= 1 GB of weights)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

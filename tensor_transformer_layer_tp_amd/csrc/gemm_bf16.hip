@@ -25,6 +25,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tp {
 
 namespace {
@@ -432,6 +434,178 @@ __global__ __launch_bounds__(256) void gemm_dma_pipe_kernel(const bf16* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Register-pipelined main loop for 64-k tiles: plain 16-byte buffer loads
+// into two register sets (each tile is requested two tiles before its MFMAs),
+// ds_write into a double-buffered LDS stage.  On gfx950 vector loads into
+// registers stream this tile traffic about 1.5x faster than the LDS DMA path,
+// and a 64-k tile reads whole 128-byte lines of every row.
+//
+// Tile kt (4 k-slices) uses LDS stage kt % 2 and register set kt % 2:
+//  slice 0: loads of tile kt+2 into set kt % 2 (its tile was written to LDS
+//           at the end of tile kt-1), interleaved with the MFMAs;
+//  slice 3: set (kt+1) % 2 is written to stage (kt+1) % 2 between the first
+//           MFMAs, then the barrier publishes it, the first fragments of tile
+//           kt+1 are read, and the remaining MFMAs of the slice cover that read.
+// Stage (kt+1) % 2 last held tile kt-1, whose reads all completed before the
+// barrier at the end of tile kt-1.
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __restrict__ A, long long lda,
+                                                                 const bf16* __restrict__ B, long long ldb, int M,
+                                                                 int N, int K, Epilogue epi, int tiles_m,
+                                                                 int tiles_n) {
+    constexpr int NT = 64 * WM * WN;            // threads
+    constexpr int BK = 64, KK = 4;
+    constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+    constexpr int RS = NT / 8;                   // rows per load step (8 chunks per 64-k row)
+    constexpr int CA = BM / RS, CB = BN / RS;    // 16-byte chunks per thread per tile
+    constexpr int STAGE = (BM + BN) * BK;
+    static_assert(FN % 2 == 0 && BM % RS == 0 && BN % RS == 0, "tile shape");
+    __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    if (blockIdx.x == 0 && threadIdx.x == 0) apply_len_update(epi.len);
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // thread t copies 16-byte chunk (t & 7) of tile rows (t >> 3) + RS i.  Each
+    // row step i has a buffer resource of its own (scalar registers) covering
+    // only its rows, so one vector offset serves every load and rows past M
+    // (or N) read as zeros.
+    const int srow = tid >> 3, skc = tid & 7;
+    __amdgpu_buffer_rsrc_t rsa[CA], rsb[CB];
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+        rsa[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long long)(m0 + i * RS) * lda), (short)0,
+                                                   max(0, min(RS, M - m0 - i * RS)) * (int)lda * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+        rsb[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (long long)(n0 + i * RS) * ldb), (short)0,
+                                                   max(0, min(RS, N - n0 - i * RS)) * (int)ldb * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, 0x00020000);
+    const int va0 = (srow * (int)lda + skc * 8) * 2;
+    const int vb0 = (srow * (int)ldb + skc * 8) * 2;
+    const int l0 = srow * BK + (swz<8>(srow, skc) << 3);   // rows srow + RS i share the swizzle
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
+
+    const int KT = K / BK;
+    const int frow = lane & 31, khalf = lane >> 5;
+    u32x4 ra[2][CA], rb[2][CB];
+    bf16x8 fa[2][FM], fb[2][FN];
+
+    // Quarter q (of four) of the loads of tile kt into register set `set`:
+    // each k-slice of a tile issues one quarter, so the CU's 16-byte loads are
+    // spread evenly over the MFMA time instead of queueing up in one slice.
+    constexpr int NL = CA + CB, QL = (NL + 3) / 4;
+    auto gload = [&](auto set, int kt, int q) {
+        // a tile past the end reads zeros through an empty resource
+        const bool in = kt < KT;
+        const int koff = in ? kt * BK * 2 : 0;
+#pragma unroll
+        for (int j = q * QL; j < min(NL, (q + 1) * QL); ++j) {
+            if (j < CA) ra[set][j] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsa[j] : rs0, va0, koff, 0);
+            else rb[set][j - CA] = __builtin_amdgcn_raw_buffer_load_b128(in ? rsb[j - CA] : rs0, vb0, koff, 0);
+        }
+    };
+    auto lstore = [&](auto set, int stage) {
+        bf16* sa = smem + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) *(u32x4*)(sa + l0 + i * RS * BK) = ra[set][i];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) *(u32x4*)(sa + BM * BK + l0 + i * RS * BK) = rb[set][i];
+    };
+    auto read = [&](int stage, int kk, int buf) {
+        const bf16* a_s = smem + stage * STAGE + (wm * TM + frow) * BK;
+        const bf16* b_s = smem + stage * STAGE + BM * BK + (wn * TN + frow) * BK;
+        const int c = swz<8>(frow, 2 * kk + khalf) << 3;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
+    };
+    auto mma = [&](int buf, int i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
+
+    // One tile.  SET = kt % 2.  Slices 0-2: a quarter of the loads of tile
+    // kt+2, the fragments of the next slice, this slice's MFMAs.  Slice 3:
+    // write tile kt+1 to the other stage, publish it, read its first
+    // fragments and issue the last quarter of the loads under the remaining
+    // MFMAs.
+    auto tile = [&](auto set, int kt) {
+        constexpr int S = decltype(set)::value;
+        const int stage = S;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < KK) {
+                gload(set, kt + 2, kk);
+                read(stage, kk + 1, nxt);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) mma(cur, i);
+#pragma unroll
+                for (int q = 0; q < FM * FN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);   // VMEM read
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                lstore(std::integral_constant<int, 1 - S>{}, 1 - S);
+#pragma unroll
+                for (int i = 0; i < FM / 2; ++i) mma(cur, i);
+#pragma unroll
+                for (int q = 0; q < NL; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x0200, 1, 0);   // DS write
+                    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                read(1 - S, 0, nxt);
+                gload(set, kt + 2, 3);
+#pragma unroll
+                for (int i = FM / 2; i < FM; ++i) mma(cur, i);
+#pragma unroll
+                for (int q = 0; q < FM * FN / 2; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);   // VMEM read
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    using T0 = std::integral_constant<int, 0>;
+    using T1 = std::integral_constant<int, 1>;
+
+    // An odd tile count runs one all-zero tile more: the loop body stays free
+    // of branches (a tail with its own control flow makes the compiler spill
+    // the accumulators).  The last pair also writes and publishes a tile that
+    // no MFMA reads.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload(T0{}, 0, q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload(T1{}, 1, q);
+    lstore(T0{}, 0);
+    __syncthreads();
+    read(0, 0, 0);
+    for (int kt = 0; kt < KT; kt += 2) {
+        tile(T0{}, kt);
+        tile(T1{}, kt + 1);
+    }
+    epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+}
+
+// ---------------------------------------------------------------------------
 // Register-staged main loop (two register stages, double-buffered LDS, BK 64).
 template <int BM, int BN, int MODE>
 __global__ __launch_bounds__(256) void gemm_reg_kernel(const bf16* __restrict__ A, long long lda,
@@ -521,7 +695,7 @@ struct Cfg {
     float eff;   // relative MFMA efficiency of one work-group (measured on the 7B/70B shapes)
     int occ;     // work-groups per CU
 };
-// index: 0-2 register-staged, 3-8 DMA ring
+// index: 0-2 register-staged, 3-10 DMA ring, 11-12 register-pipelined
 const Cfg kCfgs[] = {
     {256, 128, 0.86f, 1},  // 0 reg 256x128
     {128, 128, 0.90f, 2},  // 1 reg 128x128
@@ -534,6 +708,8 @@ const Cfg kCfgs[] = {
     {256, 128, 0.85f, 1},  // 8 dma 256x128 BK32 ST4
     {128, 384, 0.95f, 1},  // 9 dma 128x384 BK32 ST4
     {128, 384, 0.95f, 1},  // 10 dma 128x384 BK32 ST3
+    {256, 256, 1.08f, 1},  // 11 register-pipelined 256x256 BK64, 8 waves
+    {256, 128, 1.02f, 1},  // 12 register-pipelined 256x128 BK64, 8 waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -560,6 +736,12 @@ void launch_pipe(const Args& a) {
     hipLaunchKernelGGL((gemm_dma_pipe_kernel<BM, BN, BK, ST, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda,
                        a.B, a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
 }
+template <int BM, int BN, int WM, int WN, int MODE>
+void launch_vgpr(const Args& a) {
+    const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    hipLaunchKernelGGL((gemm_vgpr_kernel<BM, BN, WM, WN, MODE>), dim3(tm * tn), dim3(64 * WM * WN), 0, a.st, a.A,
+                       a.lda, a.B, a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
+}
 template <int BM, int BN, int MODE>
 void launch_reg(const Args& a) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
@@ -580,26 +762,31 @@ void launch_cfg(int c, const Args& a) {
         case 7: launch_dma<128, 128, 64, 2, MODE>(a); break;
         case 8: launch_pipe<256, 128, 32, 4, MODE>(a); break;
         case 9: launch_pipe<128, 384, 32, 4, MODE>(a); break;
-        default: launch_pipe<128, 384, 32, 3, MODE>(a); break;
+        case 10: launch_pipe<128, 384, 32, 3, MODE>(a); break;
+        case 11: launch_vgpr<256, 256, 2, 4, MODE>(a); break;
+        default: launch_vgpr<256, 128, 4, 2, MODE>(a); break;
     }
 }
 
-// The two-stage 256x256 DMA kernel holds 256 accumulators per lane and
-// spills them with the rotary, erf and plain-store epilogues.
+// The 256x256 DMA kernels hold 256 accumulators per lane: the two-stage one
+// spills them with the rotary, erf and plain-store epilogues, the four-stage
+// ring with the rotary one.
 bool usable(int c, int mode) {
-    return !(c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE));
+    if (c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE)) return false;
+    return !(c == 4 && mode == EPI_QKV);
 }
 
 // Modelled time of one launch: rounds of 256 tiles (one per CU), each the
 // tile's FLOPs at the configuration's per-CU rate, plus a launch.  The DMA
-// rings lose 20% with the rotary epilogue (measured on the 7B Q/K/V shape).
+// rings lose 20% with the rotary epilogue (measured on the 7B Q/K/V shape);
+// the register-pipelined kernels do not.
 constexpr double kCuFlopPerUs = 4.7e6;   // per-CU bf16 rate of a configuration with eff = 1
 constexpr double kLaunchUs = 3.0;
 
 double model_us(int c, int mode, int M, int N, int K) {
     const Cfg& f = kCfgs[c];
     const long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
-    const double eff = f.eff * ((c >= 3 && mode == EPI_QKV) ? 0.8 : 1.0);
+    const double eff = f.eff * ((c >= 3 && c <= 10 && mode == EPI_QKV) ? 0.8 : 1.0);
     return kLaunchUs + (double)((tiles + 255) / 256) * 2.0 * f.bm * f.bn * K / (eff * kCuFlopPerUs);
 }
 
