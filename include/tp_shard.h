@@ -291,12 +291,23 @@ int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *l
 /* tp_tune_set_gemm_config -- tuning hook: force the projection GEMM's tile
  * configuration for every later call in this process, or -1 to restore the
  * shape-based choice.  0..2: register-staged 256x128, 128x128, 128x256
- * output tiles; 3..8: direct-to-LDS rings 256x256 (K-step 64, 2 stages),
+ * output tiles; 3..10: direct-to-LDS rings 256x256 (K-step 64, 2 stages),
  * 256x256 (32, 4), 256x128 (64, 3), 128x128 (64, 4), 128x128 (64, 2),
- * 256x128 (32, 4).  A configuration that a projection cannot use (256x256
- * with the rotary or GELU epilogue) falls back to the shape-based choice.
+ * 256x128 (32, 4), 128x384 (32, 4), 128x384 (32, 3); 11..12: register-
+ * pipelined 256x256 and 256x128 (K-step 64, eight waves).  A configuration
+ * that a projection cannot use (the 256x256 DMA rings with the rotary
+ * epilogue, the two-stage one also with the GELU and plain-store ones)
+ * falls back to the shape-based choice.  Process-wide, not thread-safe.
  * TP_E_ARG if out of range. */
 int tp_tune_set_gemm_config(int cfg);
+
+/* tp_tune_set_attn_groups -- tuning hook for prefill attention: 1 runs each
+ * 128-query block with one group of four waves over all its key blocks, 2
+ * with two groups over alternate key blocks whose softmax states merge at
+ * the end (same result up to rounding order), 0 restores the choice by grid
+ * size (two groups up to 512 work-groups).  Process-wide, not thread-safe.
+ * TP_E_ARG outside 0..2. */
+int tp_tune_set_attn_groups(int kg);
 
 void tp_shard_destroy(tp_shard *s);
 void tp_kv_destroy(tp_kv *kv);

@@ -367,3 +367,8 @@ def all_gather(pieces, out: torch.Tensor | None = None, stream=None) -> torch.Te
 def set_gemm_config(cfg: int) -> None:
     """Tuning hook: force a projection tile configuration (-1 = automatic)."""
     N.check(N.lib().tp_tune_set_gemm_config(int(cfg)), "tp_tune_set_gemm_config")
+
+
+def set_attn_groups(kg: int) -> None:
+    """Tuning hook: prefill attention key groups (0 = automatic, 1 or 2)."""
+    N.check(N.lib().tp_tune_set_attn_groups(int(kg)), "tp_tune_set_attn_groups")

@@ -5,8 +5,8 @@
 // Original" and "What Undercode Say": heads are independent, so the
 // column-parallel split of Q/K/V needs no communication inside attention).
 //
-// Work-group = 4 waves = 128 queries of one (batch, head); each wave owns 32
-// queries.  Keys stream through LDS in blocks of 64.  The wave computes the
+// Work-group = 4 waves (or 2 x 4, see below) = 128 queries of one (batch,
+// head); each wave owns 32 queries.  Keys stream through LDS in blocks of 64.  The wave computes the
 // transposed score tile S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K block as
 // the A operand from LDS, the wave's Q fragment held in registers as the B
 // operand), so that every lane owns ONE query column: the online-softmax
@@ -40,23 +40,38 @@ __device__ __forceinline__ int kslot(int r, int c) {
     return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                                                           const bf16* __restrict__ V, bf16* __restrict__ O,
-                                                           int hl, int kvl, int S, int ld_seq, float scale_log2) {
+// KG key groups of 4 waves: group g takes the key blocks kb = g (mod KG) for
+// the same 128 queries, with its own LDS buffers and online-softmax state;
+// the states merge through LDS at the end.  KG = 2 halves the critical path
+// of the longest (latest) query blocks and puts two waves on each SIMD when
+// the grid alone would give one.
+template <int D, int KG>
+__global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
+    int hl, int kvl, int S, int ld_seq, float scale_log2) {
     constexpr int KC = D / 8;        // 16-byte chunks per K row
     constexpr int NT = D / 32;       // O^T tiles (32 dims each)
     constexpr int KSTEPS = D / 16;   // k16 steps of the QK^T contraction
-    __shared__ __attribute__((aligned(16))) bf16 sK[BKV * D];
-    __shared__ __attribute__((aligned(16))) bf16 sVt[D * BKV];
+    constexpr int BUF = 2 * BKV * D;                      // bf16 per group: K block + transposed V block
+    // staging row (bf16): padded against bank conflicts where the registers
+    // allow it (the one-group kernel spills with the padded addressing)
+    constexpr int OROW = KG > 1 ? D + 8 : D;
+    constexpr int MERGE = (KG > 1 ? 4 * NT * 16 * 64 + 2 * 256 : 0) * 2;   // fp32 merge area, in bf16 units
+    constexpr int STAGE_O = 4 * 32 * OROW;
+    constexpr int SMEM = (KG * BUF > MERGE ? (KG * BUF > STAGE_O ? KG * BUF : STAGE_O)
+                                           : (MERGE > STAGE_O ? MERGE : STAGE_O));
+    __shared__ __attribute__((aligned(16))) bf16 smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = KG > 1 ? wave >> 2 : 0, qw = KG > 1 ? wave & 3 : wave, gtid = KG > 1 ? tid & 255 : tid;
+    bf16* sK = smem + grp * BUF;
+    bf16* sVt = sK + BKV * D;
     const int h = lane >> 5, col = lane & 31;
     const int nqb = (S + BQ - 1) / BQ;
     const int qb = nqb - 1 - (int)blockIdx.x;  // longest (latest) query blocks first
     const int head = blockIdx.y, b = blockIdx.z;
     const int kvh = head / (hl / kvl);
-    const int q0 = qb * BQ + wave * 32;
+    const int q0 = qb * BQ + qw * 32;
     const int qme = q0 + col;                  // this lane's query
 
     const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
@@ -77,10 +92,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16* __rest
 
     const int kv_end = min(S, qb * BQ + BQ);
     const int nkb = (kv_end + BKV - 1) / BKV;
+    const int nit = (nkb + KG - 1) / KG;
 
-    // Block kb + 1 is fetched into registers while block kb is computed from
-    // LDS.  Rows past the sequence are clamped to row S-1 (read, never used),
-    // so every load is issued unconditionally and stays in bounds.
+    // The group's next block is fetched into registers while its current one
+    // is computed from LDS.  Rows past the sequence are clamped to row S-1
+    // (read, never used), so every load is issued unconditionally and stays
+    // in bounds.
     constexpr int KLD = BKV * KC / 256;         // K chunks per thread
     constexpr int VLD = (BKV / 2) * KC / 256;   // V key pairs per thread
     bf16x8 kreg[KLD];
@@ -88,34 +105,34 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16* __rest
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = gtid + 256 * i;
             const int gk = min(k0 + idx / KC, S - 1);
             kreg[i] = *(const bf16x8*)(Kb + (long long)gk * D + (idx % KC) * 8);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = gtid + 256 * i;
             const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
             const int g0 = min(k0 + 2 * a, S - 1), g1 = min(k0 + 2 * a + 1, S - 1);
             vreg[i][0] = *(const u16x8*)(Vb + (long long)g0 * D + dc * 8);
             vreg[i][1] = *(const u16x8*)(Vb + (long long)g1 * D + dc * 8);
         }
     };
-    fetch(0);
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int k0 = kb * BKV;
+    fetch(grp * BKV);
+    for (int it = 0; it < nit; ++it) {
+        const int k0 = (it * KG + grp) * BKV;
         __syncthreads();
         // K block -> LDS [key][dim], chunk swizzled by key
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = gtid + 256 * i;
             const int key = idx / KC, dc = idx % KC;
             *(bf16x8*)(sK + key * D + (kslot<KC>(key, dc) << 3)) = kreg[i];
         }
         // V block -> LDS transposed [dim][permuted key], two keys per 32-bit store
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = gtid + 256 * i;
             const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
             const u16x8 v0 = vreg[i][0], v1 = vreg[i][1];
             const int p = vt_pos(2 * a);
@@ -132,9 +149,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16* __rest
             }
         }
         __syncthreads();
-        fetch(k0 + BKV);
+        fetch(k0 + KG * BKV);
         if (k0 > q0 + 31) continue;  // every key of this block is after every query of the wave
-
         // S^T tile: keys (32t + row) x this wave's 32 queries
         f32x16 st[2];
 #pragma unroll
@@ -200,40 +216,96 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16* __rest
         }
     }
 
-    // normalise and store through LDS so that the global writes are whole rows
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = 1.f / l_tot;
-    __syncthreads();
-    bf16* sO = (tid < 128 ? sK : sVt) + (wave & 1) * 32 * D;  // 32 queries x D per wave
+    if constexpr (KG > 1) {
+        // group 1 hands its state to group 0 through LDS: the same (wave,
+        // lane) slot holds the same query and dims in both groups
+        float* mo = (float*)smem;
+        float* mm = mo + 4 * NT * 16 * 64;
+        float* ml = mm + 256;
+        __syncthreads();   // every group is done with its K/V buffers
+        if (grp == 1) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
+            for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int dim = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-            sO[col * D + dim] = f2bf(oacc[i][r] * inv);
+                for (int r = 0; r < 16; ++r) mo[((qw * NT + i) * 16 + r) * 64 + lane] = oacc[i][r];
+            mm[qw * 64 + lane] = m_run;
+            ml[qw * 64 + lane] = l_run;
         }
-    __syncthreads();
-    const long long ldo = (long long)hl * D;
+        __syncthreads();
+        if (grp == 0) {
+            const float m1 = mm[qw * 64 + lane], l1 = ml[qw * 64 + lane];
+            const float m = fmaxf(m_run, m1);   // group 0 always saw key 0: m_run is finite
+            const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+            l_run = l_run * a0 + l1 * a1;
 #pragma unroll
-    for (int i = 0; i < 32 * KC / 64; ++i) {
-        const int idx = lane + 64 * i;
-        const int qr = idx / KC, dc = idx % KC;
-        const int q = q0 + qr;
-        if (q < S) *(bf16x8*)(O + ((long long)b * S + q) * ldo + head * D + dc * 8) = *(const bf16x8*)(sO + qr * D + dc * 8);
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[i][r] = oacc[i][r] * a0 + mo[((qw * NT + i) * 16 + r) * 64 + lane] * a1;
+        }
+        __syncthreads();   // the staging below reuses the merge area
+    } else {
+        __syncthreads();   // the staging below reuses the K/V buffers
+    }
+
+    // normalise and store through LDS so that the global writes are whole rows
+    if (grp == 0) {
+        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        const float inv = 1.f / l_tot;
+        bf16* sO = smem + qw * 32 * OROW;   // 32 queries x D per wave
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dim = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                sO[col * OROW + dim] = f2bf(oacc[i][r] * inv);
+            }
+    }
+    __syncthreads();
+    if (grp == 0) {
+        const bf16* sO = smem + qw * 32 * OROW;
+        const long long ldo = (long long)hl * D;
+#pragma unroll
+        for (int i = 0; i < 32 * KC / 64; ++i) {
+            const int idx = lane + 64 * i;
+            const int qr = idx / KC, dc = idx % KC;
+            const int q = q0 + qr;
+            if (q < S)
+                *(bf16x8*)(O + ((long long)b * S + q) * ldo + head * D + dc * 8) = *(const bf16x8*)(sO + qr * OROW + dc * 8);
+        }
     }
 }
 
+int g_attn_groups = 0;   // 0: by grid size; 1 or 2: forced
+
 }  // namespace
+
+void set_attn_groups(int kg) { g_attn_groups = kg; }
 
 void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl, int S,
                        int ld_seq, int d, hipStream_t st) {
     if (B <= 0 || S <= 0) return;
     dim3 grid((S + BQ - 1) / BQ, hl, B);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
-    if (d == 128)
-        hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq, scale_log2);
-    else
-        hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq, scale_log2);
+    // Two key groups while the grid alone leaves a SIMD with at most one wave
+    // (two 4-wave work-groups fit a CU): up to 512 work-groups.
+    const long long wgs = (long long)grid.x * grid.y * grid.z;
+    const int kg = g_attn_groups ? g_attn_groups : (wgs <= 512 ? 2 : 1);
+    if (d == 128) {
+        if (kg == 2)
+            hipLaunchKernelGGL((attn_prefill_kernel<128, 2>), grid, dim3(512), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
+                               scale_log2);
+        else
+            hipLaunchKernelGGL((attn_prefill_kernel<128, 1>), grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
+                               scale_log2);
+    } else {
+        if (kg == 2)
+            hipLaunchKernelGGL((attn_prefill_kernel<64, 2>), grid, dim3(512), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
+                               scale_log2);
+        else
+            hipLaunchKernelGGL((attn_prefill_kernel<64, 1>), grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
+                               scale_log2);
+    }
 }
 
 }  // namespace tp

@@ -86,6 +86,7 @@ void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st);
 void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl,
                        int S, int ld_seq, int d, hipStream_t st);
+void set_attn_groups(int kg);   // prefill attention key groups: 0 automatic, 1 or 2 forced
 // decode GEMV for B <= 4 sequences (K <= 16384, N a multiple of 64)
 void gemv_bf16(const bf16* x, int B, const bf16* gamma, float eps, const bf16* W, int N, int K,
                const Epilogue& epi, hipStream_t st);

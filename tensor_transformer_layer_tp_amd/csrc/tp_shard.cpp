@@ -853,6 +853,12 @@ int tp_tune_set_gemm_config(int cfg) {
     return TP_OK;
 }
 
+int tp_tune_set_attn_groups(int kg) {
+    if (kg < 0 || kg > 2) return TP_E_ARG;
+    set_attn_groups(kg);
+    return TP_OK;
+}
+
 void tp_shard_destroy(tp_shard* s) {
     if (!s) return;
     for (hipEvent_t e : s->ev)

@@ -140,6 +140,9 @@ def test_tune_hook_range():
     lib = N.lib()
     assert lib.tp_tune_set_gemm_config(99) == N.TP_E_ARG
     assert lib.tp_tune_set_gemm_config(-1) == N.TP_OK
+    assert lib.tp_tune_set_attn_groups(3) == N.TP_E_ARG
+    assert lib.tp_tune_set_attn_groups(-1) == N.TP_E_ARG
+    assert lib.tp_tune_set_attn_groups(0) == N.TP_OK
 
 
 def test_fp8_option_rules():

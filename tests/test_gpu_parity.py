@@ -127,6 +127,30 @@ def test_bf16_layer_ragged_gqa_two_ranks():
     assert_close(to_np(o), ref["o"].transpose(0, 2, 1, 3).reshape(600, 512), "attention output o", "bf16")
 
 
+@pytest.mark.parametrize("kg", [1, 2])
+@pytest.mark.parametrize("hidden,heads,kv,S", [(1024, 8, 4, 300), (512, 8, 2, 130)])
+def test_attention_key_groups(kg, hidden, heads, kv, S):
+    """Prefill attention with one group of waves over every key block and
+    with two groups over alternate key blocks whose softmax states merge,
+    forced in turn (head dims 128 and 64, GQA, ragged S), against the
+    oracle's attention output."""
+    from tensor_transformer_layer_tp_amd import set_attn_groups
+    announce(f"attention key groups kg={kg} hidden={hidden} heads={heads}/{kv} S={S}")
+    t, r, B = 2, 1, 2
+    L = Layer(hidden, heads, kv, 2 * hidden, batch=B, seq=S, gamma_noise=True, seed=21)
+    ref = O.attn_stage(L.exact["x"], L.W, L.spec, t, r)
+    sh = L.shard(t, r)
+    hl, d = heads // t, hidden // heads
+    try:
+        set_attn_groups(kg)
+        sh.prefill(ATTN, L.dev["x"])
+        o = sh.debug_tensor("o", (B * S, hl * d))
+        torch.cuda.synchronize()
+    finally:
+        set_attn_groups(0)
+    assert_close(to_np(o), ref["o"].transpose(0, 2, 1, 3).reshape(B * S, hl * d), f"attention o kg={kg}", "bf16")
+
+
 def test_bf16_head_dim_64_unsharded():
     announce("bf16 layer head_dim 64, t=1, B=1, S=130")
     L = Layer(512, 8, 2, 1024, batch=1, seq=130, gamma_noise=True, seed=2)
