@@ -99,13 +99,12 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
         valid[i] = c < KC;
         cofs[i] = min(c, KC - 1);   // clamped: every load is issued and in bounds
     }
-    u32x4 wv[R][NI];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const char* wrow = W + (long long)(rbase + (r < P ? r : 32 + r - P)) * row_bytes;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) wv[r][i] = *(const u32x4*)(wrow + 16LL * cofs[i]);
-    }
+    // Activation (and gain) loads first, then every weight load, and nothing
+    // scheduled above the last weight load: the norm below then waits only
+    // for the activations (the memory counter retires in issue order) while
+    // the weights stream in.  Left to itself the scheduler hoists activation
+    // arithmetic between the loads and waits for the activations before the
+    // first weight load, which costs one whole memory latency per work-group.
     u16x8 xv[NB][NI][XC];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -113,14 +112,24 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
         for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int h = 0; h < XC; ++h) xv[b][i][h] = *(const u16x8*)(x + (long long)b * K + cofs[i] * CW + 8 * h);
-
-    float rs[NB];
     u16x8 gv[NI][XC];
     if constexpr (NORM) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int h = 0; h < XC; ++h) gv[i][h] = *(const u16x8*)(gamma + cofs[i] * CW + 8 * h);
+    }
+    u32x4 wv[R][NI];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const char* wrow = W + (long long)(rbase + (r < P ? r : 32 + r - P)) * row_bytes;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wv[r][i] = *(const u32x4*)(wrow + 16LL * cofs[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    float rs[NB];
+    if constexpr (NORM) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float ss = 0.f;
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
                         const float f = bfbits2f(xv[b][i][h][e]);
                         ss += valid[i] ? f * f : 0.f;
                     }
-            ss = wave_sum(ss);
+            ss = wave_sum_dpp(ss);
             if (lane == 0) red[wave][b] = ss;
         }
         __syncthreads();
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const float s = wave_sum(acc[r][b]);
+            const float s = wave_sum_dpp(acc[r][b]);
             if (lane == 0) red[wave][r * NB + b] = s;
         }
     __syncthreads();
@@ -322,9 +331,9 @@ __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restr
     float* stat = scr + ((long long)b * hl + kvh * G) * nchunks * (D + 2);
     for (int g = wave; g < G; g += 4) {
         const float s = ss[g * 64 + lane];
-        const float m = wave_max(s);
+        const float m = wave_max_dpp(s);
         const float p = exp2f(s - m);
-        const float l = wave_sum(p);
+        const float l = wave_sum_dpp(p);
         ss[g * 64 + lane] = p;
         if (lane == 0) {
             float* st = stat + ((long long)g * nchunks + chunk) * (D + 2);
@@ -464,9 +473,9 @@ __global__ __launch_bounds__(256) void attn_decode_chunk(const bf16* __restrict_
     float* stat = scr + ((long long)b * hl + kvh * G) * nchunks * (D + 2);
     for (int g = wave; g < G; g += 4) {
         const float s = lane < CH ? sp[g * CH + lane] : -INFINITY;
-        const float m = wave_max(s);
+        const float m = wave_max_dpp(s);
         const float p = lane < CH ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-        const float l = wave_sum(p);
+        const float l = wave_sum_dpp(p);
         if (lane < CH) sp[g * CH + lane] = p;
         if (lane == 0) {
             float* st = stat + ((long long)g * nchunks + chunk) * (D + 2);
@@ -542,7 +551,7 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
     const float* st = scr + ((long long)b * hl + head) * stride * (D + 2);
     float m = -INFINITY;
     for (int c = tid; c < nchunks; c += NT) m = fmaxf(m, st[(long long)c * (D + 2) + D]);
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     if (lane == 0) sred[wave] = m;
     __syncthreads();
     float M = sred[0];
@@ -569,7 +578,7 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
         acc += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
     spart[part][dim] = acc;
-    l = wave_sum(l);
+    l = wave_sum_dpp(l);
     __syncthreads();
     if (lane == 0) sred[wave] = l;
     __syncthreads();

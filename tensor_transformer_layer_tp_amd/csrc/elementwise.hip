@@ -6,7 +6,7 @@ namespace tp {
 namespace {
 
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
-    v = wave_sum(v);
+    v = wave_sum_dpp(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __syncthreads();
     if (lane == 0) red[wave] = v;
@@ -15,30 +15,63 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 }
 
 // n = x / sqrt(mean(x^2) + eps) * g, one row per work-group, fp32 arithmetic,
-// bf16 result rounded to nearest even.  Requires n % 8 == 0.
+// bf16 result rounded to nearest even.  Requires n % 8 == 0.  With MAXC > 0
+// the row (at most 2048 * MAXC elements) is read once and kept in registers;
+// MAXC = 0 reads it twice, for any width.
+template <int MAXC>
 __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const bf16* __restrict__ x,
                                                            const bf16* __restrict__ g,
                                                            bf16* __restrict__ out, int n, float eps) {
     __shared__ float red[4];
     const bf16* xr = x + (long long)blockIdx.x * n;
     bf16* orow = out + (long long)blockIdx.x * n;
+    const int nc = n / 8;
     float ss = 0.f;
-    for (int c = threadIdx.x; c < n / 8; c += 256) {
-        u16x8 v = *(const u16x8*)(xr + c * 8);
+    if constexpr (MAXC > 0) {
+        u16x8 v[MAXC], w[MAXC];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float f = bfbits2f(v[e]);
-            ss += f * f;
+        for (int i = 0; i < MAXC; ++i) {
+            const int c = min((int)threadIdx.x + 256 * i, nc - 1);   // clamped: issued and in bounds
+            v[i] = *(const u16x8*)(xr + c * 8);
+            w[i] = *(const u16x8*)(g + c * 8);
         }
-    }
-    const float rs = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
-    for (int c = threadIdx.x; c < n / 8; c += 256) {
-        u16x8 v = *(const u16x8*)(xr + c * 8);
-        u16x8 w = *(const u16x8*)(g + c * 8);
-        u16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f2bf_bits(bfbits2f(v[e]) * rs * bfbits2f(w[e]));
-        *(u16x8*)(orow + c * 8) = o;
+        for (int i = 0; i < MAXC; ++i)
+            if ((int)threadIdx.x + 256 * i < nc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = bfbits2f(v[i][e]);
+                    ss += f * f;
+                }
+        const float rs = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            if (c < nc) {
+                u16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = f2bf_bits(bfbits2f(v[i][e]) * rs * bfbits2f(w[i][e]));
+                *(u16x8*)(orow + c * 8) = o;
+            }
+        }
+    } else {
+        for (int c = threadIdx.x; c < nc; c += 256) {
+            u16x8 v = *(const u16x8*)(xr + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float f = bfbits2f(v[e]);
+                ss += f * f;
+            }
+        }
+        const float rs = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
+        for (int c = threadIdx.x; c < nc; c += 256) {
+            u16x8 v = *(const u16x8*)(xr + c * 8);
+            u16x8 w = *(const u16x8*)(g + c * 8);
+            u16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = f2bf_bits(bfbits2f(v[e]) * rs * bfbits2f(w[e]));
+            *(u16x8*)(orow + c * 8) = o;
+        }
     }
 }
 
@@ -131,8 +164,13 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int npos, int d, d
 }  // namespace
 
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st) {
-    if (rows <= 0) return;
-    hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
+    if (rows <= 0 || n <= 0) return;
+    if (n <= 2048 * 2)
+        hipLaunchKernelGGL(rmsnorm_bf16_kernel<2>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
+    else if (n <= 2048 * 4)
+        hipLaunchKernelGGL(rmsnorm_bf16_kernel<4>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
+    else
+        hipLaunchKernelGGL(rmsnorm_bf16_kernel<0>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
 }
 
 void rmsnorm_f32(const float* x, const float* g, float* out, int rows, int n, float eps, hipStream_t st) {
