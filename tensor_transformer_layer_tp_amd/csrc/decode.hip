@@ -290,33 +290,47 @@ __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restr
     const int G = hl / kvl;
     const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int nchunks = gridDim.x;   // chunk stride of the scratch (sized for ld_seq positions)
-    const int len = min(*len_dev + 1, ld_seq);
-    if (chunk * 64 >= len) return;   // past the cache length: no work
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     extern __shared__ float sm[];
     float* sq = sm;                 // [G][D]
     float* ss = sm + G * D;         // [G][64]
     const int k0 = chunk * 64;
 
+    // Every load is issued before the cache length arrives: rows are clamped
+    // to the capacity (always addressable) and positions at or past the
+    // length are masked once it is known.
+    constexpr int QD = D / 4;                   // score thread = (key, quarter of the head dim)
+    constexpr int DC = D / 8;                   // P V thread = (8-dim chunk, key group)
+    constexpr int KG = 256 / DC;
+    constexpr int KPG = 64 / KG;
+    const int key = tid >> 2, seg = tid & 3;
+    const int dc = tid % DC, kg = tid / DC;
+    u16x8 kraw[QD / 8], vraw[KPG];
+    {
+        const bf16* krow = K + kv_row(b, kvh, min(k0 + key, ld_seq - 1), kvl, ld_seq, D, table, bsz, max_blocks);
+#pragma unroll
+        for (int c = 0; c < QD / 8; ++c) kraw[c] = *(const u16x8*)(krow + seg * QD + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < KPG; ++i) {
+        const int gk = min(k0 + kg * KPG + i, ld_seq - 1);
+        vraw[i] = *(const u16x8*)(V + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks) + dc * 8);
+    }
     for (int i = tid; i < G * D; i += 256) {
         const int g = i / D, dd = i % D;
         sq[i] = bf2f(q[((long long)b * hl + kvh * G + g) * D + dd]);
     }
+    const int len = min(*len_dev + 1, ld_seq);
+    if (k0 >= len) return;   // past the cache length: no work (uniform per work-group)
     __syncthreads();
 
-    // scores: thread = (key, quarter of the head dim)
+    // scores
     {
-        constexpr int QD = D / 4;
-        const int key = tid >> 2, seg = tid & 3;
-        const int gk = min(k0 + key, len - 1);
         float kf[QD];
 #pragma unroll
-        for (int c = 0; c < QD / 8; ++c) {
-            const u16x8 v = *(const u16x8*)(K + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks) +
-                                            seg * QD + c * 8);
+        for (int c = 0; c < QD / 8; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kf[c * 8 + e] = bfbits2f(v[e]);
-        }
+            for (int e = 0; e < 8; ++e) kf[c * 8 + e] = bfbits2f(kraw[c][e]);
         for (int g = 0; g < G; ++g) {
             float s = 0.f;
 #pragma unroll
@@ -342,35 +356,24 @@ __global__ __launch_bounds__(256) void attn_decode_chunk_mha(const bf16* __restr
         }
     }
     __syncthreads();
-    // o[g][dim] = sum_key p[g][key] V[key][dim]; thread = (dim chunk of 8, key group of 4)
+    // o[g][dim] = sum_key p[g][key] V[key][dim]
     {
-        constexpr int DC = D / 8;               // dim chunks
-        constexpr int KG = 256 / DC;            // key groups
-        constexpr int KPG = 64 / KG;            // keys per group
-        const int dc = tid % DC, kg = tid / DC;
-        float vf[KPG][8];
+        float vf[KPG][8];   // rows past the length (stale cache contents) count as zero
 #pragma unroll
-        for (int i = 0; i < KPG; ++i) {
-            const int key = kg * KPG + i;
-            const int gk = min(k0 + key, len - 1);
-            const u16x8 v = *(const u16x8*)(V + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks) + dc * 8);
+        for (int i = 0; i < KPG; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vf[i][e] = bfbits2f(v[e]);
-        }
-        __syncthreads();
-        float* part = sm;  // reuse: [KG][8] per head pass (scores stay in ss)
+            for (int e = 0; e < 8; ++e) vf[i][e] = k0 + kg * KPG + i < len ? bfbits2f(vraw[i][e]) : 0.f;
+        float* pg = sm + G * D + G * 64;  // [KG][D] partial sums, after sq and ss
         for (int g = 0; g < G; ++g) {
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
             for (int i = 0; i < KPG; ++i) {
-                const float p = ss[g * 64 + kg * KPG + i];
+                const float p = ss[g * 64 + kg * KPG + i];   // zero past the length
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] += p * vf[i][e];
             }
-            // sum over key groups: thread (dc, kg) -> part[kg][dc*8+e]
-            float* pg = part + G * D + G * 64;  // scratch after sq and ss
 #pragma unroll
             for (int e = 0; e < 8; ++e) pg[kg * D + dc * 8 + e] = o[e];
             __syncthreads();
@@ -536,19 +539,20 @@ __global__ __launch_bounds__(256) void pages_kernel(const bf16* __restrict__ k, 
 // maxima are reduced by all threads; the chunk weights exp2(m_c - M) go to
 // LDS a tile of 1024 chunks at a time; thread (dim, part) sums the weighted
 // outputs of a contiguous share (one of NT / D) of the chunks with eight
-// loads in flight, and the parts meet in LDS.
+// loads in flight, and the parts meet in LDS.  st: the head's chunk records
+// (D outputs, max, sum; stride D + 2); lds: MERGE_LDS floats.
+constexpr int MERGE_TILE = 1024;
 template <int D, int NT>
-__global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
-                                                          int hl, int stride, const int* __restrict__ len_dev,
-                                                          int ld_seq, int CH) {
-    constexpr int NW = NT / 64, P = NT / D, TILE = 1024;
-    __shared__ float sw[TILE];
-    __shared__ float sred[NW];
-    __shared__ float spart[P][D];
-    const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+constexpr int merge_lds_floats() { return MERGE_TILE + NT / 64 + (NT / D) * D; }
+
+template <int D, int NT>
+__device__ void merge_head(const float* __restrict__ st, int nchunks, bf16* __restrict__ out, float* lds) {
+    constexpr int NW = NT / 64, P = NT / D;
+    float* sw = lds;                  // [MERGE_TILE] chunk weights
+    float* sred = sw + MERGE_TILE;    // [NW]
+    float* spart = sred + NW;         // [P][D]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int dim = tid % D, part = tid / D;
-    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by the chunk kernel
-    const float* st = scr + ((long long)b * hl + head) * stride * (D + 2);
     float m = -INFINITY;
     for (int c = tid; c < nchunks; c += NT) m = fmaxf(m, st[(long long)c * (D + 2) + D]);
     m = wave_max_dpp(m);
@@ -558,8 +562,8 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, sred[w]);
     float l = 0.f, acc = 0.f;
-    for (int c0 = 0; c0 < nchunks; c0 += TILE) {
-        const int n = min(TILE, nchunks - c0);
+    for (int c0 = 0; c0 < nchunks; c0 += MERGE_TILE) {
+        const int n = min(MERGE_TILE, nchunks - c0);
         __syncthreads();
         for (int c = tid; c < n; c += NT) {
             const float* sc = st + (long long)(c0 + c) * (D + 2);
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
         for (; c < hi; ++c) a[0] += sw[c] * st[(long long)(c0 + c) * (D + 2) + dim];
         acc += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
-    spart[part][dim] = acc;
+    spart[part * D + dim] = acc;
     l = wave_sum_dpp(l);
     __syncthreads();
     if (lane == 0) sred[wave] = l;
@@ -587,9 +591,21 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
 #pragma unroll
         for (int w = 0; w < NW; ++w) L += sred[w];
 #pragma unroll
-        for (int p = 0; p < P; ++p) o += spart[p][tid];
-        O[((long long)b * hl + head) * D + tid] = f2bf(o / L);
+        for (int p = 0; p < P; ++p) o += spart[p * D + tid];
+        out[tid] = f2bf(o / L);
     }
+    __syncthreads();   // the LDS may be reused by the caller
+}
+
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restrict__ scr, bf16* __restrict__ O,
+                                                          int hl, int stride, const int* __restrict__ len_dev,
+                                                          int ld_seq, int CH) {
+    __shared__ float lds[merge_lds_floats<D, NT>()];
+    const int head = blockIdx.x, b = blockIdx.y;
+    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by the chunk kernel
+    merge_head<D, NT>(scr + ((long long)b * hl + head) * stride * (D + 2), nchunks,
+                      O + ((long long)b * hl + head) * D, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -839,14 +855,16 @@ void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, floa
                       int kvl, const int* len_dev, int ld_seq, int d, const int* table, int bsz, int mb,
                       hipStream_t st) {
     const int ch = decode_chunk(B, hl, kvl, ld_seq, d);
+#define TP_DA(DD, CC) launch_decode_attn<DD, CC>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st)
     if (d == 128) {
-        if (ch == 64) launch_decode_attn<128, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
-        else if (ch == 32) launch_decode_attn<128, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
-        else launch_decode_attn<128, 16>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
+        if (ch == 64) TP_DA(128, 64);
+        else if (ch == 32) TP_DA(128, 32);
+        else TP_DA(128, 16);
     } else {
-        if (ch == 64) launch_decode_attn<64, 64>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
-        else launch_decode_attn<64, 32>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st);
+        if (ch == 64) TP_DA(64, 64);
+        else TP_DA(64, 32);
     }
+#undef TP_DA
 }
 
 void kv_to_pages(const bf16* k, const bf16* v, bf16* kpool, bf16* vpool, int B, int kvl, int S, int d,
