@@ -712,10 +712,19 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
     up = [r for r in stats if re.search(TRAFFIC_KERNELS["gemm_up_7b_t2"][1], r["Name"])]
     rocprof_up = sum(float(r["AverageNs"]) for r in up) / 1e3
     kinds = [re.search(r"gemm_\w+_kernel<[^>]*>", r["Name"]).group(0) for r in up]
+    # the timed window: the 7B t=2 prefill stack runs the other rank's MLP once, then
+    # `warmup` untimed steps, then the `steps` timed ones (one projection each)
+    disp = sorted(rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    lo, k = 1 + int(line["warmup"]), int(line["steps"])
+    window = 0.0
+    for r in up:
+        d = [int(x["End_Timestamp"]) - int(x["Start_Timestamp"]) for x in disp if x["Kernel_Name"] == r["Name"]]
+        window += statistics.mean(d[lo:lo + k]) / 1e3 if len(d) >= lo + k else float("nan")
     live.append(f"- prefill roofline kernel ({line['roofline']['kernel']}): live HIP-event average "
-                f"{line['roofline']['avg_us']} µs over {line['roofline']['launches']} projections; rocprof: "
-                f"{rocprof_up:.1f} µs, the sum of the averages of its {len(up)} launch kind(s) "
-                f"({', '.join(kinds)})")
+                f"{line['roofline']['avg_us']} µs over the {line['roofline']['launches']} timed projections; "
+                f"rocprof over the same {k} dispatches (after the {line['warmup']} warmup steps): {window:.1f} µs, "
+                f"over all {up[0]['Calls'] if up else 0} dispatches of the run: {rocprof_up:.1f} µs "
+                f"(sum over its {len(up)} launch kind(s): {', '.join(kinds)})")
     if "decode" in line:
         dk = line["decode"]["kernels"].get("gemv_up")
         gv = [r for r in stats if re.search(TRAFFIC_KERNELS["gemv_up_7b_t4"][1], r["Name"])]
