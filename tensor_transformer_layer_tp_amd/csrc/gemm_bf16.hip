@@ -709,7 +709,7 @@ const Cfg kCfgs[] = {
     {128, 384, 0.95f, 1},  // 9 dma 128x384 BK32 ST4
     {128, 384, 0.95f, 1},  // 10 dma 128x384 BK32 ST3
     {256, 256, 1.08f, 1},  // 11 register-pipelined 256x256 BK64, 8 waves
-    {256, 128, 1.02f, 1},  // 12 register-pipelined 256x128 BK64, 8 waves
+    {256, 128, 1.00f, 1},  // 12 register-pipelined 256x128 BK64, 8 waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
