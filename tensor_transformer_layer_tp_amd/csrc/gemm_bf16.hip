@@ -787,7 +787,11 @@ double model_us(int c, int mode, int M, int N, int K) {
     const Cfg& f = kCfgs[c];
     const long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
     const double eff = f.eff * ((c >= 3 && c <= 10 && mode == EPI_QKV) ? 0.8 : 1.0);
-    return kLaunchUs + (double)((tiles + 255) / 256) * 2.0 * f.bm * f.bn * K / (eff * kCuFlopPerUs);
+    // a configuration with `occ` work-groups per CU reaches its rate only with all of them resident: a
+    // round is 256 * occ tiles and costs occ tiles' time, however few tiles the last round has
+    const long long per_round = 256LL * f.occ;
+    return kLaunchUs + (double)((tiles + per_round - 1) / per_round) * f.occ * 2.0 * f.bm * f.bn * K /
+                           (eff * kCuFlopPerUs);
 }
 
 // A GEMM runs as one launch, or as two over column ranges: the first covers
