@@ -309,6 +309,13 @@ int tp_tune_set_gemm_config(int cfg);
  * TP_E_ARG outside 0..2. */
 int tp_tune_set_attn_groups(int kg);
 
+/* tp_tune_set_decode_chunk -- tuning hook for bf16 decode attention with
+ * query groups (query heads > KV heads): 16, 32 or 64 cached positions per
+ * chunk work-group (32 at least for head dim 64), or 0 to restore the choice
+ * by grid size.  The workspace follows the chunk size on the next call.
+ * Process-wide, not thread-safe; TP_E_ARG for other values. */
+int tp_tune_set_decode_chunk(int ch);
+
 void tp_shard_destroy(tp_shard *s);
 void tp_kv_destroy(tp_kv *kv);
 

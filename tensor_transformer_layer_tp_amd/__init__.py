@@ -369,6 +369,11 @@ def set_gemm_config(cfg: int) -> None:
     N.check(N.lib().tp_tune_set_gemm_config(int(cfg)), "tp_tune_set_gemm_config")
 
 
+def set_decode_chunk(ch: int) -> None:
+    """Tuning hook: decode attention positions per chunk for query groups (0 = automatic, 16, 32, 64)."""
+    N.check(N.lib().tp_tune_set_decode_chunk(int(ch)), "tp_tune_set_decode_chunk")
+
+
 def set_attn_groups(kg: int) -> None:
     """Tuning hook: prefill attention key groups (0 = automatic, 1 or 2)."""
     N.check(N.lib().tp_tune_set_attn_groups(int(kg)), "tp_tune_set_attn_groups")

@@ -811,13 +811,18 @@ void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part,
 // Positions per chunk: 64; query groups take fewer when 64 leaves fewer
 // than 128 chunk work-groups (few KV heads and sequences), down to 16 (32
 // for d = 64).
+int g_decode_chunk = 0;   // 0: automatic; 16, 32, 64: forced for query groups
+
 int decode_chunk(int B, int hl, int kvl, int cap, int d) {
     int ch = 64;
     if (hl == kvl) return ch;
     const int lo = d == 128 ? 16 : 32;
+    if (g_decode_chunk) return std::max(g_decode_chunk, lo);
     while (ch > lo && (long long)((cap + ch - 1) / ch) * kvl * B < 128) ch >>= 1;
     return ch;
 }
+
+void set_decode_chunk(int ch) { g_decode_chunk = ch; }
 
 size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d) {
     const int ch = decode_chunk(B, hl, kvl, cap, d);

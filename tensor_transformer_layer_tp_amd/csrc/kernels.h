@@ -105,6 +105,7 @@ void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, floa
 void kv_to_pages(const bf16* k, const bf16* v, bf16* kpool, bf16* vpool, int B, int kvl, int S, int d,
                  const int* table, int bsz, int max_blocks, hipStream_t st);
 size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d);
+void set_decode_chunk(int ch);   // decode attention chunk for query groups: 0 automatic, 16/32/64 forced
 // small decode batches (2..64): split-K MFMA projection + epilogue pass; part
 // is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
 void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,

@@ -853,6 +853,12 @@ int tp_tune_set_gemm_config(int cfg) {
     return TP_OK;
 }
 
+int tp_tune_set_decode_chunk(int ch) {
+    if (ch != 0 && ch != 16 && ch != 32 && ch != 64) return TP_E_ARG;
+    set_decode_chunk(ch);
+    return TP_OK;
+}
+
 int tp_tune_set_attn_groups(int kg) {
     if (kg < 0 || kg > 2) return TP_E_ARG;
     set_attn_groups(kg);

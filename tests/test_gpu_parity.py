@@ -245,6 +245,29 @@ def test_decode_gemv_shapes(hidden, heads, kv, ffn, tp, B):
     assert_close(to_np(pm), refm["partial"][:, 0], "decode mlp partial", "bf16")
 
 
+@pytest.mark.parametrize("ch", [16, 32, 64])
+@pytest.mark.parametrize("hidden,heads,kv,B,S", [(2048, 32, 8, 3, 200), (1024, 16, 2, 2, 137)])
+def test_decode_chunk_sizes(ch, hidden, heads, kv, B, S):
+    """Query-group decode attention with each chunk length forced (head dims
+    64 and 128; ragged last chunk), against the oracle."""
+    from tensor_transformer_layer_tp_amd import set_decode_chunk
+    announce(f"decode chunk {ch}: hidden={hidden} heads={heads}/{kv} B={B} S={S}")
+    tp, r = 2, 1
+    L = Layer(hidden, heads, kv, 2 * hidden, batch=B, seq=S + 1, gamma_noise=True, seed=31)
+    sh = L.shard(tp, r)
+    kvc = sh.kv_cache(B, S + 1)
+    sh.prefill(ATTN, L.dev["x"][:, :S].contiguous(), kvc)
+    try:
+        set_decode_chunk(ch)
+        p = sh.decode(ATTN, L.dev["x"][:, S].contiguous(), kvc, out=nan_like((B, hidden)))
+        torch.cuda.synchronize()
+    finally:
+        set_decode_chunk(0)
+    pre = O.attn_stage(L.exact["x"][:, :S], L.W, L.spec, tp, r)
+    ref = O.decode_attn_stage(L.exact["x"][:, S], pre["k"], pre["v"], L.W, L.spec, tp, r)
+    assert_close(to_np(p), ref["partial"], f"decode attn partial (chunk {ch})", "bf16")
+
+
 @pytest.mark.parametrize("L_len", [1023, 70000])
 def test_decode_long_cache(L_len):
     """Decode against a cache written directly (seeded bf16 values), long
