@@ -92,14 +92,51 @@ struct Parts {
 };
 
 // out = (sum_r parts[r]) + residual, fp32 in rank order, stored as bf16 or fp32.
-template <bool BF16_OUT>
+// TT > 0: t == TT is known at compile time, so the t partial loads and the
+// residual load of an element go out together before any add (a loop over
+// a run-time t waits for each load in turn, which is the whole duration of
+// a decode-sized reduce).  The sum is the same rank-order sum either way.
+template <bool BF16_OUT, int TT>
 __global__ __launch_bounds__(256) void reduce_kernel(Parts parts, int t, const void* __restrict__ residual,
                                                      void* __restrict__ out, long long n) {
     const long long n4 = n >> 2;
     const long long stride = (long long)gridDim.x * 256;
     for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += stride) {
-        f32x4 s = *(const f32x4*)(parts.p[0] + i * 4);
-        for (int r = 1; r < t; ++r) s += *(const f32x4*)(parts.p[r] + i * 4);
+        f32x4 s;
+        if constexpr (TT > 0) {
+            // the residual is loaded with the partials (from a valid dummy address when
+            // there is none) and the sum with it selected afterwards, so no load waits
+            // behind a branch; selecting, not adding zero, keeps a -0 sum intact
+            const bool hr = residual != nullptr;
+            f32x4 rf;
+            if constexpr (BF16_OUT) {
+                const uint2 rv = *(const uint2*)((const uint16_t*)(hr ? residual : (const void*)parts.p[0]) + i * 4);
+                rf = (f32x4){__uint_as_float(rv.x << 16), __uint_as_float(rv.x & 0xffff0000u),
+                             __uint_as_float(rv.y << 16), __uint_as_float(rv.y & 0xffff0000u)};
+            } else {
+                rf = *(const f32x4*)((const float*)(hr ? residual : (const void*)parts.p[0]) + i * 4);
+            }
+            f32x4 v[TT];
+#pragma unroll
+            for (int r = 0; r < TT; ++r) v[r] = *(const f32x4*)(parts.p[r] + i * 4);
+            s = v[0];
+#pragma unroll
+            for (int r = 1; r < TT; ++r) s += v[r];
+            const f32x4 sr = s + rf;
+            s = hr ? sr : s;
+            if constexpr (BF16_OUT) {
+                uint2 ov;
+                ov.x = (uint32_t)f2bf_bits(s[0]) | ((uint32_t)f2bf_bits(s[1]) << 16);
+                ov.y = (uint32_t)f2bf_bits(s[2]) | ((uint32_t)f2bf_bits(s[3]) << 16);
+                *(uint2*)((uint16_t*)out + i * 4) = ov;
+            } else {
+                *(f32x4*)((float*)out + i * 4) = s;
+            }
+            continue;
+        } else {
+            s = *(const f32x4*)(parts.p[0] + i * 4);
+            for (int r = 1; r < t; ++r) s += *(const f32x4*)(parts.p[r] + i * 4);
+        }
         if (BF16_OUT) {
             if (residual) {
                 const uint16_t* rp = (const uint16_t*)residual + i * 4;
@@ -194,10 +231,28 @@ void partial_reduce(const float* const* parts, int t, const void* residual, void
     for (int r = 0; r < 64; ++r) P.p[r] = r < t ? parts[r] : nullptr;
     long long n4 = n >> 2;
     int blocks = (int)std::min<long long>(std::max<long long>((n4 + 255) / 256, 1), 256LL * 8);
-    if (bf16_out)
-        hipLaunchKernelGGL(reduce_kernel<true>, dim3(blocks), dim3(256), 0, st, P, t, residual, out, n);
-    else
-        hipLaunchKernelGGL(reduce_kernel<false>, dim3(blocks), dim3(256), 0, st, P, t, residual, out, n);
+#define TP_RED(BO, TT) hipLaunchKernelGGL((reduce_kernel<BO, TT>), dim3(blocks), dim3(256), 0, st, P, t, residual, out, n)
+    // the all-loads-first kernels are for reductions that one pass of the grid covers
+    // (decode sizes); a long grid-stride loop streams better with one load at a time
+    const int tt = n4 <= (long long)blocks * 256 ? t : 0;
+    if (bf16_out) {
+        switch (tt) {
+            case 1: TP_RED(true, 1); break;
+            case 2: TP_RED(true, 2); break;
+            case 4: TP_RED(true, 4); break;
+            case 8: TP_RED(true, 8); break;
+            default: TP_RED(true, 0); break;
+        }
+    } else {
+        switch (tt) {
+            case 1: TP_RED(false, 1); break;
+            case 2: TP_RED(false, 2); break;
+            case 4: TP_RED(false, 4); break;
+            case 8: TP_RED(false, 8); break;
+            default: TP_RED(false, 0); break;
+        }
+    }
+#undef TP_RED
 }
 
 void rope_table(float* cos_t, float* sin_t, int npos, int d, float theta, hipStream_t st) {
