@@ -77,7 +77,8 @@ def run_chain(layer: Layer, tp: int, B: int, S: int, check_kv=True):
 # ---------------------------------------------------------------- reduce kernel
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("t,n", [(1, 1), (2, 3), (3, 4099), (8, 1 << 20), (4, 0)])
+@pytest.mark.parametrize("t,n", [(1, 1), (2, 3), (3, 4099), (8, 1 << 20), (4, 0), (1, 64), (2, 4096), (4, 4101),
+                                 (2, 1 << 22)])
 def test_partial_reduce(dtype, t, n):
     announce(f"partial_reduce dtype={dtype} t={t} n={n}")
     parts64 = [synth.draw_normal((n,), 10 + r, 3.0).astype(np.float64) for r in range(t)]
