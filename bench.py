@@ -48,7 +48,7 @@ MIN_DECODE_FOOTPRINT = 1.0e9   # decode weight copies span at least this many by
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--decode-layers", type=int, default=0,
                     help="layer copies in the decode stack (0: enough for >= 1 GB of weights)")
@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                     help="no GPU: turn rocprofv3 outputs of this script into profiles/traffic.json and "
                          "profiles/*.md (see profiles/README.md for the commands)")
+    ap.add_argument("--summarize-mfma", nargs=1, metavar="PMC_DIR",
+                    help="no GPU: turn a rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE run of this script "
+                         "into profiles/mfma_counters.md")
     return ap.parse_args()
 
 
@@ -740,6 +743,73 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
     print(json.dumps(rec, indent=1))
 
 
+def summarize_mfma(pmc_dir):
+    """MFMA evidence for the prefill kernels of the 7B t=2 step from one
+    rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE run: per kernel
+    kind the dispatch count, mean duration, rocprofv3's MfmaUtil (MFMA busy
+    cycles / (active cycles x SIMDs)), the executed bf16 MFMA FLOPs per
+    dispatch and the clock the kernel ran at (active cycles per XCD over the
+    duration)."""
+    import csv
+    import glob
+    import re
+    import statistics
+    rows = []
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        rows.extend(csv.DictReader(open(f)))
+    agents = []
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*agent_info.csv"), recursive=True)):
+        agents.extend(a for a in csv.DictReader(open(f)) if a.get("Name", "").startswith("gfx"))
+    n_xcc = int(agents[0]["Num_Xcc"]) if agents else 8
+    disp = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if not re.search(r"gemm_\w+_kernel|attn_prefill_kernel", name):
+            continue
+        d = disp.setdefault((name, r["Dispatch_Id"]),
+                            {"name": name, "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    kinds = {}
+    for d in disp.values():
+        kinds.setdefault(d["name"], []).append(d)
+    w = synth_workload("7b-t2-prefill")
+    gemm, attn = prefill_flops(w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, w.batch, w.seq)
+    mode_of = {"0": "fp32 partial (out and down projections)", "1": "Q/K/V + rotary", "2": "gate/up + SwiGLU"}
+    md = ["| kernel | dispatches | mean µs | MfmaUtil % | executed bf16 MFMA GFLOP per dispatch | clock GHz |",
+          "|---|---:|---:|---:|---:|---:|"]
+    up_flops = 0.0
+    for name, ds in sorted(kinds.items(), key=lambda kv: -statistics.mean(x["us"] for x in kv[1])):
+        us = statistics.mean(x["us"] for x in ds)
+        util = statistics.mean(x.get("MfmaUtil", float("nan")) for x in ds)
+        gf = statistics.mean(x.get("MfmaFlopsBF16", float("nan")) for x in ds) / 1e9
+        ghz = statistics.mean(x.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcc / (x["us"] * 1e3) for x in ds)
+        m = re.search(r"gemm_\w+_kernel<[^>]*, (\d)>", name)
+        label = (re.search(r"(gemm_\w+_kernel<[^>]*>|attn_prefill_kernel\w*)", name) or re.search(r".*", name)).group(0)
+        if m:
+            label += f" ({mode_of.get(m.group(1), '')})"
+            if m.group(1) == "2":
+                up_flops += gf
+        md.append(f"| `{label[:90]}` | {len(ds)} | {us:.1f} | {util:.1f} | {gf:.2f} | {ghz:.2f} |")
+    lines = ["# MFMA counters of the 7B t=2 prefill kernels (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE)",
+             "",
+             "Command: see profiles/README.md (command 4). MfmaUtil is rocprofv3's derived counter: MFMA busy cycles "
+             "over active cycles times SIMDs, at the clock the kernel ran at; executed FLOPs are "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; the clock is GRBM_GUI_ACTIVE per XCD over the dispatch duration.",
+             "",
+             f"- gate/up projection: {up_flops:.2f} GFLOP executed by its launch kinds per projection against "
+             f"{gemm['gemm_up'] / 1e9:.2f} algorithmic (zero padding of ragged tiles is the difference)",
+             "",
+             *md]
+    with open(os.path.join(ROOT, "profiles", "mfma_counters.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def synth_workload(name):
+    from tensor_transformer_layer_tp_amd import synth
+    return synth.WORKLOADS[name]
+
+
 def calib_copy(torch, mib):
     """A plain device copy of known size (the scale for byte counters)."""
     n = mib * 1024 * 1024
@@ -760,6 +830,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(*args.summarize, args.calib_copy or 1024)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma[0])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
