@@ -51,6 +51,13 @@ __device__ __forceinline__ int swz(int r, int c) {
     return CPR == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15: no wait)
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Write the accumulator tile of one wave.  acc[i][j][r] sits at row
 // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of MFMA tile (i, j).
 template <int FM, int FN, int MODE>
@@ -109,6 +116,17 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
         const int d = q.d;
         const int half = d >> 1;
         const int qcols = q.hl * d, kcols = q.kvl * d;
+        // Everything the stores depend on is read before the first store: the
+        // compiler cannot prove the stores leave these locations alone, so a
+        // load placed after a store waits for it.
+        const int base_pos = q.pos_dev ? *q.pos_dev : q.pos0;
+        // Token row -> (sequence b, offset s).  One integer division per
+        // 32-row tile gives the first row's pair; the other rows lie at most
+        // 27 rows further, so their extra wrap count n / S is below 29 and a
+        // float quotient corrected by one step is exact.  Rows past M take
+        // row M-1's pair (their stores are dropped; their reads stay in range).
+        const float inv_s = 1.f / (float)q.S;
+        const int b_last = (M - 1) / q.S, s_last = (M - 1) - b_last * q.S;
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
             const int gcol = wcol0 + p * 64;          // launch-relative (bounds)
@@ -121,32 +139,56 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
             bf16* dbase = region == 0 ? (bf16*)q.q : (region == 1 ? (bf16*)q.k : (bf16*)q.v);
             const int nh = region == 0 ? q.hl : q.kvl;
             const int ld = region == 0 ? q.S : q.ld_seq;
-            const int base_pos = q.pos_dev ? *q.pos_dev : q.pos0;
             const int poff = region == 0 ? 0 : base_pos;   // q is stored by token index, k/v by position
+            const bool paged = region != 0 && q.table != nullptr;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i) {
+                // The lane's 16 rows of this MFMA tile: rotation factors and
+                // destination rows (block-table reads included) are gathered
+                // first so that their loads are in flight together.
+                const int row0 = wrow0 + i * 32 + row_in;
+                const int b0 = row0 / q.S, s0 = row0 - b0 * q.S;
+                float cs[16], sn[16];
+                int key[16], ps[16];   // key: sequence, or pool block of a paged cache
+                bool ok[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = wrow0 + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
-                    const int rr = min(row, M - 1);
-                    const int b = rr / q.S, s = rr - b * q.S;
+                    const int row = row0 + 8 * (r >> 2) + (r & 3);
+                    const int n = s0 + 8 * (r >> 2) + (r & 3);
+                    int w = (int)((float)n * inv_s);
+                    const int t = n - w * q.S;
+                    w = t < 0 ? w - 1 : (t >= q.S ? w + 1 : w);
+                    const int b = row < M ? b0 + w : b_last;
+                    const int s = row < M ? n - w * q.S : s_last;
                     const int pos = base_pos + s;
-                    float y1 = acc[i][2 * p][r], y2 = acc[i][2 * p + 1][r];
-                    float c = 1.f, sn = 0.f;
+                    cs[r] = 1.f;
+                    sn[r] = 0.f;
                     if (rot) {
-                        c = q.rope_cos[(long long)pos * half + i1];
-                        sn = q.rope_sin[(long long)pos * half + i1];
+                        cs[r] = q.rope_cos[(long long)pos * half + i1];
+                        sn[r] = q.rope_sin[(long long)pos * half + i1];
                     }
-                    const float o1 = y1 * c - y2 * sn;
-                    const float o2 = y2 * c + y1 * sn;
-                    bf16* dst = dbase + (region == 0 || q.table == nullptr
-                                             ? (((long long)b * nh + head) * ld + poff + s) * d
-                                             : kv_row(b, head, pos, q.kvl, q.ld_seq, d, q.table, q.bsz, q.max_blocks));
-                    if (row < M && gcol < N && (region == 0 || pos < q.ld_seq)) {
-                        dst[i1] = f2bf(o1);
-                        dst[i1 + half] = f2bf(o2);
+                    key[r] = paged ? kv_block(b, pos, q.table, q.bsz, q.max_blocks) : b;
+                    ps[r] = s;
+                    ok[r] = row < M && gcol < N && (region == 0 || pos < q.ld_seq);
+                }
+                // One wait for all of them: with the predicated stores below,
+                // the compiler would otherwise wait per row, and on this
+                // architecture such a wait also covers the stores before it.
+                wait_vm<0>();
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float y1 = acc[i][2 * p][r], y2 = acc[i][2 * p + 1][r];
+                    const float o1 = y1 * cs[r] - y2 * sn[r];
+                    const float o2 = y2 * cs[r] + y1 * sn[r];
+                    const long long off =
+                        paged ? kv_row_in_block(key[r], head, base_pos + ps[r], q.kvl, q.bsz, d)
+                              : (((long long)key[r] * nh + head) * ld + poff + ps[r]) * d;
+                    if (ok[r]) {
+                        dbase[off + i1] = f2bf(o1);
+                        dbase[off + i1 + half] = f2bf(o2);
                     }
                 }
+            }
         }
     }
 }
@@ -168,12 +210,6 @@ __device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t voff, uint32_t soff
         : "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    // s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15: no wait)
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
     const uint64_t b = (uint64_t)base;

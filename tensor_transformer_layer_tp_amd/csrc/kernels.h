@@ -34,11 +34,20 @@ struct QKVDest {
 
 // Address of cache row (sequence b, kv head h, position p) in a contiguous
 // cache [B, kvl, ld_seq, d] or, with a block table, in a paged pool.
+// The paged form is split in two steps (table read, then the row address)
+// so that callers can issue the table reads of several rows together.  The
+// block size is a power of two (checked when a paged cache is created).
+__device__ __forceinline__ int kv_block(int b, int p, const int* table, int bsz, int max_blocks) {
+    const int blk = p >> (31 - __builtin_clz(bsz));
+    return table[(long long)b * max_blocks + min(blk, max_blocks - 1)];   // clamped: in bounds
+}
+__device__ __forceinline__ long long kv_row_in_block(int blk, int h, int p, int kvl, int bsz, int d) {
+    return (((long long)blk * kvl + h) * bsz + (p & (bsz - 1))) * d;
+}
 __device__ __forceinline__ long long kv_row(int b, int h, int p, int kvl, int ld_seq, int d, const int* table,
                                             int bsz, int max_blocks) {
     if (table == nullptr) return (((long long)b * kvl + h) * ld_seq + p) * d;
-    const int blk = table[(long long)b * max_blocks + min(p / bsz, max_blocks - 1)];   // clamped: in bounds
-    return (((long long)blk * kvl + h) * bsz + (p % bsz)) * d;
+    return kv_row_in_block(kv_block(b, p, table, bsz, max_blocks), h, p, kvl, bsz, d);
 }
 
 // Update of a device-resident cache length, done by one thread of the
