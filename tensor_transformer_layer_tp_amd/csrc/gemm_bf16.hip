@@ -566,11 +566,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
     };
-    auto mma = [&](int buf, int i) {
+    // MFMAs q0 .. q1-1 of a k-slice, numbered i * FN + j
+    auto mma = [&](int buf, int q0, int q1) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        for (int q = q0; q < q1; ++q)
+            acc[q / FN][q % FN] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][q / FN], fb[buf][q % FN], acc[q / FN][q % FN], 0, 0, 0);
     };
+    constexpr int NQ = FM * FN, HQ = NQ / 2;
 
     // One tile.  SET = kt % 2.  Slices 0-2: a quarter of the loads of tile
     // kt+2, the fragments of the next slice, this slice's MFMAs.  Slice 3:
@@ -586,10 +589,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
             if (kk + 1 < KK) {
                 gload(set, kt + 2, kk);
                 read(stage, kk + 1, nxt);
+                mma(cur, 0, NQ);
 #pragma unroll
-                for (int i = 0; i < FM; ++i) mma(cur, i);
-#pragma unroll
-                for (int q = 0; q < FM * FN; ++q) {
+                for (int q = 0; q < NQ; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
                     __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
                     __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);   // VMEM read
@@ -597,8 +599,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 lstore(std::integral_constant<int, 1 - S>{}, 1 - S);
-#pragma unroll
-                for (int i = 0; i < FM / 2; ++i) mma(cur, i);
+                mma(cur, 0, HQ);
 #pragma unroll
                 for (int q = 0; q < NL; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x0200, 1, 0);   // DS write
@@ -608,10 +609,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
                 __syncthreads();
                 read(1 - S, 0, nxt);
                 gload(set, kt + 2, 3);
+                mma(cur, HQ, NQ);
 #pragma unroll
-                for (int i = FM / 2; i < FM; ++i) mma(cur, i);
-#pragma unroll
-                for (int q = 0; q < FM * FN / 2; ++q) {
+                for (int q = 0; q < NQ - HQ; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
                     __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
                     __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);   // VMEM read
@@ -746,6 +746,7 @@ const Cfg kCfgs[] = {
     {128, 384, 0.95f, 1},  // 10 dma 128x384 BK32 ST3
     {256, 256, 1.08f, 1},  // 11 register-pipelined 256x256 BK64, 8 waves
     {256, 128, 1.00f, 1},  // 12 register-pipelined 256x128 BK64, 8 waves
+    {256, 192, 0.84f, 1},  // 13 register-pipelined 256x192 BK64, 8 waves of 32x192
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -800,7 +801,8 @@ void launch_cfg(int c, const Args& a) {
         case 9: launch_pipe<128, 384, 32, 4, MODE>(a); break;
         case 10: launch_pipe<128, 384, 32, 3, MODE>(a); break;
         case 11: launch_vgpr<256, 256, 2, 4, MODE>(a); break;
-        default: launch_vgpr<256, 128, 4, 2, MODE>(a); break;
+        case 12: launch_vgpr<256, 128, 4, 2, MODE>(a); break;
+        default: launch_vgpr<256, 192, 8, 1, MODE>(a); break;
     }
 }
 
