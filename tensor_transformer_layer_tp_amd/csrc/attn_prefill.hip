@@ -40,6 +40,18 @@ __device__ __forceinline__ int kslot(int r, int c) {
     return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
+// The other 32-lane half's value of v, one VALU op (no LDS round trip): the
+// half swap leaves each lane its own value in one result and its partner's
+// in the other, so max and sum over the pair are the same in every lane.
+__device__ __forceinline__ float half_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 // KG key groups of 4 waves: group g takes the key blocks kb = g (mod KG) for
 // the same 128 queries, with its own LDS buffers and online-softmax state;
 // the states merge through LDS at the end.  KG = 2 halves the critical path
@@ -62,7 +74,8 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
                                            : (MERGE > STAGE_O ? MERGE : STAGE_O));
     __shared__ __attribute__((aligned(16))) bf16 smem[SMEM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block starts stay scalar
     const int grp = KG > 1 ? wave >> 2 : 0, qw = KG > 1 ? wave & 3 : wave, gtid = KG > 1 ? tid & 255 : tid;
     bf16* sK = smem + grp * BUF;
     bf16* sVt = sK + BKV * D;
@@ -95,29 +108,43 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
     const int nit = (nkb + KG - 1) / KG;
 
     // The group's next block is fetched into registers while its current one
-    // is computed from LDS.  Rows past the sequence are clamped to row S-1
-    // (read, never used), so every load is issued unconditionally and stays
-    // in bounds.
+    // is computed from LDS.  Each block is read through a buffer resource
+    // that covers only its rows below S, so rows past the sequence (and whole
+    // blocks past it) read as zeros: every load is issued unconditionally,
+    // with per-lane offsets that stay the same for every block.
     constexpr int KLD = BKV * KC / 256;         // K chunks per thread
     constexpr int VLD = (BKV / 2) * KC / 256;   // V key pairs per thread
-    bf16x8 kreg[KLD];
-    u16x8 vreg[VLD][2];
-    auto fetch = [&](int k0) {
+    u32x4 kreg[KLD];
+    u32x4 vreg[VLD][2];
+    int koff[KLD], voff[VLD][2];
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int idx = gtid + 256 * i;
-            const int gk = min(k0 + idx / KC, S - 1);
-            kreg[i] = *(const bf16x8*)(Kb + (long long)gk * D + (idx % KC) * 8);
-        }
+    for (int i = 0; i < KLD; ++i) {
+        const int idx = gtid + 256 * i;
+        koff[i] = ((idx / KC) * D + (idx % KC) * 8) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+        const int idx = gtid + 256 * i;
+        const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
+        voff[i][0] = ((2 * a) * D + dc * 8) * 2;
+        voff[i][1] = ((2 * a + 1) * D + dc * 8) * 2;
+    }
+    auto fetch = [&](int k0) {
+        const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(BKV, S - k0)) * D * 2);   // uniform
+        const long long base = (long long)min(k0, S) * D;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + base), (short)0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + base), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0);
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int idx = gtid + 256 * i;
-            const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
-            const int g0 = min(k0 + 2 * a, S - 1), g1 = min(k0 + 2 * a + 1, S - 1);
-            vreg[i][0] = *(const u16x8*)(Vb + (long long)g0 * D + dc * 8);
-            vreg[i][1] = *(const u16x8*)(Vb + (long long)g1 * D + dc * 8);
+            vreg[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i][0], 0, 0);
+            vreg[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i][1], 0, 0);
         }
     };
+    // byte selectors of v_perm_b32 that pack the low (high) bf16 halves of two words
+    constexpr uint32_t SEL_LO = 0x05040100u, SEL_HI = 0x07060302u;
+    const uint32_t sel_even = h ? SEL_HI : SEL_LO, sel_odd = h ? SEL_LO : SEL_HI;
     fetch(grp * BKV);
     for (int it = 0; it < nit; ++it) {
         const int k0 = (it * KG + grp) * BKV;
@@ -127,25 +154,24 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
         for (int i = 0; i < KLD; ++i) {
             const int idx = gtid + 256 * i;
             const int key = idx / KC, dc = idx % KC;
-            *(bf16x8*)(sK + key * D + (kslot<KC>(key, dc) << 3)) = kreg[i];
+            *(u32x4*)(sK + key * D + (kslot<KC>(key, dc) << 3)) = kreg[i];
         }
         // V block -> LDS transposed [dim][permuted key], two keys per 32-bit store
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int idx = gtid + 256 * i;
             const int a = idx % (BKV / 2), dc = idx / (BKV / 2);
-            const u16x8 v0 = vreg[i][0], v1 = vreg[i][1];
+            const u32x4 v0 = vreg[i][0], v1 = vreg[i][1];
             const int p = vt_pos(2 * a);
-            const bool hi = (lane >> 5) != 0;
 #pragma unroll
             for (int e0 = 0; e0 < 8; ++e0) {
                 // the two 32-lane halves write rows of opposite parity (distinct banks);
                 // register indices stay static, the upper half takes the partner element
-                const uint32_t a0 = hi ? v0[e0 ^ 1] : v0[e0];
-                const uint32_t a1 = hi ? v1[e0 ^ 1] : v1[e0];
-                const int dim = dc * 8 + (e0 ^ (int)hi);
+                // (the other bf16 half of the same word: one byte permute per store)
+                const uint32_t w = __builtin_amdgcn_perm(v1[e0 >> 1], v0[e0 >> 1], (e0 & 1) ? sel_odd : sel_even);
+                const int dim = dc * 8 + (e0 ^ h);
                 const int off = dim * BKV + ((((p >> 3) ^ ((dim >> 1) & 7)) << 3) | (p & 7));
-                *(uint32_t*)(sVt + off) = a0 | (a1 << 16);
+                *(uint32_t*)(sVt + off) = w;
             }
         }
         __syncthreads();
@@ -165,20 +191,24 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
         }
         // causal mask only where the block reaches past the wave's first query
         const bool diag = k0 + BKV - 1 > q0;
+        // the max is taken on the raw scores and scaled once (the scale is
+        // positive); the exponent below is one fma per score
+        // (a branch of its own on the uniform flag: folded into the loop
+        // below, the compares and selects would run on every block)
+        if (diag) {
+            const int lim = qme - k0 - 4 * h;   // masked: 32t + 8(r/4) + r%4 > lim
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    st[t][r] = 32 * t + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : st[t][r];
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = st[t][r] * scale_log2;
-                if (diag) {
-                    const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-                    s = key > qme ? -INFINITY : s;
-                }
-                st[t][r] = s;
-                mx = fmaxf(mx, s);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+        mx = half_max(mx) * scale_log2;
         // The running max is raised (and the output rescaled) only when a score
         // exceeds it by more than 2^8: softmax does not depend on the reference
         // value, so a stale max only scales P and l by the same factor <= 2^8.
@@ -191,11 +221,12 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
             for (int i = 0; i < NT; ++i) oacc[i] *= alpha;
         }
         float lsum = 0.f;
+        const float neg_m = -m_run;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(st[t][r] - m_run);
+                const float p = __builtin_amdgcn_exp2f(fmaf(st[t][r], scale_log2, neg_m));
                 st[t][r] = p;
                 lsum += p;
             }
@@ -250,7 +281,7 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
 
     // normalise and store through LDS so that the global writes are whole rows
     if (grp == 0) {
-        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        const float l_tot = half_sum(l_run);
         const float inv = 1.f / l_tot;
         bf16* sO = smem + qw * 32 * OROW;   // 32 queries x D per wave
 #pragma unroll
