@@ -642,6 +642,126 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
 }
 
 // ---------------------------------------------------------------------------
+// Producer/consumer 256x256 tile, BK 64, twelve waves.  Waves 0-7 (two per
+// SIMD, a 2 x 4 grid of 128x64 accumulator tiles) only read MFMA fragments
+// from LDS and issue MFMAs; waves 8-11 (one per SIMD) only move tiles from
+// global memory into LDS.  With the loads and LDS writes on waves of their
+// own, the MFMA waves never wait for global memory and never issue a
+// memory-unit instruction.  Two 64 KB LDS stages: while the MFMA waves read
+// tile kt from one, the producers write tile kt+1 into the other; one barrier
+// per tile hands both over.  Register budget: three waves per SIMD, 168 each
+// (128 accumulators + one set of fragments; two register sets of staged
+// loads on the producers).
+template <int MODE>
+__global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A, long long lda,
+                                                      const bf16* __restrict__ B, long long ldb, int M, int N,
+                                                      int K, Epilogue epi, int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4, KK = 4;
+    constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int RS = 32;                       // rows per producer load step (256 threads x 16 B)
+    constexpr int NL = (BM + BN) / RS;           // 16-byte loads per producer thread per tile
+    __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0) apply_len_update(epi.len);
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int KT = K / BK;
+
+    if (wave >= 8) {
+        // Producer thread p copies 16-byte chunk (p & 7) of rows (p >> 3) + 32 i
+        // of the A tile (i < 8) and the B tile (i >= 8).  Rows past M (N) lie
+        // outside the tile's buffer resource and read as zeros; tiles past
+        // the end read zeros through an empty resource.
+        const int p = tid - 512, srow = p >> 3, skc = p & 7;
+        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(A + (long long)m0 * lda), (short)0, max(0, min(BM, M - m0)) * (int)lda * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(B + (long long)n0 * ldb), (short)0, max(0, min(BN, N - n0)) * (int)ldb * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, 0x00020000);
+        int voff[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            voff[i] = i < BM / RS ? ((srow + RS * i) * (int)lda + skc * 8) * 2
+                                  : ((srow + RS * (i - BM / RS)) * (int)ldb + skc * 8) * 2;
+        const int l0 = srow * BK + (swz<8>(srow, skc) << 3);   // rows srow + 32 i share the swizzle
+        u32x4 r[2][NL];
+        auto gload = [&](auto set, int kt) {
+            constexpr int S = decltype(set)::value;
+            const bool in = kt < KT;
+            const int koff = in ? kt * BK * 2 : 0;
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                r[S][i] = __builtin_amdgcn_raw_buffer_load_b128(in ? (i < BM / RS ? rsa : rsb) : rs0, voff[i], koff, 0);
+        };
+        auto lstore = [&](auto set, int stage) {
+            constexpr int S = decltype(set)::value;
+            bf16* sa = smem + stage * STAGE;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) *(u32x4*)(sa + l0 + i * RS * BK) = r[S][i];
+        };
+        using T0 = std::integral_constant<int, 0>;
+        using T1 = std::integral_constant<int, 1>;
+        gload(T0{}, 0);
+        gload(T1{}, 1);
+        wait_vm<NL>();
+        lstore(T0{}, 0);
+        __syncthreads();
+        // iteration kt: set kt%2 is free (its tile is in LDS), set 1-kt%2 holds tile kt+1
+        for (int kt = 0; kt < KT; kt += 2) {
+            gload(T0{}, kt + 2);
+            wait_vm<NL>();
+            lstore(T1{}, 1);
+            __syncthreads();
+            gload(T1{}, kt + 3);
+            wait_vm<NL>();
+            lstore(T0{}, 0);
+            __syncthreads();
+        }
+        wait_vm<0>();
+        return;
+    }
+
+    // MFMA waves
+    const int wm = wave / WN, wn = wave % WN;
+    const int frow = lane & 31, khalf = lane >> 5;
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
+    bf16x8 fa[FM], fb[FN];
+    __syncthreads();
+    // An odd tile count runs one more (all-zero) tile: the loop stays in pairs
+    // so that the stage index is static, like the producers' loop.
+    for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const bf16* a_s = smem + st * STAGE + (wm * TM + frow) * BK;
+            const bf16* b_s = smem + st * STAGE + BM * BK + (wn * TN + frow) * BK;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int c = swz<8>(frow, 2 * kk + khalf) << 3;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+    }
+    epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+}
+
+// ---------------------------------------------------------------------------
 // Register-staged main loop (two register stages, double-buffered LDS, BK 64).
 template <int BM, int BN, int MODE>
 __global__ __launch_bounds__(256) void gemm_reg_kernel(const bf16* __restrict__ A, long long lda,
@@ -747,6 +867,7 @@ const Cfg kCfgs[] = {
     {256, 256, 1.08f, 1},  // 11 register-pipelined 256x256 BK64, 8 waves
     {256, 128, 1.00f, 1},  // 12 register-pipelined 256x128 BK64, 8 waves
     {256, 192, 0.84f, 1},  // 13 register-pipelined 256x192 BK64, 8 waves of 32x192
+    {256, 256, 1.12f, 1},  // 14 producer/consumer 256x256 BK64, 8 MFMA waves + 4 load waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -773,6 +894,13 @@ void launch_pipe(const Args& a) {
     hipLaunchKernelGGL((gemm_dma_pipe_kernel<BM, BN, BK, ST, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda,
                        a.B, a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
 }
+template <int MODE>
+void launch_ws(const Args& a) {
+    const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE>), dim3(tm * tn), dim3(768), 0, a.st, a.A, a.lda, a.B, a.ldb, a.M,
+                       a.N, a.K, a.epi, tm, tn);
+}
+
 template <int BM, int BN, int WM, int WN, int MODE>
 void launch_vgpr(const Args& a) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
@@ -802,7 +930,8 @@ void launch_cfg(int c, const Args& a) {
         case 10: launch_pipe<128, 384, 32, 3, MODE>(a); break;
         case 11: launch_vgpr<256, 256, 2, 4, MODE>(a); break;
         case 12: launch_vgpr<256, 128, 4, 2, MODE>(a); break;
-        default: launch_vgpr<256, 192, 8, 1, MODE>(a); break;
+        case 13: launch_vgpr<256, 192, 8, 1, MODE>(a); break;
+        default: launch_ws<MODE>(a); break;
     }
 }
 
@@ -811,7 +940,8 @@ void launch_cfg(int c, const Args& a) {
 // ring with the rotary one.
 bool usable(int c, int mode) {
     if (c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE)) return false;
-    return !(c == 4 && mode == EPI_QKV);
+    // the rotary epilogue does not fit the producer/consumer kernel's register budget
+    return !((c == 4 || c == 14) && mode == EPI_QKV);
 }
 
 // Modelled time of one launch: rounds of 256 tiles (one per CU), each the
@@ -857,6 +987,8 @@ Plan plan(int M, int N, int K, int mode) {
             best = Plan{1, {c, c}, {0, 0}, {N, 0}};
         }
     }
+    Plan split{};
+    double split_t = 1e30;
     for (int b = 0; b < kNumCfg; ++b) {
         if (!usable(b, mode) || kCfgs[b].occ != 1) continue;
         const int tiles_m = cdiv(M, kCfgs[b].bm);
@@ -868,13 +1000,13 @@ Plan plan(int M, int N, int K, int mode) {
         for (int c = 0; c < kNumCfg; ++c) {
             if (!usable(c, mode)) continue;
             const double t = t_big + model_us(c, mode, M, N - n_big, K);
-            if (t < best_t * 0.97) {   // a second launch must clearly pay for itself
-                best_t = t;
-                best = Plan{2, {b, c}, {0, n_big}, {n_big, N - n_big}};
+            if (t < split_t * 0.999) {
+                split_t = t;
+                split = Plan{2, {b, c}, {0, n_big}, {n_big, N - n_big}};
             }
         }
     }
-    return best;
+    return split_t < best_t * 0.97 ? split : best;   // a second launch must clearly pay for itself
 }
 
 }  // namespace
