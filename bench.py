@@ -645,7 +645,7 @@ def cpu_model():
 # algorithmic bytes per launch).  Template argument MODE 2 is the SwiGLU
 # epilogue, which only the gate/up projection uses.
 TRAFFIC_KERNELS = {
-    "gemm_up_7b_t2": ("gemm_bf16.hip", r"gemm_\w+_kernel<[^>]*, 2>",
+    "gemm_up_7b_t2": ("gemm_bf16.hip", r"gemm_\w+_kernel<(?:[^>]*, )?2>",
                       2 * (2048 * 4096 + 11008 * 4096 + 2048 * 5504)),
     "gemv_up_7b_t4": ("decode.hip", r"gemv_kernel<1, \d+, \d+, 2, true, false, \d+>",
                       2 * (5504 * 4096 + 4096 + 2752)),
@@ -783,7 +783,7 @@ def summarize_mfma(pmc_dir):
         util = statistics.mean(x.get("MfmaUtil", float("nan")) for x in ds)
         gf = statistics.mean(x.get("MfmaFlopsBF16", float("nan")) for x in ds) / 1e9
         ghz = statistics.mean(x.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcc / (x["us"] * 1e3) for x in ds)
-        m = re.search(r"gemm_\w+_kernel<[^>]*, (\d)>", name)
+        m = re.search(r"gemm_\w+_kernel<(?:[^>]*, )?(\d)>", name)
         label = (re.search(r"(gemm_\w+_kernel<[^>]*>|attn_prefill_kernel\w*)", name) or re.search(r".*", name)).group(0)
         if m:
             label += f" ({mode_of.get(m.group(1), '')})"
