@@ -60,9 +60,10 @@ __device__ __forceinline__ void wait_vm() {
 
 // Write the accumulator tile of one wave.  acc[i][j][r] sits at row
 // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of MFMA tile (i, j).
-template <int FM, int FN, int MODE>
+template <int FM, int FN, int MODE, int QB = 16>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& epi, int lane, int wrow0,
                                          int wcol0, int M, int N) {
+    static_assert(QB == 4 || QB == 8 || QB == 16, "rotary gather batch");
     const int col_in = lane & 31;
     const int row_in = 4 * (lane >> 5);
     const int cb = epi.col0;   // this launch's first output column (bounds stay launch-relative)
@@ -143,49 +144,56 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
             const bool paged = region != 0 && q.table != nullptr;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                // The lane's 16 rows of this MFMA tile: rotation factors and
-                // destination rows (block-table reads included) are gathered
-                // first so that their loads are in flight together.
                 const int row0 = wrow0 + i * 32 + row_in;
                 const int b0 = row0 / q.S, s0 = row0 - b0 * q.S;
-                float cs[16], sn[16];
-                int key[16], ps[16];   // key: sequence, or pool block of a paged cache
-                bool ok[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row0 + 8 * (r >> 2) + (r & 3);
-                    const int n = s0 + 8 * (r >> 2) + (r & 3);
-                    int w = (int)((float)n * inv_s);
-                    const int t = n - w * q.S;
-                    w = t < 0 ? w - 1 : (t >= q.S ? w + 1 : w);
-                    const int b = row < M ? b0 + w : b_last;
-                    const int s = row < M ? n - w * q.S : s_last;
-                    const int pos = base_pos + s;
-                    cs[r] = 1.f;
-                    sn[r] = 0.f;
-                    if (rot) {
-                        cs[r] = q.rope_cos[(long long)pos * half + i1];
-                        sn[r] = q.rope_sin[(long long)pos * half + i1];
+                for (int r0 = 0; r0 < 16; r0 += QB) {
+                    // QB of the lane's 16 rows of this MFMA tile: rotation
+                    // factors and destination rows (block-table reads
+                    // included) are gathered first so that their loads are in
+                    // flight together.
+                    float cs[QB], sn[QB];
+                    int key[QB], ps[QB];   // key: sequence, or pool block of a paged cache
+                    bool ok[QB];
+#pragma unroll
+                    for (int rq = 0; rq < QB; ++rq) {
+                        const int r = r0 + rq;
+                        const int row = row0 + 8 * (r >> 2) + (r & 3);
+                        const int n = s0 + 8 * (r >> 2) + (r & 3);
+                        int w = (int)((float)n * inv_s);
+                        const int t = n - w * q.S;
+                        w = t < 0 ? w - 1 : (t >= q.S ? w + 1 : w);
+                        const int b = row < M ? b0 + w : b_last;
+                        const int s = row < M ? n - w * q.S : s_last;
+                        const int pos = base_pos + s;
+                        cs[rq] = 1.f;
+                        sn[rq] = 0.f;
+                        if (rot) {
+                            cs[rq] = q.rope_cos[(long long)pos * half + i1];
+                            sn[rq] = q.rope_sin[(long long)pos * half + i1];
+                        }
+                        key[rq] = paged ? kv_block(b, pos, q.table, q.bsz, q.max_blocks) : b;
+                        ps[rq] = s;
+                        ok[rq] = row < M && gcol < N && (region == 0 || pos < q.ld_seq);
                     }
-                    key[r] = paged ? kv_block(b, pos, q.table, q.bsz, q.max_blocks) : b;
-                    ps[r] = s;
-                    ok[r] = row < M && gcol < N && (region == 0 || pos < q.ld_seq);
-                }
-                // One wait for all of them: with the predicated stores below,
-                // the compiler would otherwise wait per row, and on this
-                // architecture such a wait also covers the stores before it.
-                wait_vm<0>();
+                    // One wait for all of them: with the predicated stores
+                    // below, the compiler would otherwise wait per row, and on
+                    // this architecture such a wait also covers the stores
+                    // before it.
+                    wait_vm<0>();
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float y1 = acc[i][2 * p][r], y2 = acc[i][2 * p + 1][r];
-                    const float o1 = y1 * cs[r] - y2 * sn[r];
-                    const float o2 = y2 * cs[r] + y1 * sn[r];
-                    const long long off =
-                        paged ? kv_row_in_block(key[r], head, base_pos + ps[r], q.kvl, q.bsz, d)
-                              : (((long long)key[r] * nh + head) * ld + poff + ps[r]) * d;
-                    if (ok[r]) {
-                        dbase[off + i1] = f2bf(o1);
-                        dbase[off + i1 + half] = f2bf(o2);
+                    for (int rq = 0; rq < QB; ++rq) {
+                        const int r = r0 + rq;
+                        const float y1 = acc[i][2 * p][r], y2 = acc[i][2 * p + 1][r];
+                        const float o1 = y1 * cs[rq] - y2 * sn[rq];
+                        const float o2 = y2 * cs[rq] + y1 * sn[rq];
+                        const long long off =
+                            paged ? kv_row_in_block(key[rq], head, base_pos + ps[rq], q.kvl, q.bsz, d)
+                                  : (((long long)key[rq] * nh + head) * ld + poff + ps[rq]) * d;
+                        if (ok[rq]) {
+                            dbase[off + i1] = f2bf(o1);
+                            dbase[off + i1 + half] = f2bf(o2);
+                        }
                     }
                 }
             }
@@ -642,25 +650,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
 }
 
 // ---------------------------------------------------------------------------
-// Producer/consumer 256x256 tile, BK 64, twelve waves.  Waves 0-7 (two per
-// SIMD, a 2 x 4 grid of 128x64 accumulator tiles) only read MFMA fragments
-// from LDS and issue MFMAs; waves 8-11 (one per SIMD) only move tiles from
-// global memory into LDS.  With the loads and LDS writes on waves of their
+// Producer/consumer tile (256x256 as 2 x 4 waves of 128x64, or 256x192 as
+// 8 x 1 waves of 32x192), BK 64, twelve waves.  Waves 0-7 (two per SIMD) only
+// read MFMA fragments from LDS and issue MFMAs; waves 8-11 (one per SIMD) only
+// move tiles from global memory into LDS.  With the loads and LDS writes on waves of their
 // own, the MFMA waves never wait for global memory and never issue a
 // memory-unit instruction.  Two 64 KB LDS stages: while the MFMA waves read
 // tile kt from one, the producers write tile kt+1 into the other; one barrier
 // per tile hands both over.  Register budget: three waves per SIMD, 168 each
-// (128 accumulators + one set of fragments; two register sets of staged
-// loads on the producers).
-template <int MODE>
+// (up to 128 accumulators + one set of fragments; two register sets of
+// staged loads on the producers); the rotary epilogue gathers 8 rows at a
+// time to stay inside it.
+template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A, long long lda,
                                                       const bf16* __restrict__ B, long long ldb, int M, int N,
                                                       int K, Epilogue epi, int tiles_m, int tiles_n) {
-    constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4, KK = 4;
+    constexpr int BK = 64, KK = 4;
     constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
     constexpr int STAGE = (BM + BN) * BK;
     constexpr int RS = 32;                       // rows per producer load step (256 threads x 16 B)
     constexpr int NL = (BM + BN) / RS;           // 16-byte loads per producer thread per tile
+    static_assert(WM * WN == 8 && FN % 2 == 0 && BM % RS == 0 && BN % RS == 0, "tile shape");
     __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -758,7 +768,7 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
             __syncthreads();
         }
     }
-    epilogue<FM, FN, MODE>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+    epilogue<FM, FN, MODE, 8>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -868,6 +878,7 @@ const Cfg kCfgs[] = {
     {256, 128, 1.00f, 1},  // 12 register-pipelined 256x128 BK64, 8 waves
     {256, 192, 0.84f, 1},  // 13 register-pipelined 256x192 BK64, 8 waves of 32x192
     {256, 256, 1.12f, 1},  // 14 producer/consumer 256x256 BK64, 8 MFMA waves + 4 load waves
+    {256, 192, 1.10f, 1},  // 15 producer/consumer 256x192 BK64, 8 MFMA waves of 32x192 + 4 load waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -894,11 +905,11 @@ void launch_pipe(const Args& a) {
     hipLaunchKernelGGL((gemm_dma_pipe_kernel<BM, BN, BK, ST, MODE>), dim3(tm * tn), dim3(256), 0, a.st, a.A, a.lda,
                        a.B, a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
 }
-template <int MODE>
+template <int BM, int BN, int WM, int WN, int MODE>
 void launch_ws(const Args& a) {
-    const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
-    hipLaunchKernelGGL((gemm_ws_kernel<MODE>), dim3(tm * tn), dim3(768), 0, a.st, a.A, a.lda, a.B, a.ldb, a.M,
-                       a.N, a.K, a.epi, tm, tn);
+    const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WM, WN, MODE>), dim3(tm * tn), dim3(768), 0, a.st, a.A, a.lda, a.B,
+                       a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
 }
 
 template <int BM, int BN, int WM, int WN, int MODE>
@@ -931,7 +942,8 @@ void launch_cfg(int c, const Args& a) {
         case 11: launch_vgpr<256, 256, 2, 4, MODE>(a); break;
         case 12: launch_vgpr<256, 128, 4, 2, MODE>(a); break;
         case 13: launch_vgpr<256, 192, 8, 1, MODE>(a); break;
-        default: launch_ws<MODE>(a); break;
+        case 14: launch_ws<256, 256, 2, 4, MODE>(a); break;
+        default: launch_ws<256, 192, 8, 1, MODE>(a); break;
     }
 }
 
@@ -940,8 +952,8 @@ void launch_cfg(int c, const Args& a) {
 // ring with the rotary one.
 bool usable(int c, int mode) {
     if (c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE)) return false;
-    // the rotary epilogue does not fit the producer/consumer kernel's register budget
-    return !((c == 4 || c == 14) && mode == EPI_QKV);
+    // the rotary epilogue spills in the producer/consumer kernels' register budget
+    return !((c == 4 || c == 14 || c == 15) && mode == EPI_QKV);
 }
 
 // Modelled time of one launch: rounds of 256 tiles (one per CU), each the
