@@ -121,21 +121,30 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
         // compiler cannot prove the stores leave these locations alone, so a
         // load placed after a store waits for it.
         const int base_pos = q.pos_dev ? *q.pos_dev : q.pos0;
-        // Token row -> (sequence b, offset s).  One integer division per
-        // 32-row tile gives the first row's pair; the other rows lie at most
-        // 27 rows further, so their extra wrap count n / S is below 29 and a
-        // float quotient corrected by one step is exact.  Rows past M take
-        // row M-1's pair (their stores are dropped; their reads stay in range).
+        // Token row -> (sequence b, offset s), without integer divisions (their
+        // reciprocal constants stay live through the epilogue).  The first row
+        // of each 32-row tile: a double quotient corrected by one step, exact
+        // for any int row.  The other rows lie at most 27 rows further, so
+        // their extra wrap count n / S is below 29 and a float quotient
+        // corrected by one step is exact.  Rows past M take row M-1's pair
+        // (their stores are dropped; their reads stay in range).
         const float inv_s = 1.f / (float)q.S;
-        const int b_last = (M - 1) / q.S, s_last = (M - 1) - b_last * q.S;
+        const double inv_sd = 1.0 / (double)q.S;
+        auto seq_of = [&](int row) {
+            int w = (int)((double)row * inv_sd);
+            const int t = row - w * q.S;
+            return t < 0 ? w - 1 : (t >= q.S ? w + 1 : w);
+        };
+        const int b_last = seq_of(M - 1), s_last = (M - 1) - b_last * q.S;
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
             const int gcol = wcol0 + p * 64;          // launch-relative (bounds)
             const int acol = cb + gcol;               // absolute packed column
             const int region = acol < qcols ? 0 : (acol < qcols + kcols ? 1 : 2);
             const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
-            const int head = (acol - base) / d;
-            const int i1 = 32 * (((acol - base) % d) >> 6) + col_in;
+            // d is 64 or 128 (checked when a shard is created): shifts, no divisions
+            const int head = (acol - base) >> (31 - __builtin_clz(d));
+            const int i1 = 32 * (((acol - base) & (d - 1)) >> 6) + col_in;
             const bool rot = region < 2 && q.rope_cos != nullptr;
             bf16* dbase = region == 0 ? (bf16*)q.q : (region == 1 ? (bf16*)q.k : (bf16*)q.v);
             const int nh = region == 0 ? q.hl : q.kvl;
@@ -145,7 +154,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int row0 = wrow0 + i * 32 + row_in;
-                const int b0 = row0 / q.S, s0 = row0 - b0 * q.S;
+                const int b0 = seq_of(row0), s0 = row0 - b0 * q.S;
 #pragma unroll
                 for (int r0 = 0; r0 < 16; r0 += QB) {
                     // QB of the lane's 16 rows of this MFMA tile: rotation
@@ -650,17 +659,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
 }
 
 // ---------------------------------------------------------------------------
-// Producer/consumer tile (256x256 as 2 x 4 waves of 128x64, or 256x192 as
-// 8 x 1 waves of 32x192), BK 64, twelve waves.  Waves 0-7 (two per SIMD) only
-// read MFMA fragments from LDS and issue MFMAs; waves 8-11 (one per SIMD) only
-// move tiles from global memory into LDS.  With the loads and LDS writes on waves of their
-// own, the MFMA waves never wait for global memory and never issue a
-// memory-unit instruction.  Two 64 KB LDS stages: while the MFMA waves read
-// tile kt from one, the producers write tile kt+1 into the other; one barrier
-// per tile hands both over.  Register budget: three waves per SIMD, 168 each
-// (up to 128 accumulators + one set of fragments; two register sets of
-// staged loads on the producers); the rotary epilogue gathers 8 rows at a
-// time to stay inside it.
+// Producer/consumer tile, BK 64, twelve waves: 256x256 as 2 x 4 MFMA waves
+// of 128x64, 256x192 as 8 x 1 of 32x192, or 256x128 as 4 x 2 of 64x64.
+// Waves 0-7 (two per SIMD) only read MFMA fragments from LDS and issue MFMAs;
+// waves 8-11 (one per SIMD) only move tiles from global memory into LDS.
+// With the loads and LDS writes on waves of their own, the MFMA waves never
+// wait for global memory and never issue a memory-unit instruction.  Two LDS
+// stages: while the MFMA waves read tile kt from one, the producers write
+// tile kt+1 into the other; one barrier per tile hands both over.  Register
+// budget: three waves per SIMD, 168 each (up to 128 accumulators + one set of
+// fragments; two register sets of staged loads on the producers); the rotary
+// epilogue gathers 4 rows at a time to stay inside it.
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A, long long lda,
                                                       const bf16* __restrict__ B, long long ldb, int M, int N,
@@ -768,7 +777,7 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
             __syncthreads();
         }
     }
-    epilogue<FM, FN, MODE, 8>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+    epilogue<FM, FN, MODE, 4>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -879,6 +888,7 @@ const Cfg kCfgs[] = {
     {256, 192, 0.84f, 1},  // 13 register-pipelined 256x192 BK64, 8 waves of 32x192
     {256, 256, 1.12f, 1},  // 14 producer/consumer 256x256 BK64, 8 MFMA waves + 4 load waves
     {256, 192, 1.10f, 1},  // 15 producer/consumer 256x192 BK64, 8 MFMA waves of 32x192 + 4 load waves
+    {256, 128, 1.02f, 1},  // 16 producer/consumer 256x128 BK64, 8 MFMA waves of 64x64 + 4 load waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -943,7 +953,8 @@ void launch_cfg(int c, const Args& a) {
         case 12: launch_vgpr<256, 128, 4, 2, MODE>(a); break;
         case 13: launch_vgpr<256, 192, 8, 1, MODE>(a); break;
         case 14: launch_ws<256, 256, 2, 4, MODE>(a); break;
-        default: launch_ws<256, 192, 8, 1, MODE>(a); break;
+        case 15: launch_ws<256, 192, 8, 1, MODE>(a); break;
+        default: launch_ws<256, 128, 4, 2, MODE>(a); break;
     }
 }
 
@@ -952,8 +963,7 @@ void launch_cfg(int c, const Args& a) {
 // ring with the rotary one.
 bool usable(int c, int mode) {
     if (c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE)) return false;
-    // the rotary epilogue spills in the producer/consumer kernels' register budget
-    return !((c == 4 || c == 14 || c == 15) && mode == EPI_QKV);
+    return !(c == 4 && mode == EPI_QKV);
 }
 
 // Modelled time of one launch: rounds of 256 tiles (one per CU), each the

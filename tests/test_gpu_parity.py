@@ -698,7 +698,7 @@ def test_every_gemm_config(ffn):
     ref_a = O.attn_stage(L.exact["x"], L.W, L.spec, 2, 1)
     ref_m = O.mlp_stage(h.float().numpy(), L.W, L.spec, 2, 1)
     sh = L.shard(2, 1)
-    n_cfg = 16
+    n_cfg = 17
     assert N.lib().tp_tune_set_gemm_config(n_cfg) == N.TP_E_ARG   # the table has exactly n_cfg entries
     try:
         for cfg in range(n_cfg):
