@@ -294,12 +294,11 @@ int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *l
  * output tiles; 3..10: direct-to-LDS rings 256x256 (K-step 64, 2 stages),
  * 256x256 (32, 4), 256x128 (64, 3), 128x128 (64, 4), 128x128 (64, 2),
  * 256x128 (32, 4), 128x384 (32, 4), 128x384 (32, 3); 11..13: register-
- * pipelined 256x256, 256x128 and 256x192 (K-step 64, eight waves); 14..15:
- * producer/consumer 256x256 and 256x192 (eight MFMA waves, four load
- * waves).  A configuration that a projection cannot use (the 256x256 DMA
- * rings and the producer/consumer tiles with the rotary epilogue, the
- * two-stage ring also with the GELU and plain-store ones) falls back to the
- * shape-based choice.
+ * pipelined 256x256, 256x128 and 256x192 (K-step 64, eight waves); 14..16:
+ * producer/consumer 256x256, 256x192 and 256x128 (eight MFMA waves, four
+ * load waves).  A configuration that a projection cannot use (the 256x256
+ * DMA rings with the rotary epilogue, the two-stage ring also with the GELU
+ * and plain-store ones) falls back to the shape-based choice.
  * Process-wide, not thread-safe.
  * TP_E_ARG if out of range. */
 int tp_tune_set_gemm_config(int cfg);
