@@ -752,29 +752,63 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
-    bf16x8 fa[FM], fb[FN];
+    // Fragments of the next k-slice are read while the current one's MFMAs
+    // run, where the register budget allows two sets (not with 128
+    // accumulators); the compiler otherwise reads each fragment right before
+    // its MFMA.
+    constexpr bool DB = FM * FN * 16 + 8 * (FM + FN) <= 152;
+    bf16x8 fa[DB ? 2 : 1][FM], fb[DB ? 2 : 1][FN];
+    auto rd = [&](int st, int kk, int buf) {
+        const bf16* a_s = smem + st * STAGE + (wm * TM + frow) * BK;
+        const bf16* b_s = smem + st * STAGE + BM * BK + (wn * TN + frow) * BK;
+        const int c = swz<8>(frow, 2 * kk + khalf) << 3;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
+    };
+    auto mm = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
     __syncthreads();
     // An odd tile count runs one more (all-zero) tile: the loop stays in pairs
     // so that the stage index is static, like the producers' loop.
-    for (int kt = 0; kt < KT; kt += 2) {
+    if constexpr (DB) {
+        rd(0, 0, 0);
+        for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const bf16* a_s = smem + st * STAGE + (wm * TM + frow) * BK;
-            const bf16* b_s = smem + st * STAGE + BM * BK + (wn * TN + frow) * BK;
+            for (int st = 0; st < 2; ++st) {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int c = swz<8>(frow, 2 * kk + khalf) << 3;
+                for (int kk = 0; kk < KK; ++kk) {
+                    const int cur = kk & 1;
+                    if (kk + 1 < KK) rd(st, kk + 1, cur ^ 1);
+                    mm(cur);
 #pragma unroll
-                for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(a_s + i * 32 * BK + c);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(b_s + j * 32 * BK + c);
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    for (int q = 0; q < FM * FN; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __syncthreads();
+                rd(st ^ 1, 0, 0);   // the next tile's first slice, published by the barrier
             }
-            __syncthreads();
+        }
+    } else {
+        for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    rd(st, kk, 0);
+                    mm(0);
+                }
+                __syncthreads();
+            }
         }
     }
     epilogue<FM, FN, MODE, 4>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
