@@ -60,7 +60,7 @@ __device__ __forceinline__ float half_sum(float v) {
 template <int D, int KG>
 __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
-    int hl, int kvl, int S, int ld_seq, float scale_log2) {
+    int hl, int kvl, int S, int ld_seq, float scale_log2, int B) {
     constexpr int KC = D / 8;        // 16-byte chunks per K row
     constexpr int NT = D / 32;       // O^T tiles (32 dims each)
     constexpr int KSTEPS = D / 16;   // k16 steps of the QK^T contraction
@@ -80,9 +80,15 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
     bf16* sK = smem + grp * BUF;
     bf16* sVt = sK + BKV * D;
     const int h = lane >> 5, col = lane & 31;
+    // Work-group -> (query block, head, sequence): the query block is the
+    // slowest index, counted from the latest (longest) one, so the whole grid
+    // goes out in order of decreasing work and the dispatcher can pack the
+    // short blocks behind the long ones.
     const int nqb = (S + BQ - 1) / BQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;  // longest (latest) query blocks first
-    const int head = blockIdx.y, b = blockIdx.z;
+    const int nhb = hl * B;
+    const int rank = blockIdx.x / nhb, hb = blockIdx.x - rank * nhb;
+    const int qb = nqb - 1 - rank;
+    const int head = hb % hl, b = hb / hl;
     const int kvh = head / (hl / kvl);
     const int q0 = qb * BQ + qw * 32;
     const int qme = q0 + col;                  // this lane's query
@@ -316,26 +322,26 @@ void set_attn_groups(int kg) { g_attn_groups = kg; }
 void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl, int S,
                        int ld_seq, int d, hipStream_t st) {
     if (B <= 0 || S <= 0) return;
-    dim3 grid((S + BQ - 1) / BQ, hl, B);
+    dim3 grid((S + BQ - 1) / BQ * hl * B);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     // Two key groups while the grid alone leaves a SIMD with at most one wave
     // (two 4-wave work-groups fit a CU): up to 512 work-groups.
-    const long long wgs = (long long)grid.x * grid.y * grid.z;
+    const long long wgs = grid.x;
     const int kg = g_attn_groups ? g_attn_groups : (wgs <= 512 ? 2 : 1);
     if (d == 128) {
         if (kg == 2)
             hipLaunchKernelGGL((attn_prefill_kernel<128, 2>), grid, dim3(512), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2);
+                               scale_log2, B);
         else
             hipLaunchKernelGGL((attn_prefill_kernel<128, 1>), grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2);
+                               scale_log2, B);
     } else {
         if (kg == 2)
             hipLaunchKernelGGL((attn_prefill_kernel<64, 2>), grid, dim3(512), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2);
+                               scale_log2, B);
         else
             hipLaunchKernelGGL((attn_prefill_kernel<64, 1>), grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2);
+                               scale_log2, B);
     }
 }
 
