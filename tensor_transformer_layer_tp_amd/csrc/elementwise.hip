@@ -186,12 +186,13 @@ __global__ __launch_bounds__(256) void gather_kernel(Pieces pieces, int t, long 
 }
 
 // cos/sin of p * theta^(-2i/d) for p < npos, i < d/2, evaluated in double.
-__global__ void rope_table_kernel(float* cos_t, float* sin_t, int npos, int d, double theta) {
+__global__ void rope_table_kernel(float* cos_t, float* sin_t, double* rev, int npos, int d, double theta) {
     const int half = d / 2;
     const long long total = (long long)npos * half;
     for (long long idx = blockIdx.x * 256LL + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
         const int p = (int)(idx / half), i = (int)(idx % half);
         const double inv = pow(theta, -2.0 * i / (double)d);
+        if (p == 0) rev[i] = inv * 0.15915494309189535;   // theta_i / (2 pi): turns per position
         const double a = (double)p * inv;
         cos_t[idx] = (float)cos(a);
         sin_t[idx] = (float)sin(a);
@@ -255,10 +256,10 @@ void partial_reduce(const float* const* parts, int t, const void* residual, void
 #undef TP_RED
 }
 
-void rope_table(float* cos_t, float* sin_t, int npos, int d, float theta, hipStream_t st) {
+void rope_table(float* cos_t, float* sin_t, double* rev, int npos, int d, float theta, hipStream_t st) {
     long long total = (long long)npos * (d / 2);
     int blocks = (int)std::min<long long>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, st, cos_t, sin_t, npos, d, (double)theta);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, st, cos_t, sin_t, rev, npos, d, (double)theta);
 }
 
 }  // namespace tp

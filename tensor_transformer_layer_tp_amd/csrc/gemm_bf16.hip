@@ -136,34 +136,54 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
             return t < 0 ? w - 1 : (t >= q.S ? w + 1 : w);
         };
         const int b_last = seq_of(M - 1), s_last = (M - 1) - b_last * q.S;
+        // d is 64 or 128 (checked when a shard is created): shifts, no divisions
+        const int dlog = 31 - __builtin_clz(d);
+        auto dim_of = [&](int p) { return 32 * (((cb + wcol0 + p * 64) & (d - 1)) >> 6) + col_in; };
+        // rotation turns per position of each pair's dim, read before any store
+        double turns_p[FN / 2];
+#pragma unroll
+        for (int p = 0; p < FN / 2; ++p) turns_p[p] = q.rope_rev != nullptr ? q.rope_rev[dim_of(p)] : 0.0;
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
             const int gcol = wcol0 + p * 64;          // launch-relative (bounds)
             const int acol = cb + gcol;               // absolute packed column
             const int region = acol < qcols ? 0 : (acol < qcols + kcols ? 1 : 2);
             const int base = region == 0 ? 0 : (region == 1 ? qcols : qcols + kcols);
-            // d is 64 or 128 (checked when a shard is created): shifts, no divisions
-            const int head = (acol - base) >> (31 - __builtin_clz(d));
+            const int head = (acol - base) >> dlog;
             const int i1 = 32 * (((acol - base) & (d - 1)) >> 6) + col_in;
-            const bool rot = region < 2 && q.rope_cos != nullptr;
+            const bool rot = region < 2 && q.rope_rev != nullptr;
             bf16* dbase = region == 0 ? (bf16*)q.q : (region == 1 ? (bf16*)q.k : (bf16*)q.v);
             const int nh = region == 0 ? q.hl : q.kvl;
             const int ld = region == 0 ? q.S : q.ld_seq;
             const int poff = region == 0 ? 0 : base_pos;   // q is stored by token index, k/v by position
             const bool paged = region != 0 && q.table != nullptr;
+            // The rotation of row position pos is pos * theta_i turns: its
+            // fraction, formed in double (exact for any position), goes to the
+            // hardware sine and cosine, which take turns (|error| <= 1.3e-7 on
+            // [0, 1)).  No table reads: without a block table the epilogue
+            // issues no loads at all.
+            const double turns = turns_p[p];
+            auto rotation = [&](int pos, float& c, float& sn) {
+                c = 1.f;
+                sn = 0.f;
+                if (rot) {
+                    const double a = (double)pos * turns;
+                    const float f = (float)(a - floor(a));
+                    c = __builtin_amdgcn_cosf(f);
+                    sn = __builtin_amdgcn_sinf(f);
+                }
+            };
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int row0 = wrow0 + i * 32 + row_in;
                 const int b0 = seq_of(row0), s0 = row0 - b0 * q.S;
 #pragma unroll
                 for (int r0 = 0; r0 < 16; r0 += QB) {
-                    // QB of the lane's 16 rows of this MFMA tile: rotation
-                    // factors and destination rows (block-table reads
-                    // included) are gathered first so that their loads are in
-                    // flight together.
-                    float cs[QB], sn[QB];
+                    // QB of the lane's 16 rows of this MFMA tile.  With a block
+                    // table, the table reads of the QB rows are issued together
+                    // and waited for once (a wait per row would also wait for
+                    // the stores before it).
                     int key[QB], ps[QB];   // key: sequence, or pool block of a paged cache
-                    bool ok[QB];
 #pragma unroll
                     for (int rq = 0; rq < QB; ++rq) {
                         const int r = r0 + rq;
@@ -173,33 +193,29 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                         const int t = n - w * q.S;
                         w = t < 0 ? w - 1 : (t >= q.S ? w + 1 : w);
                         const int b = row < M ? b0 + w : b_last;
-                        const int s = row < M ? n - w * q.S : s_last;
-                        const int pos = base_pos + s;
-                        cs[rq] = 1.f;
-                        sn[rq] = 0.f;
-                        if (rot) {
-                            cs[rq] = q.rope_cos[(long long)pos * half + i1];
-                            sn[rq] = q.rope_sin[(long long)pos * half + i1];
-                        }
-                        key[rq] = paged ? kv_block(b, pos, q.table, q.bsz, q.max_blocks) : b;
-                        ps[rq] = s;
-                        ok[rq] = row < M && gcol < N && (region == 0 || pos < q.ld_seq);
+                        ps[rq] = row < M ? n - w * q.S : s_last;
+                        key[rq] = b;
                     }
-                    // One wait for all of them: with the predicated stores
-                    // below, the compiler would otherwise wait per row, and on
-                    // this architecture such a wait also covers the stores
-                    // before it.
-                    wait_vm<0>();
+                    if (paged) {
+#pragma unroll
+                        for (int rq = 0; rq < QB; ++rq)
+                            key[rq] = kv_block(key[rq], base_pos + ps[rq], q.table, q.bsz, q.max_blocks);
+                        wait_vm<0>();
+                    }
 #pragma unroll
                     for (int rq = 0; rq < QB; ++rq) {
                         const int r = r0 + rq;
+                        const int row = row0 + 8 * (r >> 2) + (r & 3);
+                        const int pos = base_pos + ps[rq];
+                        float c, sn;
+                        rotation(pos, c, sn);
                         const float y1 = acc[i][2 * p][r], y2 = acc[i][2 * p + 1][r];
-                        const float o1 = y1 * cs[rq] - y2 * sn[rq];
-                        const float o2 = y2 * cs[rq] + y1 * sn[rq];
+                        const float o1 = y1 * c - y2 * sn;
+                        const float o2 = y2 * c + y1 * sn;
                         const long long off =
-                            paged ? kv_row_in_block(key[rq], head, base_pos + ps[rq], q.kvl, q.bsz, d)
+                            paged ? kv_row_in_block(key[rq], head, pos, q.kvl, q.bsz, d)
                                   : (((long long)key[rq] * nh + head) * ld + poff + ps[rq]) * d;
-                        if (ok[rq]) {
+                        if (row < M && gcol < N && (region == 0 || pos < q.ld_seq)) {
                             dbase[off + i1] = f2bf(o1);
                             dbase[off + i1 + half] = f2bf(o2);
                         }

@@ -26,6 +26,8 @@ struct QKVDest {
     int ld_seq;         // cache capacity (positions)
     const float* rope_cos;  // [max_pos, d/2] or nullptr (no rotary embedding)
     const float* rope_sin;
+    const double* rope_rev; // [d/2] turns per position (theta_i / 2 pi); the projection GEMM
+                            // forms the rotation from it instead of reading the tables
     // paged cache: k/v are pools [blocks, kvl, bsz, d]; position p of sequence
     // b lives in block table[b * max_blocks + p / bsz] at row p % bsz
     const int* table;   // nullptr: contiguous [B, kvl, ld_seq, d]
@@ -131,7 +133,9 @@ void attn_f32(const float* Q, const float* K, const float* V, float* O, int B, i
 // ---- shared ----
 void partial_reduce(const float* const* parts, int t, const void* residual, void* out, long long n,
                     int bf16_out, hipStream_t st);
-void rope_table(float* cos_t, float* sin_t, int npos, int d, float theta, hipStream_t st);
+// cos/sin of p * theta_i for p < npos, i < d/2 ([npos, d/2] fp32), and rev[i] =
+// theta_i / (2 pi) in double (the rotation per position in turns)
+void rope_table(float* cos_t, float* sin_t, double* rev, int npos, int d, float theta, hipStream_t st);
 // out = rank-order concatenation of t pieces of piece_bytes each (multiple of 16, 16-byte aligned)
 void all_gather(const void* const* pieces, int t, long long piece_bytes, void* out, hipStream_t st);
 

@@ -37,6 +37,7 @@ struct tp_shard {
     char* ws;
     size_t ws_bytes;
     float *rcos, *rsin;
+    double* rrev;     // [d/2] rotary turns per position
     int rope_npos;
     // offsets of the last call's workspace tensors (debug view)
     size_t off_n, off_o, off_act;
@@ -113,13 +114,17 @@ int ensure_rope(tp_shard* s, int npos, hipStream_t st) {
         if (e1 != hipSuccess) return hip_fail(e1, "hipFree(rope)");
         if (e2 != hipSuccess) return hip_fail(e2, "hipFree(rope)");
     }
+    if (!s->rrev && hipMalloc((void**)&s->rrev, (size_t)(s->d / 2) * sizeof(double)) != hipSuccess) {
+        s->rrev = nullptr;
+        return TP_E_NOMEM;
+    }
     size_t bytes = (size_t)want * (s->d / 2) * sizeof(float);
     if (hipMalloc((void**)&s->rcos, bytes) != hipSuccess || hipMalloc((void**)&s->rsin, bytes) != hipSuccess) {
         if (s->rcos) (void)hipFree(s->rcos);
         s->rcos = s->rsin = nullptr;
         return TP_E_NOMEM;
     }
-    rope_table(s->rcos, s->rsin, want, s->d, s->o.rope_theta, st);
+    rope_table(s->rcos, s->rsin, s->rrev, want, s->d, s->o.rope_theta, st);
     LAUNCH_CHECK("rope_table");
     s->rope_npos = want;
     return TP_OK;
@@ -180,6 +185,7 @@ int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void
     epi.qkv.ld_seq = ld_seq;
     epi.qkv.rope_cos = s->o.rope ? s->rcos : nullptr;
     epi.qkv.rope_sin = s->o.rope ? s->rsin : nullptr;
+    epi.qkv.rope_rev = s->o.rope ? s->rrev : nullptr;
     if (s->o.dtype == TP_BF16)
         gemm_bf16((const bf16*)n_in, s->hidden, (const bf16*)s->w_qkv, s->hidden, (int)M, s->nqkv, s->hidden, epi, st);
     else
@@ -659,7 +665,7 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.mode = EPI_QKV;
             epi.qkv = QKVDest{1, L, kv->dlen, s->hl, s->kvl, s->d, qbuf, kv->k, kv->v, kv->max_seq,
                               s->o.rope ? s->rcos : nullptr, s->o.rope ? s->rsin : nullptr,
-                              kv->table, kv->block_size, kv->max_blocks};
+                              s->o.rope ? s->rrev : nullptr, kv->table, kv->block_size, kv->max_blocks};
             KTimer kt(s, TP_K_GEMV_QKV, st);
             const void* g1 = s->o.rmsnorm && !prenorm ? s->g1 : nullptr;
             TRY(launch_gemv(s, x, batch, g1, s->w_qkv, s->nqkv, s->hidden, epi, ws + lay.n, ws + lay.scr, st, 0));
@@ -869,7 +875,7 @@ void tp_shard_destroy(tp_shard* s) {
     if (!s) return;
     for (hipEvent_t e : s->ev)
         if (e) (void)hipEventDestroy(e);
-    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin,
+    void* bufs[] = {s->w_qkv, s->w_o, s->w_up, s->w_down, s->g1, s->g2, s->ws, s->rcos, s->rsin, s->rrev,
                     s->q8[0], s->q8[1], s->q8[2], s->q8[3], s->s8[0], s->s8[1], s->s8[2], s->s8[3]};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
