@@ -226,6 +226,70 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
     }
 }
 
+// Epilogue through LDS (SwiGLU and fp32 partials): the wave writes its
+// accumulator tile, finished, into a private LDS region in row order, then
+// stores whole 16-byte row chunks.  The direct epilogue stores 2 or 4 bytes
+// per lane and instruction (one instruction per accumulator register); this
+// one a sixth to a quarter of the instructions.  The caller guarantees that no
+// other wave touches the region any more (RB bf16 elements, 16-byte aligned).
+template <int FM, int FN, int MODE, int RB>
+__device__ __forceinline__ void epilogue_staged(f32x16 (&acc)[FM][FN], const Epilogue& epi, int lane, int wrow0,
+                                                int wcol0, int M, int N, bf16* sreg) {
+    static_assert(MODE == EPI_SWIGLU || MODE == EPI_F32, "staged epilogue modes");
+    const int col_in = lane & 31;
+    const int row_in = 4 * (lane >> 5);
+    const int cb = epi.col0;
+    if constexpr (MODE == EPI_SWIGLU) {
+        constexpr int OC = FN * 16;        // output columns of the wave's tile (one per gate/up pair)
+        constexpr int OCP = OC + 8;        // padded LDS row (bf16)
+        constexpr int CPR = OC / 8;        // 16-byte chunks per row
+        static_assert(FM * 32 * OCP <= RB, "LDS region");
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int p = 0; p < FN / 2; ++p)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = i * 32 + 8 * (r >> 2) + row_in + (r & 3);
+                    sreg[rl * OCP + p * 32 + col_in] = f2bf(silu_f(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
+                }
+        bf16* o = (bf16*)epi.out;
+#pragma unroll
+        for (int k = 0; k < FM * 32 * CPR / 64; ++k) {
+            const int c = lane + 64 * k;
+            const int rl = c / CPR, ch = c % CPR;
+            const int row = wrow0 + rl;
+            const int gcol = wcol0 + (ch >> 2) * 64;   // the chunk's 64-column input group
+            if (row < M && gcol < N)
+                *(u32x4_t*)(o + (long long)row * epi.ldo + ((cb + wcol0) >> 1) + ch * 8) =
+                    *(const u32x4_t*)(sreg + rl * OCP + ch * 8);
+        }
+    } else {
+        constexpr int TN = FN * 32;
+        constexpr int TNP = TN + 4;        // padded LDS row (fp32)
+        constexpr int CPR = TN / 4;        // 16-byte chunks per row
+        static_assert(32 * TNP * 2 <= RB, "LDS region");
+        float* sf = (float*)sreg;
+        float* o = (float*)epi.out;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {     // 32 rows at a time
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sf[(8 * (r >> 2) + row_in + (r & 3)) * TNP + j * 32 + col_in] = acc[i][j][r];
+#pragma unroll
+            for (int k = 0; k < 32 * CPR / 64; ++k) {
+                const int c = lane + 64 * k;
+                const int rl = c / CPR, ch = c % CPR;
+                const int row = wrow0 + i * 32 + rl;
+                const int col = wcol0 + ch * 4;
+                if (row < M && col < N)
+                    *(u32x4_t*)(o + (long long)row * epi.ldo + cb + col) = *(const u32x4_t*)(sf + rl * TNP + ch * 4);
+            }
+        }
+    }
+}
+
 // Direct-to-LDS load of one 16-byte chunk per lane: lane i of the wave lands
 // at LDS byte m0 + 16 i.  The compiler does not see this as an LDS write, so
 // it adds no conservative waits; the caller waits on vmcnt before the barrier
@@ -827,7 +891,16 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
             }
         }
     }
-    epilogue<FM, FN, MODE, 4>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
+    // Every wave, producers included, has passed the loop's last barrier:
+    // no LDS read or write of the main loop is still pending, so each MFMA
+    // wave may use a private part of the stages for its epilogue.
+    constexpr int RB = 2 * STAGE / 8;
+    constexpr bool staged = (MODE == EPI_SWIGLU && FM * 32 * (FN * 16 + 8) <= RB) ||
+                            (MODE == EPI_F32 && 32 * (FN * 32 + 4) * 2 <= RB);
+    if constexpr (staged)
+        epilogue_staged<FM, FN, MODE, RB>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N, smem + wave * RB);
+    else
+        epilogue<FM, FN, MODE, 4>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N);
 }
 
 // ---------------------------------------------------------------------------
