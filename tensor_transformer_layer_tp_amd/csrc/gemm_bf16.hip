@@ -10,17 +10,22 @@
 // column-parallel = full input times a column slice, row-parallel = matching
 // blocks giving partial results).
 //
-// Structure: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
-// (BM/2) x (BN/2) tile of 32x32 MFMA accumulators (v_mfma_f32_32x32x16_bf16).
-// Two main-loop variants feed the MFMAs from LDS:
-//  * "dma": buffer_load ... lds moves 16-byte chunks straight from HBM into a
-//    ring of ST LDS stages (no staging registers, ST-1 tiles in flight);
-//  * "reg": buffer loads into two register stages, then ds_write into a
-//    double-buffered LDS stage (used where the DMA ring does not fit).
-// LDS rows hold BK bf16 with the 16-byte chunk index XOR-swizzled by row so
-// that the fragment reads of 16 consecutive rows hit distinct bank groups.
-// Work-groups are remapped so that each XCD (hardware places work-group i on
-// XCD i % 8) receives a contiguous, L2-friendly block of tiles.
+// Every family computes 32x32 MFMA accumulator tiles (v_mfma_f32_32x32x16_bf16)
+// from fragments in LDS; they differ in who moves the tiles into LDS:
+//  * producer/consumer (gemm_ws_kernel, the default for large projections):
+//    eight waves only read fragments and issue MFMAs, four more only load
+//    the next tile into registers and write it to the free LDS stage;
+//  * register-pipelined (gemm_vgpr_kernel): eight waves do both, the loads
+//    of tile kt+2 spread over the k-slices of tile kt;
+//  * four-wave kernels in a 2 x 2 grid: "dma" (buffer_load ... lds into a ring
+//    of ST stages, no staging registers) and "reg" (two register stages, then
+//    a double-buffered LDS stage).
+// A planner (plan(), from a per-CU cost model) picks the tile and family per
+// shape, and may run a GEMM as two launches over column ranges.  LDS rows
+// hold BK bf16 with the 16-byte chunk index XOR-swizzled by row so that the
+// fragment reads of 16 consecutive rows hit distinct bank groups.  Work-groups
+// are remapped so that each XCD (hardware places work-group i on XCD i % 8)
+// receives a contiguous, L2-friendly block of tiles.
 #include "kernels.h"
 
 #include <stdint.h>
