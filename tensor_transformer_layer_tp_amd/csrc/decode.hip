@@ -737,10 +737,11 @@ void gemv_mode(const bf16* x, const bf16* gamma, float eps, const void* W, const
 template <int NB, int NI, bool W8, int T>
 void gemv_ni(const bf16* x, const bf16* gamma, float eps, const void* W, const float* ws, int N, int K,
              const Epilogue& epi, hipStream_t st) {
-    // 8 rows per work-group keep 8 x NI loads in flight per thread; 4 rows when
-    // 8 would leave the GPU short of work-groups or the thread short of registers
-    if constexpr (NI <= 2) {
-        if (N / 8 >= 512) {
+    // 8 rows per work-group keep 8 x NI loads in flight per thread; 4 rows
+    // (twice the work-groups) are faster up to N 5504 and for E4M3 rows, and
+    // where 8 would leave the thread short of registers
+    if constexpr (NI <= 2 && !W8) {
+        if (N / 8 >= 1024) {
             if (gamma) gemv_mode<NB, 4, NI, true, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
             else gemv_mode<NB, 4, NI, false, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
             return;
