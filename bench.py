@@ -617,7 +617,7 @@ def cpu_baseline(state):
     h = O.reduce([a0, a1], x, spec)
     m1 = O.mlp_stage(h, ex, spec, w.tp, 1)["partial"]
     steps, t_tot = 0, 0.0
-    while steps < 5 and (t_tot < 10.0 or steps == 0):
+    while steps < 30 and (t_tot < 10.0 or steps == 0):
         t0 = time.perf_counter()
         a0 = O.attn_stage(x, ex, spec, w.tp, 0)["partial"]
         hh = O.reduce([a0, a1], x, spec)
@@ -785,6 +785,9 @@ def summarize_mfma(pmc_dir):
         ghz = statistics.mean(x.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcc / (x["us"] * 1e3) for x in ds)
         m = re.search(r"gemm_\w+_kernel<(?:[^>]*, )?(\d)>", name)
         label = (re.search(r"(gemm_\w+_kernel<[^>]*>|attn_prefill_kernel\w*)", name) or re.search(r".*", name)).group(0)
+        a = re.search(r"attn_prefill_kernelILi(\d+)ELi(\d+)E", name)
+        if a:
+            label = f"attn_prefill_kernel<{a.group(1)}, {a.group(2)}> (causal GQA attention)"
         if m:
             label += f" ({mode_of.get(m.group(1), '')})"
             if m.group(1) == "2":
