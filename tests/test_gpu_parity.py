@@ -542,6 +542,38 @@ def test_kv_full_and_errors():
     torch.cuda.synchronize()
 
 
+def test_empty_inputs():
+    """Zero sequences or zero tokens: the forward calls refuse them before any
+    launch (TP_E_ARG; the output buffer and the cache length stay as they
+    were), and a reduce over zero elements does nothing, called through the C
+    ABI directly with valid buffers."""
+    import ctypes as C
+    from tensor_transformer_layer_tp_amd import _native as N
+    announce("empty inputs")
+    L = Layer(512, 4, 4, 768, batch=1, seq=8, seed=15)
+    sh = L.shard(2, 0)
+    kv = sh.kv_cache(1, 16)
+    sh.prefill(ATTN, L.dev["x"], kv)
+    torch.cuda.synchronize()
+    assert kv.length == 8
+    lib = N.lib()
+    out = torch.full((1, 8, 512), 7.0, device="cuda")
+    xp, op = C.c_void_p(L.dev["x"].data_ptr()), C.c_void_p(out.data_ptr())
+    assert lib.tp_shard_forward_prefill(sh._h, ATTN, xp, 1, 0, kv._h, op, None) == N.TP_E_ARG
+    assert lib.tp_shard_forward_prefill(sh._h, ATTN, xp, 0, 8, kv._h, op, None) == N.TP_E_ARG
+    assert lib.tp_shard_forward_prefill(sh._h, MLP, xp, 1, 0, None, op, None) == N.TP_E_ARG
+    assert lib.tp_shard_forward_decode(sh._h, ATTN, xp, 0, kv._h, op, None) == N.TP_E_ARG
+    assert lib.tp_shard_forward_decode(sh._h, MLP, xp, 0, None, op, None) == N.TP_E_ARG
+    res = torch.full((4,), 3.0, dtype=torch.bfloat16, device="cuda")
+    red = torch.full((4,), 5.0, dtype=torch.bfloat16, device="cuda")
+    parts = (C.c_void_p * 2)(out.data_ptr(), out.data_ptr())
+    assert lib.tp_partial_reduce(parts, 2, C.c_void_p(res.data_ptr()), C.c_void_p(red.data_ptr()), 0,
+                                 N.TP_BF16, None) == N.TP_OK
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 7.0)) and bool(torch.all(red == 5.0))
+    assert kv.length == 8
+
+
 # ---------------------------------------------------------------- sequence-parallel variant
 
 @pytest.mark.parametrize("tp,B,S", [(2, 2, 64), (4, 1, 96)])
