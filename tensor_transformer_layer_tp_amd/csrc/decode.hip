@@ -119,12 +119,14 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
 #pragma unroll
             for (int h = 0; h < XC; ++h) gv[i][h] = *(const u16x8*)(gamma + cofs[i] * CW + 8 * h);
     }
+    // Weight rows are read once per call: non-temporal loads stream them
+    // without displacing the activations and partials from the caches.
     u32x4 wv[R][NI];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const char* wrow = W + (long long)(rbase + (r < P ? r : 32 + r - P)) * row_bytes;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) wv[r][i] = *(const u32x4*)(wrow + 16LL * cofs[i]);
+        for (int i = 0; i < NI; ++i) wv[r][i] = __builtin_nontemporal_load((const u32x4*)(wrow + 16LL * cofs[i]));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -643,7 +645,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16* __restrict__ x,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[t][c] = (f32x16){};
-    // two k-groups per iteration, all loads issued before the MFMAs; past the
+    // two k-groups per iteration, all loads issued before the MFMAs (plain
+    // loads: a lane reads 64 bytes of a row in four 16-byte loads, and
+    // non-temporal ones refetched the line for each, 20-30 % slower); past the
     // wave's last group the second group re-reads it (in bounds) with its
     // activations zeroed, so no branch splits the loads from their use
     for (int g = g0; g < g1; g += 2) {

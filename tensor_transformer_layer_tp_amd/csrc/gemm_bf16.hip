@@ -288,8 +288,11 @@ __device__ __forceinline__ void epilogue_staged(f32x16 (&acc)[FM][FN], const Epi
                 const int rl = c / CPR, ch = c % CPR;
                 const int row = wrow0 + i * 32 + rl;
                 const int col = wcol0 + ch * 4;
+                // non-temporal: the partial is read once, by the reduce that follows,
+                // which then finds no dirty lines of it to write back from L2
                 if (row < M && col < N)
-                    *(u32x4_t*)(o + (long long)row * epi.ldo + cb + col) = *(const u32x4_t*)(sf + rl * TNP + ch * 4);
+                    __builtin_nontemporal_store(*(const u32x4_t*)(sf + rl * TNP + ch * 4),
+                                                (u32x4_t*)(o + (long long)row * epi.ldo + cb + col));
             }
         }
     }
