@@ -134,8 +134,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(Parts parts, int t, const v
             }
             continue;
         } else {
-            s = *(const f32x4*)(parts.p[0] + i * 4);
-            for (int r = 1; r < t; ++r) s += *(const f32x4*)(parts.p[r] + i * 4);
+            // streamed once: non-temporal loads keep the partials from displacing
+            // the residual and the output in the caches
+            s = __builtin_nontemporal_load((const f32x4*)(parts.p[0] + i * 4));
+            for (int r = 1; r < t; ++r) s += __builtin_nontemporal_load((const f32x4*)(parts.p[r] + i * 4));
         }
         if (BF16_OUT) {
             if (residual) {
