@@ -141,7 +141,10 @@ int tp_shard_load_weights(tp_shard *s, const tp_weights *full, void *stream);
  * waits for the device). */
 int tp_shard_reserve(tp_shard *s, long long max_tokens);
 
-/* tp_kv_create -- KV cache for this rank's kv_heads/t heads:
+/* tp_kv_create -- KV cache for this rank's kv_heads/t heads (the KV cache
+ * is split across the devices like the heads: byteledger "Tensor
+ * Parallelism: Splitting One Layer Across GPUs", "Interaction with the rest
+ * of serving"):
  * K and V each [batch, kv_heads/t, max_seq, head_dim] in the shard's dtype,
  * zero-filled, length 0.  TP_F32 caches hold at most 16000 positions. */
 int tp_kv_create(const tp_shard *s, int batch, int max_seq, tp_kv **out);
@@ -174,14 +177,31 @@ int tp_kv_view(tp_kv *kv, void **k, void **v);
 
 /* tp_kv_set_len / tp_kv_get_len -- number of valid positions [0, len).
  * The length lives in device memory, where the kernels read and advance it
- * (so a decode call captured in a HIP graph stays correct on replay); the
- * library also keeps a host copy for its capacity checks.  Both calls wait
- * for the whole device first (hipDeviceSynchronize), then copy the value;
- * get_len also refreshes the host copy.  TP_E_ARG if len > max_seq. */
+ * (so a decode call captured in a HIP graph stays correct on replay), next
+ * to an overflow flag that a decode call raises when it finds the length at
+ * max_seq and so appends nothing; the library also keeps a host copy of the
+ * length for its capacity checks.  Both calls wait for the whole device
+ * first (hipDeviceSynchronize: they are set-up and inspection calls, not
+ * part of a step), then copy.  set_len also clears the overflow flag
+ * (TP_E_ARG if len > max_seq); get_len refreshes the host copy, stores the
+ * length in *len and returns TP_E_KV_FULL if the flag has been raised since
+ * the last set_len or prefill (only replayed or host-stale calls can raise
+ * it: an eager call on a full cache is refused up front). */
 int tp_kv_set_len(tp_kv *kv, int len);
 int tp_kv_get_len(const tp_kv *kv, int *len);
 
-/* tp_shard_forward_prefill -- one stage over a prompt batch.
+/* tp_shard_forward_prefill -- one stage over a prompt batch.  The stages
+ * are the pages' split of a layer (undercodenews post 110319 on tensor
+ * parallelism in transformers, "the Original"): ATTN = the column-parallel
+ * Q/K/V projection over the rank's own heads, attention per head with no
+ * communication, and the row-parallel output projection whose result is a
+ * partial sum; MLP = the column-parallel first FFN linear with its
+ * activation and the row-parallel second linear, again a partial sum.  The
+ * stage boundary is where the all-reduce of the partials must happen before
+ * the layer can go on (byteledger "Tensor Parallelism: Splitting One Layer
+ * Across GPUs", "Communication is the constraint").  A prompt runs the same
+ * layer over many tokens at once (clusterbid "When Tensor Parallelism Makes
+ * a Small Model Slower", the prefill paragraph).
  *   stage TP_STAGE_ATTN: x = layer input [batch, seq, hidden]; positions
  *     0..seq-1; K/V of the rank's heads are written to kv positions
  *     [0, seq) and the cache length becomes seq (kv may be NULL: K/V then
@@ -193,25 +213,38 @@ int tp_shard_forward_prefill(tp_shard *s, int stage, const void *x,
                              void *stream);
 
 /* tp_shard_forward_decode -- one stage for one new token per sequence.
+ * Decode is a sequence of one-token steps through the same layer
+ * (clusterbid "When Tensor Parallelism Makes a Small Model Slower", the
+ * decode paragraph); each step's ATTN stage reads and extends the rank's
+ * split of the KV cache (byteledger "Tensor Parallelism: Splitting One
+ * Layer Across GPUs", "Interaction with the rest of serving").
  *   stage TP_STAGE_ATTN: x [batch, hidden] sits at position L = the cache
  *     length; its k, v are appended at slot L, the query attends to
  *     positions 0..L, and the cache length becomes L+1.  TP_E_KV_FULL if
  *     the host copy of L equals max_seq; batch must equal the cache's batch.
  *   stage TP_STAGE_MLP: x = reduced h [batch, hidden]; kv must be NULL.
+ *     TP_E_STATE if no ATTN stage (prefill or decode) has run on this shard.
  *   partial [batch, hidden] fp32 receives this rank's summand.
  * Graph capture (TP_BF16 only): the kernels take L from the cache's device
  * length and advance it themselves, the attention grid and the workspace are
  * sized by max_seq, so a captured sequence of decode calls may be replayed;
  * each replay appends one token per captured ATTN call.  Make one eager call
  * of the same shape first (it sizes the workspace and the rotary table: no
- * allocation may happen during capture).  A replay past max_seq appends
- * nothing and attends over the first max_seq positions; the host copy of the
- * length is refreshed by tp_kv_get_len.  TP_F32 shards return TP_E_STATE on a
+ * allocation may happen during capture).  Capture leaves the host copy of
+ * the length alone.  A replay past max_seq appends nothing, attends over the
+ * first max_seq positions and raises the cache's overflow flag, which
+ * tp_kv_get_len reports (TP_E_KV_FULL); the host copy of the length is
+ * refreshed by tp_kv_get_len.  TP_F32 shards return TP_E_STATE on a
  * capturing stream. */
 int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
                             tp_kv *kv, float *partial, void *stream);
 
-/* tp_partial_reduce -- the all-reduce's arithmetic on one device:
+/* tp_partial_reduce -- the all-reduce's arithmetic on one device.  A
+ * row-parallel linear leaves each rank with a partial result that an
+ * all-reduce sums (undercodenews post 110319, "the Original"; netray
+ * glossary "What Is Tensor Parallelism?", "Tensor Parallelism Explained");
+ * here the t ranks' partials are resident on one device and summed by one
+ * kernel:
  *   out[i] = (sum_{r=0..t-1} partials[r][i]) + residual[i]
  * summed in fp32 in rank order, then stored as out_dtype (TP_BF16 rounds to
  * nearest even).  `partials` is a HOST array of t device pointers, each to
@@ -302,6 +335,31 @@ int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *l
  * Process-wide, not thread-safe.
  * TP_E_ARG if out of range. */
 int tp_tune_set_gemm_config(int cfg);
+
+/* Projection kinds of the planner hooks below (the epilogue each applies). */
+#define TP_PROJ_PARTIAL 0   /* out and down projections: fp32 partial   */
+#define TP_PROJ_QKV     1   /* Q/K/V with the rotary epilogue           */
+#define TP_PROJ_SWIGLU  2   /* gate/up with SwiGLU                      */
+#define TP_PROJ_GELU    3   /* up projection with GELU                  */
+
+/* tp_tune_gemm_plan -- host only, no device call: the launch plan that a
+ * bf16 projection C[M, N] = A[M, K] B[N, K]^T of kind `proj` takes under the
+ * current tuning hooks.  *parts receives 1 or 2 (launches over column
+ * ranges), cfg[i] the tile configuration of launch i (the numbering of
+ * tp_tune_set_gemm_config, -1 for no second launch) and ncols[i] its column
+ * count (0 for none).  TP_E_ARG for non-positive sizes, a NULL output or an
+ * unknown kind. */
+int tp_tune_gemm_plan(int M, int N, int K, int proj, int *parts, int cfg[2], int ncols[2]);
+
+/* tp_tune_set_gemm_split -- tuning and test hook: every later bf16
+ * projection wider than cols0 columns runs as two launches, columns
+ * [0, cols0) with tile configuration cfg0 and the others with cfg1 -- the
+ * form the planner itself takes when a shape's last round of tiles would be
+ * mostly idle.  cols0 = 0 restores the planner.  cols0 must be a multiple of
+ * 64 (a rotary or gate/up column group never straddles the split); a
+ * configuration that a projection cannot use leaves that projection to the
+ * planner.  Process-wide, not thread-safe.  TP_E_ARG otherwise. */
+int tp_tune_set_gemm_split(int cfg0, int cfg1, int cols0);
 
 /* tp_tune_set_attn_groups -- tuning hook for prefill attention: 1 runs each
  * 128-query block with one group of four waves over all its key blocks, 2

@@ -369,6 +369,24 @@ def set_gemm_config(cfg: int) -> None:
     N.check(N.lib().tp_tune_set_gemm_config(int(cfg)), "tp_tune_set_gemm_config")
 
 
+def set_gemm_split(cfg0: int, cfg1: int, cols0: int) -> None:
+    """Tuning hook: run every projection wider than cols0 columns as two
+    launches (cfg0 on the first cols0 columns, cfg1 on the rest); cols0 = 0
+    restores the planner."""
+    N.check(N.lib().tp_tune_set_gemm_split(int(cfg0), int(cfg1), int(cols0)), "tp_tune_set_gemm_split")
+
+
+def gemm_plan(M: int, N_: int, K: int, proj: str):
+    """The planner's launch plan for an M x N x K projection ('partial',
+    'qkv', 'swiglu' or 'gelu'): a list of (tile configuration, columns) per
+    launch."""
+    kind = {"partial": N.TP_PROJ_PARTIAL, "qkv": N.TP_PROJ_QKV, "swiglu": N.TP_PROJ_SWIGLU,
+            "gelu": N.TP_PROJ_GELU}[proj]
+    parts, cfg, cols = C.c_int(), (C.c_int * 2)(), (C.c_int * 2)()
+    N.check(N.lib().tp_tune_gemm_plan(int(M), int(N_), int(K), kind, C.byref(parts), cfg, cols), "tp_tune_gemm_plan")
+    return [(cfg[i], cols[i]) for i in range(parts.value)]
+
+
 def set_decode_chunk(ch: int) -> None:
     """Tuning hook: decode attention positions per chunk for query groups (0 = automatic, 16, 32, 64)."""
     N.check(N.lib().tp_tune_set_decode_chunk(int(ch)), "tp_tune_set_decode_chunk")

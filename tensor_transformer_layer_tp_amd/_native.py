@@ -16,6 +16,7 @@ TP_OK, TP_E_ARG, TP_E_DIVIDE, TP_E_RANK, TP_E_NOMEM, TP_E_HIP, TP_E_KV_FULL, TP_
 TP_F32, TP_BF16 = 0, 1
 TP_STAGE_ATTN, TP_STAGE_MLP, TP_STAGE_PRENORM = 0, 1, 0x10
 TP_ACT_SWIGLU, TP_ACT_GELU = 0, 1
+TP_PROJ_PARTIAL, TP_PROJ_QKV, TP_PROJ_SWIGLU, TP_PROJ_GELU = 0, 1, 2, 3
 # kernel kinds of the shard's event timer (TP_K_*)
 KERNEL_KINDS = ["rmsnorm", "gemm_qkv", "attn_prefill", "gemm_out", "gemm_up", "gemm_down", "gemv_qkv",
                 "attn_decode", "gemv_out", "gemv_up", "gemv_down"]
@@ -57,6 +58,9 @@ SIGNATURES = [
                                     C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     ("tp_tune_set_gemm_config", C.c_int, [C.c_int]),
     ("tp_tune_set_attn_groups", C.c_int, [C.c_int]),
+    ("tp_tune_gemm_plan", C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int),
+                                    C.POINTER(C.c_int)]),
+    ("tp_tune_set_gemm_split", C.c_int, [C.c_int, C.c_int, C.c_int]),
     ("tp_tune_set_decode_chunk", C.c_int, [C.c_int]),
     ("tp_shard_timing", C.c_int, [C.c_void_p, C.c_int]),
     ("tp_shard_timing_read", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),

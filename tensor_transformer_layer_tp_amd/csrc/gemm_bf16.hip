@@ -1023,6 +1023,10 @@ const Cfg kCfgs[] = {
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
+// forced two-launch split (tests): the first g_split_cols columns with
+// configuration g_split_cfg[0], the rest with g_split_cfg[1]; 0 = off
+int g_split_cols = 0;
+int g_split_cfg[2] = {0, 0};
 
 struct Args {
     const bf16* A;
@@ -1127,6 +1131,8 @@ struct Plan {
 
 Plan plan(int M, int N, int K, int mode) {
     Plan best{1, {1, 1}, {0, 0}, {N, 0}};
+    if (g_split_cols > 0 && g_split_cols < N && usable(g_split_cfg[0], mode) && usable(g_split_cfg[1], mode))
+        return Plan{2, {g_split_cfg[0], g_split_cfg[1]}, {0, g_split_cols}, {g_split_cols, N - g_split_cols}};
     if (g_forced_cfg >= 0 && g_forced_cfg < kNumCfg && usable(g_forced_cfg, mode)) {
         best.cfg[0] = g_forced_cfg;
         return best;
@@ -1167,13 +1173,28 @@ Plan plan(int M, int N, int K, int mode) {
 void set_gemm_config(int cfg) { g_forced_cfg = cfg; }
 int gemm_config_count() { return kNumCfg; }
 
+void set_gemm_split(int cfg0, int cfg1, int cols0) {
+    g_split_cfg[0] = cfg0;
+    g_split_cfg[1] = cfg1;
+    g_split_cols = cols0;
+}
+
+void gemm_plan_info(int M, int N, int K, int mode, int* parts, int cfg[2], int ncols[2]) {
+    const Plan p = plan(M, N, K, mode);
+    *parts = p.parts;
+    for (int i = 0; i < 2; ++i) {
+        cfg[i] = i < p.parts ? p.cfg[i] : -1;
+        ncols[i] = i < p.parts ? p.ncols[i] : 0;
+    }
+}
+
 void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M, int N, int K,
                const Epilogue& epi, hipStream_t st) {
     const Plan p = plan(M, N, K, epi.mode);
     for (int i = 0; i < p.parts; ++i) {
         Epilogue e = epi;
         e.col0 = epi.col0 + p.c0[i];
-        if (i > 0) e.len = LenUpdate{nullptr, 0, 0};   // one launch updates the cache length
+        if (i > 0) e.len = LenUpdate{nullptr, 0, 0, nullptr};   // one launch updates the cache length
         const Args a{A, lda, B + (long long)p.c0[i] * ldb, ldb, M, p.ncols[i], K, e, st};
         switch (epi.mode) {
             case EPI_F32: launch_cfg<EPI_F32>(p.cfg[i], a); break;

@@ -58,6 +58,8 @@ struct LenUpdate {
     int* ptr;           // nullptr: no update
     int value;          // >= 0: *ptr = value;  < 0: *ptr = min(*ptr + 1, cap)
     int cap;
+    int* overflow;      // set to 1 when an advance finds the length at cap: that
+                        // call's token was not appended (nullptr: not reported)
 };
 
 struct Epilogue {
@@ -73,9 +75,11 @@ __device__ __forceinline__ void apply_len_update(const LenUpdate& u) {
     if (u.ptr == nullptr) return;
     if (u.value >= 0) {
         *u.ptr = u.value;
+        if (u.overflow != nullptr) *u.overflow = 0;
     } else {
         const int v = *u.ptr;
-        *u.ptr = v < u.cap ? v + 1 : v;
+        if (v < u.cap) *u.ptr = v + 1;
+        else if (u.overflow != nullptr) *u.overflow = 1;
     }
 }
 
@@ -142,5 +146,10 @@ void all_gather(const void* const* pieces, int t, long long piece_bytes, void* o
 // tuning: -1 = heuristic, otherwise a fixed GEMM tile configuration index
 void set_gemm_config(int cfg);
 int gemm_config_count();
+// tests: force every GEMM wider than cols0 columns to run as two launches
+// (columns [0, cols0) with cfg0, the rest with cfg1); cols0 = 0 turns it off
+void set_gemm_split(int cfg0, int cfg1, int cols0);
+// the launch plan the planner picks for a shape (host only)
+void gemm_plan_info(int M, int N, int K, int mode, int* parts, int cfg[2], int ncols[2]);
 
 }  // namespace tp

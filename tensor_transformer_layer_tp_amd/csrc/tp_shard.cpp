@@ -47,12 +47,14 @@ struct tp_shard {
     std::vector<hipEvent_t> ev;
     std::vector<int> evkind;
     size_t evused;
+    bool attn_seen;   // an ATTN stage has run on this shard (decode MLP needs one first)
 };
 
 struct tp_kv {
     int batch, max_seq;
     int len;      // host copy of the cache length, advanced by every enqueued call
-    int* dlen;    // device copy, read and advanced by the kernels themselves
+    int* dlen;    // device copy [length, overflow flag]: the kernels read and advance
+                  // the length and raise the flag when a decode call finds it at max_seq
     int kvl, d;
     size_t esz;
     int dtype;
@@ -195,7 +197,7 @@ int launch_qkv(tp_shard* s, const void* n_in, long long M, int S, int pos0, void
 }
 
 int launch_proj(tp_shard* s, const void* A, long long M, int K, const void* W, int N, int mode, void* out,
-                long long ldo, hipStream_t st, LenUpdate len = LenUpdate{nullptr, 0, 0}) {
+                long long ldo, hipStream_t st, LenUpdate len = LenUpdate{nullptr, 0, 0, nullptr}) {
     Epilogue epi{};
     epi.mode = mode;
     epi.out = out;
@@ -398,10 +400,16 @@ int tp_shard_load_weights(tp_shard* s, const tp_weights* W, void* stream) {
         for (int i = 0; i < 4; ++i) {
             int rows, cols;
             fp8_shape(s, i, &rows, &cols);
-            if (!s->q8[i]) {
+            if (!s->q8[i] || !s->s8[i]) {
+                // both or neither: a half-made pair is freed, so a retry starts clean
                 if (hipMalloc((void**)&s->q8[i], (size_t)rows * cols) != hipSuccess ||
-                    hipMalloc((void**)&s->s8[i], (size_t)rows * sizeof(float)) != hipSuccess)
+                    hipMalloc((void**)&s->s8[i], (size_t)rows * sizeof(float)) != hipSuccess) {
+                    if (s->q8[i]) (void)hipFree(s->q8[i]);
+                    if (s->s8[i]) (void)hipFree(s->s8[i]);
+                    s->q8[i] = nullptr;
+                    s->s8[i] = nullptr;
                     return TP_E_NOMEM;
+                }
             }
             quant_rows_e4m3((const bf16*)src[i], rows, cols, s->q8[i], s->s8[i], st);
             LAUNCH_CHECK("fp8 quantisation");
@@ -444,14 +452,14 @@ int tp_kv_create(const tp_shard* s, int batch, int max_seq, tp_kv** out) {
     kv->dtype = s->o.dtype;
     size_t bytes = (size_t)batch * s->kvl * max_seq * s->d * s->esz;
     if (hipMalloc(&kv->k, bytes) != hipSuccess || hipMalloc(&kv->v, bytes) != hipSuccess ||
-        hipMalloc((void**)&kv->dlen, sizeof(int)) != hipSuccess) {
+        hipMalloc((void**)&kv->dlen, 2 * sizeof(int)) != hipSuccess) {
         if (kv->k) (void)hipFree(kv->k);
         if (kv->v) (void)hipFree(kv->v);
         delete kv;
         return TP_E_NOMEM;
     }
     if (hipMemset(kv->k, 0, bytes) != hipSuccess || hipMemset(kv->v, 0, bytes) != hipSuccess ||
-        hipMemset(kv->dlen, 0, sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        hipMemset(kv->dlen, 0, 2 * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(kv->k);
         (void)hipFree(kv->v);
         (void)hipFree(kv->dlen);
@@ -481,7 +489,7 @@ int tp_kv_create_paged(const tp_shard* s, int batch, int max_seq, int block_size
     const size_t pool = (size_t)num_blocks * s->kvl * block_size * s->d * s->esz;
     const size_t tbytes = (size_t)batch * kv->max_blocks * sizeof(int);
     if (hipMalloc(&kv->k, pool) != hipSuccess || hipMalloc(&kv->v, pool) != hipSuccess ||
-        hipMalloc((void**)&kv->dlen, sizeof(int)) != hipSuccess || hipMalloc((void**)&kv->table, tbytes) != hipSuccess) {
+        hipMalloc((void**)&kv->dlen, 2 * sizeof(int)) != hipSuccess || hipMalloc((void**)&kv->table, tbytes) != hipSuccess) {
         tp_kv_destroy(kv);
         return TP_E_NOMEM;
     }
@@ -489,7 +497,7 @@ int tp_kv_create_paged(const tp_shard* s, int batch, int max_seq, int block_size
     std::vector<int> t0((size_t)batch * kv->max_blocks);
     for (size_t i = 0; i < t0.size(); ++i) t0[i] = (int)(i < (size_t)num_blocks ? i : 0);
     if (hipMemset(kv->k, 0, pool) != hipSuccess || hipMemset(kv->v, 0, pool) != hipSuccess ||
-        hipMemset(kv->dlen, 0, sizeof(int)) != hipSuccess ||
+        hipMemset(kv->dlen, 0, 2 * sizeof(int)) != hipSuccess ||
         hipMemcpy(kv->table, t0.data(), tbytes, hipMemcpyHostToDevice) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         const int rc = hip_fail(hipGetLastError(), "paged kv init");
@@ -520,20 +528,21 @@ int tp_kv_view(tp_kv* kv, void** k, void** v) {
 
 int tp_kv_set_len(tp_kv* kv, int len) {
     if (!kv || len < 0 || len > kv->max_seq) return TP_E_ARG;
+    const int v[2] = {len, 0};   // the length, and a cleared overflow flag
     HIP_TRY(hipDeviceSynchronize());
-    HIP_TRY(hipMemcpy(kv->dlen, &len, sizeof(int), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(kv->dlen, v, sizeof(v), hipMemcpyHostToDevice));
     kv->len = len;
     return TP_OK;
 }
 
 int tp_kv_get_len(const tp_kv* kv, int* len) {
     if (!kv || !len) return TP_E_ARG;
-    int v = 0;
+    int v[2] = {0, 0};
     HIP_TRY(hipDeviceSynchronize());
-    HIP_TRY(hipMemcpy(&v, kv->dlen, sizeof(int), hipMemcpyDeviceToHost));
-    const_cast<tp_kv*>(kv)->len = v;   // replays of captured calls advance only the device copy
-    *len = v;
-    return TP_OK;
+    HIP_TRY(hipMemcpy(v, kv->dlen, sizeof(v), hipMemcpyDeviceToHost));
+    const_cast<tp_kv*>(kv)->len = v[0];   // replays of captured calls advance only the device copy
+    *len = v[0];
+    return v[1] ? TP_E_KV_FULL : TP_OK;
 }
 
 int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv, float* partial,
@@ -601,9 +610,10 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         {
             KTimer kt(s, TP_K_GEMM_OUT, st);
             TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
-                            kv ? LenUpdate{kv->dlen, seq, 0} : LenUpdate{nullptr, 0, 0}));
+                            kv ? LenUpdate{kv->dlen, seq, 0, kv->dlen + 1} : LenUpdate{nullptr, 0, 0, nullptr}));
         }
         if (kv) kv->len = seq;
+        s->attn_seen = true;
     } else {
         if (s->o.rmsnorm && !prenorm) {
             KTimer kt(s, TP_K_RMSNORM, st);
@@ -642,14 +652,16 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
         if (kv->len >= kv->max_seq) return TP_E_KV_FULL;
     } else if (kv) {
         return TP_E_ARG;
+    } else if (!s->attn_seen) {
+        return TP_E_STATE;   // a decode MLP stage follows the step's ATTN stage
     }
     // bf16 decode takes the cache length from the device copy, so a captured
-    // call stays valid on replay; the fp32 path uses the host copy
-    if (!bf) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        HIP_TRY(hipStreamIsCapturing(st, &cs));
-        if (cs != hipStreamCaptureStatusNone) return TP_E_STATE;
-    }
+    // call stays valid on replay; the fp32 path uses the host copy.  Capture
+    // executes nothing, so it leaves the host copy alone.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(st, &cs));
+    const bool capturing = cs != hipStreamCaptureStatusNone;
+    if (!bf && capturing) return TP_E_STATE;
     const int L = stage == TP_STAGE_ATTN ? kv->len : 0;
     Layout lay = layout(s, batch, stage == TP_STAGE_ATTN ? kv->max_seq : 0, batch);
     TRY(ensure_ws(s, lay.total));
@@ -695,16 +707,17 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
             epi.mode = EPI_F32;
             epi.out = partial;
             epi.ldo = s->hidden;
-            epi.len = LenUpdate{kv->dlen, -1, kv->max_seq};
+            epi.len = LenUpdate{kv->dlen, -1, kv->max_seq, kv->dlen + 1};
             KTimer kt(s, TP_K_GEMV_OUT, st);
             TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, ws + lay.n,
                             ws + lay.scr, st, 1));
         } else {
             KTimer kt(s, TP_K_GEMM_OUT, st);
             TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
-                            LenUpdate{kv->dlen, -1, kv->max_seq}));
+                            LenUpdate{kv->dlen, -1, kv->max_seq, kv->dlen + 1}));
         }
-        kv->len = L + 1;
+        if (!capturing) kv->len = L + 1;
+        s->attn_seen = true;
     } else {
         const int mode = s->o.act == TP_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU;
         if (use_gemv) {
@@ -856,6 +869,22 @@ int tp_shard_timing_read(tp_shard* s, int kernel, double* total_ms, long long* l
 int tp_tune_set_gemm_config(int cfg) {
     if (cfg < -1 || cfg >= gemm_config_count()) return TP_E_ARG;
     set_gemm_config(cfg);
+    return TP_OK;
+}
+
+int tp_tune_gemm_plan(int M, int N, int K, int proj, int* parts, int cfg[2], int ncols[2]) {
+    if (M <= 0 || N <= 0 || K <= 0 || !parts || !cfg || !ncols) return TP_E_ARG;
+    if (proj != TP_PROJ_PARTIAL && proj != TP_PROJ_QKV && proj != TP_PROJ_SWIGLU && proj != TP_PROJ_GELU)
+        return TP_E_ARG;
+    gemm_plan_info(M, N, K, proj, parts, cfg, ncols);
+    return TP_OK;
+}
+
+int tp_tune_set_gemm_split(int cfg0, int cfg1, int cols0) {
+    if (cols0 < 0 || cols0 % 64) return TP_E_ARG;
+    if (cols0 > 0 && (cfg0 < 0 || cfg0 >= gemm_config_count() || cfg1 < 0 || cfg1 >= gemm_config_count()))
+        return TP_E_ARG;
+    set_gemm_split(cfg0, cfg1, cols0);
     return TP_OK;
 }
 

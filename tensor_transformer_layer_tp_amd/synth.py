@@ -149,7 +149,8 @@ def draw_layer_device(hidden, heads, kv_heads, ffn, *, seed=0, device="cuda", dt
 
 
 def draw_normal_device(shape, seed, scale=1.0, device="cuda", dtype=None):
-    """Timing-only N(0, scale^2) device tensor in the storage type."""
+    """N(0, scale^2) device tensor in the storage type (torch's generator):
+    for timing, or as filler in rows that are never compared."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed)

@@ -200,3 +200,41 @@ def test_paged_cache_argument_rules():
     assert lib.tp_shard_create(512, 8, 8, 1024, 2, 0, C.byref(f32), C.byref(h)) == N.TP_OK
     assert lib.tp_kv_create_paged(h, 1, 64, 16, 16, C.byref(kv)) == N.TP_E_ARG
     lib.tp_shard_destroy(h)
+
+
+def test_gemm_plan_column_splits():
+    """The planner's launch plans (host only): the shapes for which it runs
+    a projection as two launches over column ranges, the forced split hook,
+    and that every plan covers all N columns with 64-aligned split points."""
+    from tensor_transformer_layer_tp_amd import gemm_plan, set_gemm_split
+    lib = N.lib()
+    # unsharded 7B gate/up at 2048 tokens (crossover sweep B1 S2048, B4 S512, B16 S128)
+    assert [c for _, c in gemm_plan(2048, 22016, 4096, "swiglu")] == [16384, 5632]
+    # sharded 7B gate/up at 8192 tokens (B1 S8192, B4 S2048, B16 S512, B64 S128)
+    assert [c for _, c in gemm_plan(8192, 11008, 4096, "swiglu")] == [10240, 768]
+    # 70B t=8 Q/K/V projection (B4 S4096)
+    assert len(gemm_plan(16384, 1280, 8192, "qkv")) == 2
+    # the 7B t=2 prefill at 2048 tokens: single launches
+    assert len(gemm_plan(2048, 11008, 4096, "swiglu")) == 1
+    assert len(gemm_plan(2048, 6144, 4096, "qkv")) == 1
+    for M in (1, 128, 300, 2048, 8192, 16384, 524288):
+        for N_, K, kind in ((6144, 4096, "qkv"), (12288, 4096, "qkv"), (1280, 8192, "qkv"), (11008, 4096, "swiglu"),
+                            (22016, 4096, "swiglu"), (7168, 8192, "swiglu"), (4096, 5504, "partial"),
+                            (8192, 1024, "partial"), (1408, 1024, "gelu")):
+            plan = gemm_plan(M, N_, K, kind)
+            assert sum(c for _, c in plan) == N_
+            assert all(c % 64 == 0 for _, c in plan[:-1])
+            assert all(0 <= cfg < 17 for cfg, _ in plan)
+    try:
+        set_gemm_split(14, 16, 640)
+        assert gemm_plan(2048, 11008, 4096, "swiglu") == [(14, 640), (16, 10368)]
+        assert len(gemm_plan(300, 512, 1024, "qkv")) == 1   # not wider than the split: the planner's plan
+    finally:
+        set_gemm_split(0, 0, 0)
+    assert len(gemm_plan(2048, 11008, 4096, "swiglu")) == 1
+    assert lib.tp_tune_set_gemm_split(14, 16, 100) == N.TP_E_ARG      # not a multiple of 64
+    assert lib.tp_tune_set_gemm_split(99, 16, 640) == N.TP_E_ARG      # no such configuration
+    assert lib.tp_tune_set_gemm_split(14, 16, -64) == N.TP_E_ARG
+    parts, cfg, cols = C.c_int(), (C.c_int * 2)(), (C.c_int * 2)()
+    assert lib.tp_tune_gemm_plan(0, 64, 64, N.TP_PROJ_QKV, C.byref(parts), cfg, cols) == N.TP_E_ARG
+    assert lib.tp_tune_gemm_plan(64, 64, 64, 7, C.byref(parts), cfg, cols) == N.TP_E_ARG
