@@ -62,6 +62,7 @@ extern "C" {
 #define TP_E_HIP      -5   /* a HIP runtime call or kernel launch failed */
 #define TP_E_KV_FULL  -6   /* the KV cache has no room for the tokens asked for */
 #define TP_E_STATE    -7   /* call out of order (e.g. forward before weights are loaded) */
+#define TP_E_SCRATCH  -8   /* the allocation-free entry point needs more than its static scratch */
 
 /* element types */
 #define TP_F32   0
@@ -238,6 +239,26 @@ int tp_shard_forward_prefill(tp_shard *s, int stage, const void *x,
  * capturing stream. */
 int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
                             tp_kv *kv, float *partial, void *stream);
+
+/* tp_shard_forward_decode_noalloc -- tp_shard_forward_decode for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels,
+ * results and errors, but no call to hipMalloc, hipFree or any allocating
+ * routine: every intermediate (normalised input, q, attention output and
+ * split-KV records, FFN activation, split-K partials) lives in one static
+ * device array of TP_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends; its address on a device is
+ * looked up at tp_shard_load_weights.  TP_BF16 shards only (TP_E_STATE for
+ * TP_F32).  Returns TP_E_SCRATCH, before any launch, when the call's
+ * workspace -- set by batch, the shard's widths and, for ATTN, the cache's
+ * max_seq -- exceeds the array (e.g. 7B-shaped t=4: batch 1 up to ~1.8M
+ * cached positions; 70B-shaped t=8, batch 1, up to ~250k positions).
+ * Every call on a device shares that device's array and finds the previous
+ * call's contents in it; no part of it needs to start at zero.  Calls that
+ * overlap on one device (two streams, or two threads) race on it. */
+#define TP_NOALLOC_SCRATCH_BYTES (32 << 20)
+int tp_shard_forward_decode_noalloc(tp_shard *s, int stage, const void *x, int batch,
+                                    tp_kv *kv, float *partial, void *stream);
 
 /* tp_partial_reduce -- the all-reduce's arithmetic on one device.  A
  * row-parallel linear leaves each rank with a partial result that an

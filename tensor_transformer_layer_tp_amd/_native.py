@@ -13,6 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtpshard.so")
 
 TP_OK, TP_E_ARG, TP_E_DIVIDE, TP_E_RANK, TP_E_NOMEM, TP_E_HIP, TP_E_KV_FULL, TP_E_STATE = 0, -1, -2, -3, -4, -5, -6, -7
+TP_E_SCRATCH = -8
+TP_NOALLOC_SCRATCH_BYTES = 32 << 20
 TP_F32, TP_BF16 = 0, 1
 TP_STAGE_ATTN, TP_STAGE_MLP, TP_STAGE_PRENORM = 0, 1, 0x10
 TP_ACT_SWIGLU, TP_ACT_GELU = 0, 1
@@ -45,6 +47,8 @@ SIGNATURES = [
                                            C.c_void_p, C.c_void_p]),
     ("tp_shard_forward_decode", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                                           C.c_void_p]),
+    ("tp_shard_forward_decode_noalloc", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
+                                                  C.c_void_p, C.c_void_p]),
     ("tp_partial_reduce", C.c_int, [C.POINTER(C.c_void_p), C.c_int, C.c_void_p, C.c_void_p, C.c_longlong, C.c_int,
                                     C.c_void_p]),
     ("tp_shard_debug_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),

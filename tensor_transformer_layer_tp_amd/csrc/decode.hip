@@ -43,9 +43,13 @@ __device__ __forceinline__ void pair_store(const Epilogue& epi, int b, int r1, f
         const int pos = q.pos_dev ? *q.pos_dev : q.pos0;
         if (region > 0 && pos >= q.ld_seq) return;   // cache full: nothing to append
         float o1 = y1, o2 = y2;
-        if (region < 2 && q.rope_cos != nullptr) {
-            const float c = q.rope_cos[(long long)pos * half + i1];
-            const float sn = q.rope_sin[(long long)pos * half + i1];
+        if (region < 2 && q.rope_rev != nullptr) {
+            // pos * theta_i turns: the fraction, formed in double (exact for any
+            // position), goes to the hardware sine and cosine, which take turns;
+            // no table, so the decode path needs nothing sized by the cache
+            const double a = (double)pos * q.rope_rev[i1];
+            const float f = (float)(a - floor(a));
+            const float c = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
             o1 = y1 * c - y2 * sn;
             o2 = y2 * c + y1 * sn;
         }

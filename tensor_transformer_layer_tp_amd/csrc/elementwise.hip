@@ -201,7 +201,17 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, double* rev, int n
     }
 }
 
+// theta^(-2i/d) / (2 pi) for i < d/2: the rotation per position in turns
+__global__ void rope_turns_kernel(double* rev, int d, double theta) {
+    const int i = threadIdx.x;
+    if (i < d / 2) rev[i] = pow(theta, -2.0 * i / (double)d) * 0.15915494309189535;
+}
+
 }  // namespace
+
+void rope_turns(double* rev, int d, float theta, hipStream_t st) {
+    hipLaunchKernelGGL(rope_turns_kernel, dim3(1), dim3(64), 0, st, rev, d, (double)theta);
+}
 
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st) {
     if (rows <= 0 || n <= 0) return;

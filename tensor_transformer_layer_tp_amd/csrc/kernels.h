@@ -24,10 +24,10 @@ struct QKVDest {
     void* k;            // [B, kvl, ld_seq, d], written at slots pos0 + s
     void* v;
     int ld_seq;         // cache capacity (positions)
-    const float* rope_cos;  // [max_pos, d/2] or nullptr (no rotary embedding)
+    const float* rope_cos;  // [max_pos, d/2] or nullptr: the fp32 path's rotation tables
     const float* rope_sin;
-    const double* rope_rev; // [d/2] turns per position (theta_i / 2 pi); the projection GEMM
-                            // forms the rotation from it instead of reading the tables
+    const double* rope_rev; // [d/2] turns per position (theta_i / 2 pi), or nullptr (no rotary
+                            // embedding): the bf16 kernels form the rotation from it
     // paged cache: k/v are pools [blocks, kvl, bsz, d]; position p of sequence
     // b lives in block table[b * max_blocks + p / bsz] at row p % bsz
     const int* table;   // nullptr: contiguous [B, kvl, ld_seq, d]
@@ -140,6 +140,8 @@ void partial_reduce(const float* const* parts, int t, const void* residual, void
 // cos/sin of p * theta_i for p < npos, i < d/2 ([npos, d/2] fp32), and rev[i] =
 // theta_i / (2 pi) in double (the rotation per position in turns)
 void rope_table(float* cos_t, float* sin_t, double* rev, int npos, int d, float theta, hipStream_t st);
+// rev[i] = theta_i / (2 pi) alone (d <= 128): what the bf16 kernels rotate with
+void rope_turns(double* rev, int d, float theta, hipStream_t st);
 // out = rank-order concatenation of t pieces of piece_bytes each (multiple of 16, 16-byte aligned)
 void all_gather(const void* const* pieces, int t, long long piece_bytes, void* out, hipStream_t st);
 

@@ -16,12 +16,19 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "kernels.h"
 
 using namespace tp;
+
+// Workspace of the allocation-free decode entry point: a static device array
+// that the code object brings along on every device the library runs on.
+// In host code its name is a host-side stand-in, never a device address:
+// host code uses only the per-device address looked up once at set-up.
+static __device__ __align__(256) char scratch[TP_NOALLOC_SCRATCH_BYTES];
 
 struct tp_shard {
     int hidden, heads, kv_heads, ffn, t, rank;
@@ -39,7 +46,8 @@ struct tp_shard {
     float *rcos, *rsin;
     double* rrev;     // [d/2] rotary turns per position
     int rope_npos;
-    // offsets of the last call's workspace tensors (debug view)
+    // base and offsets of the last call's workspace tensors (debug view)
+    char* dbg_base;
     size_t off_n, off_o, off_act;
     // kernel timer: event pairs in launch order and the kind of each pair
     bool timing;
@@ -87,6 +95,29 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Device address of `scratch` per device, looked up once with the device
+// current (hipGetSymbolAddress), kept for every later call on that device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return TP_E_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[device]) return TP_OK;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_dev[device] = (char*)p;
+    return TP_OK;
+}
+
+char* scratch_of(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_dev[device];
+}
+
 int ensure_ws(tp_shard* s, size_t bytes) {
     if (bytes <= s->ws_bytes) return TP_OK;
     if (s->ws) {
@@ -106,8 +137,9 @@ int ensure_ws(tp_shard* s, size_t bytes) {
     return TP_OK;
 }
 
+// cos/sin tables of the fp32 path (the bf16 kernels rotate with s->rrev alone)
 int ensure_rope(tp_shard* s, int npos, hipStream_t st) {
-    if (!s->o.rope || npos <= s->rope_npos) return TP_OK;
+    if (!s->o.rope || s->o.dtype != TP_F32 || npos <= s->rope_npos) return TP_OK;
     int want = std::max(npos, std::max(2 * s->rope_npos, 4096));
     if (s->rcos) {
         hipError_t e1 = hipFree(s->rcos), e2 = hipFree(s->rsin);
@@ -292,6 +324,8 @@ const char* tp_status_string(int status) {
         case TP_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
         case TP_E_KV_FULL: return "KV cache full";
         case TP_E_STATE: return "call out of order (weights not loaded?)";
+        case TP_E_SCRATCH: return "the call needs more workspace than the allocation-free entry point's static "
+                                  "scratch array holds (TP_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -348,6 +382,7 @@ int tp_shard_load_weights(tp_shard* s, const tp_weights* W, void* stream) {
     const int h = s->hidden, d = s->d, r = s->rank;
     if (!s->w_qkv) {
         HIP_TRY(hipGetDevice(&s->device));
+        TRY(scratch_setup(s->device));
         void** bufs[] = {&s->w_qkv, &s->w_o, &s->w_up, &s->w_down, &s->g1, &s->g2};
         size_t sizes[] = {(size_t)s->nqkv * h * e, (size_t)h * s->hl * d * e, (size_t)s->nup * h * e,
                           (size_t)h * s->fl * e, (size_t)h * e, (size_t)h * e};
@@ -394,6 +429,15 @@ int tp_shard_load_weights(tp_shard* s, const tp_weights* W, void* stream) {
     if (s->o.rmsnorm) {
         HIP_TRY(hipMemcpyAsync(s->g1, W->g1, (size_t)h * e, hipMemcpyDeviceToDevice, st));
         HIP_TRY(hipMemcpyAsync(s->g2, W->g2, (size_t)h * e, hipMemcpyDeviceToDevice, st));
+    }
+    if (s->o.rope) {
+        // the rotation per position of every dim pair, in turns
+        if (!s->rrev && hipMalloc((void**)&s->rrev, (size_t)(d / 2) * sizeof(double)) != hipSuccess) {
+            s->rrev = nullptr;
+            return TP_E_NOMEM;
+        }
+        rope_turns(s->rrev, d, s->o.rope_theta, st);
+        LAUNCH_CHECK("rope_turns");
     }
     if (s->o.decode_fp8) {
         const void* src[4] = {s->w_qkv, s->w_o, s->w_up, s->w_down};
@@ -565,6 +609,7 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
     Layout L = layout(s, T, 0, 0);
     TRY(ensure_ws(s, L.total));
     char* ws = s->ws;
+    s->dbg_base = ws;
     s->off_n = L.n;
     s->off_o = L.o;
     s->off_act = L.act;
@@ -633,8 +678,15 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
     return TP_OK;
 }
 
-int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode stage over the workspace at `base`: the library's own workspace
+// (grown on demand) or, for the allocation-free entry point, the device's
+// static scratch array.
+int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial, void* stream,
+                 bool noalloc) {
     const bool prenorm = (stage & TP_STAGE_PRENORM) != 0;
     stage &= ~TP_STAGE_PRENORM;
     if (!s || !x || !partial || batch <= 0) return TP_E_ARG;
@@ -662,15 +714,24 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
     HIP_TRY(hipStreamIsCapturing(st, &cs));
     const bool capturing = cs != hipStreamCaptureStatusNone;
     if (!bf && capturing) return TP_E_STATE;
+    if (noalloc && !bf) return TP_E_STATE;   // the fp32 path's rotation tables grow with the cache
     const int L = stage == TP_STAGE_ATTN ? kv->len : 0;
     Layout lay = layout(s, batch, stage == TP_STAGE_ATTN ? kv->max_seq : 0, batch);
-    TRY(ensure_ws(s, lay.total));
-    char* ws = s->ws;
+    char* ws;
+    if (noalloc) {
+        if (lay.total > (size_t)TP_NOALLOC_SCRATCH_BYTES) return TP_E_SCRATCH;
+        ws = scratch_of(s->device);
+        if (ws == nullptr) return TP_E_STATE;
+    } else {
+        TRY(ensure_ws(s, lay.total));
+        ws = s->ws;
+    }
+    s->dbg_base = ws;
     s->off_n = lay.n;
     s->off_o = lay.o;
     s->off_act = lay.act;
     if (stage == TP_STAGE_ATTN) {
-        TRY(ensure_rope(s, kv->max_seq + 1, st));   // a query at position max_seq (full cache) stays in range
+        if (!noalloc) TRY(ensure_rope(s, kv->max_seq + 1, st));   // fp32: a query at position max_seq stays in range
         void* qbuf = ws + lay.q;
         if (use_gemv) {
             Epilogue epi{};
@@ -755,6 +816,20 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
     return TP_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial,
+                            void* stream) {
+    return decode_stage(s, stage, x, batch, kv, partial, stream, false);
+}
+
+int tp_shard_forward_decode_noalloc(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial,
+                                    void* stream) {
+    return decode_stage(s, stage, x, batch, kv, partial, stream, true);
+}
+
 int tp_partial_reduce(const float* const* partials, int t, const void* residual, void* out, long long n,
                       int out_dtype, void* stream) {
     if (!partials || t < 1 || t > 64 || n < 0) return TP_E_ARG;
@@ -818,11 +893,11 @@ int tp_shard_norm(tp_shard* s, int which, const void* x, long long rows, void* o
 }
 
 int tp_shard_debug_view(tp_shard* s, int which, void** ptr) {
-    if (!s || !ptr || !s->ws) return TP_E_ARG;
+    if (!s || !ptr || !s->dbg_base) return TP_E_ARG;
     switch (which) {
-        case 0: *ptr = s->ws + s->off_o; return TP_OK;
-        case 1: *ptr = s->ws + s->off_act; return TP_OK;
-        case 2: *ptr = s->ws + s->off_n; return TP_OK;
+        case 0: *ptr = s->dbg_base + s->off_o; return TP_OK;
+        case 1: *ptr = s->dbg_base + s->off_act; return TP_OK;
+        case 2: *ptr = s->dbg_base + s->off_n; return TP_OK;
         default: return TP_E_ARG;
     }
 }

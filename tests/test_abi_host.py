@@ -40,7 +40,7 @@ def test_exports_every_declared_function():
 
 def test_status_strings():
     lib = N.lib()
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         assert lib.tp_status_string(code)
 
 
