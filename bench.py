@@ -1,27 +1,33 @@
 """Benchmark of one rank's tensor-parallel layer shard on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-70b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-7b] [--no-70b]
     python bench.py --sweep          # the 7B t=2 vs t=1 batch x prompt-length sweep
 
-Prints ONE JSON line.  The timed step is the whole prefill hot path of rank 0
-of a 7B-shaped layer split two ways (hidden 4096, 16 of 32 heads x 128,
-SwiGLU 5504 of 11008, RMSNorm, RoPE, bf16, batch 1 x 2048 tokens, causal):
-ATTN stage (RMSNorm, Q/K/V projection with RoPE and KV-cache write, causal
-attention, row-parallel output projection) -> reduce of the two ranks'
-partials + residual -> MLP stage (RMSNorm, gate/up projection with SwiGLU,
-row-parallel down projection) -> reduce.  Rank 1's partials are computed once
-before timing (they stand for the other GPU's contribution).
+Prints ONE JSON line.  The headline step is the whole prefill hot path of
+rank 0 of a 70B-shaped GQA layer split eight ways (hidden 8192, 8 of 64
+query heads + 1 of 8 KV heads x 128, SwiGLU 3584 of 28672, RMSNorm, RoPE,
+bf16, batch 4 x 4096 tokens, causal) -- the largest single-GPU prefill
+configuration: ATTN stage (RMSNorm, Q/K/V projection with RoPE and KV-cache
+write, causal attention, row-parallel output projection) -> reduce of the
+eight ranks' partials + residual -> MLP stage (RMSNorm, gate/up projection
+with SwiGLU, row-parallel down projection) -> reduce.  The other ranks'
+partials are seeded stand-ins, resident in HBM before timing (they stand
+for the other GPUs' contributions).
 
-`value` is the shard step's algorithmic FLOPs (GEMMs + causal attention) per
+`value` is the step's algorithmic FLOPs (GEMMs + causal attention) per
 second.  `roofline` covers the dominant kernel (the gate/up projection GEMM),
-timed with HIP events on its launch stream inside the timed steps.  `decode`
-reports batch-1 decode of rank 0 of the 7B layer split four ways against a
-1024-position cache, in microseconds per token per layer, over a stack of
-distinct layer copies whose weights (>= 1 GB) exceed the 256 MB Infinity
-Cache.  `prefill_70b` / `decode_70b` report the same for rank 0 of a
-70B-shaped GQA layer split eight ways (prefill batch 4 x 4096 tokens; decode
-batch 1 at cache length 4096).  `cpu_baseline` times the CPU oracle (NumPy
-float64) on the same 7B prefill step.
+timed with HIP events on its launch stream inside the timed steps.
+`prefill_7b` reports the same for rank 0 of a 7B-shaped layer split two ways
+(hidden 4096, 16 of 32 heads, SwiGLU 5504 of 11008, batch 1 x 2048 tokens;
+the other rank's partials computed by its own shard) and its
+sequence-parallel variant.  `decode` / `decode_70b` report batch-1 decode of
+rank 0 of the 7B layer split four ways (cache 1024) and of the 70B layer
+split eight ways (cache 4096), in microseconds per token per layer, over
+stacks of distinct layer copies whose weights (>= 1 GB) exceed the 256 MB
+Infinity Cache.  `clock` is the GPU clock sampled while the headline steps
+run, `hbm_copy_GBps` a plain device copy's rate (the measured streaming
+ceiling).  `cpu_baseline` times the CPU oracle (NumPy float64) on a bounded
+sample of the headline workload: one of its four sequences, whole.
 """
 
 from __future__ import annotations
@@ -48,22 +54,27 @@ MIN_DECODE_FOOTPRINT = 1.0e9   # decode weight copies span at least this many by
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-layers", type=int, default=0,
                     help="layer copies in the decode stack (0: enough for >= 1 GB of weights)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped prefill and decode")
+    ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped prefill and decode (the headline: "
+                                                           "the 7B prefill takes its place)")
+    ap.add_argument("--no-7b", action="store_true", help="skip the 7B-shaped prefill and decode")
     ap.add_argument("--sweep", action="store_true", help="run the 7B t=2 vs t=1 crossover sweep instead")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB three times: the known-size copy that scales rocprofv3 byte counters")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                     help="no GPU: turn rocprofv3 outputs of this script into profiles/traffic.json and "
                          "profiles/*.md (see profiles/README.md for the commands)")
-    ap.add_argument("--summarize-mfma", nargs=1, metavar="PMC_DIR",
+    ap.add_argument("--summarize-warmup", nargs=3, metavar=("PMC_DIR", "KEY", "OUT_MD"),
+                    help="no GPU: per-dispatch duration and clock of the first dispatches of roofline kernel KEY "
+                         "from a rocprofv3 --pmc GRBM_GUI_ACTIVE run, into profiles/OUT_MD")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_MD"),
                     help="no GPU: turn a rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE run of this script "
-                         "into profiles/mfma_counters.md")
+                         "into profiles/OUT_MD")
     return ap.parse_args()
 
 
@@ -164,6 +175,104 @@ def rounded(d):
     return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
 
 
+class ClockSampler:
+    """The GPU clock while a step runs, from amdsmi's GPU metrics table (per-XCD
+    current GFX clocks and socket power), when amdsmi is present.  The
+    firmware refreshes that table about once a second, so a sample counts
+    only once the table's timestamp has moved past its value at the start;
+    the caller keeps the GPU busy for a few seconds."""
+
+    def __init__(self):
+        self.ok, self.samples = False, []
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi, self.h = amdsmi, amdsmi.amdsmi_get_processor_handles()[0]
+            self.t0 = self.read()["stamp"]
+            self.ok = True
+        except Exception:
+            pass
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        clks = [c for c in m.get("current_gfxclks") or [] if isinstance(c, (int, float))]
+        return {"stamp": m.get("system_clock_counter"), "mhz": sum(clks) / len(clks) if clks else None,
+                "power": m.get("current_socket_power")}
+
+    def __enter__(self):
+        if self.ok:
+            import threading
+            self.stop = threading.Event()
+
+            def run():
+                last = self.t0
+                while not self.stop.is_set():
+                    try:
+                        r = self.read()
+                        if r["stamp"] != last and r["mhz"]:
+                            last = r["stamp"]
+                            self.samples.append(r)
+                    except Exception:
+                        pass
+                    time.sleep(0.01)
+
+            self.thread = threading.Thread(target=run, daemon=True)
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.ok:
+            self.stop.set()
+            self.thread.join()
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return None
+        mhz = np.array([r["mhz"] for r in self.samples])
+        pw = [r["power"] for r in self.samples if isinstance(r["power"], (int, float))]
+        return {"median_MHz": round(float(np.median(mhz)), 1), "min_MHz": round(float(mhz.min()), 1),
+                "max_MHz": round(float(mhz.max()), 1), "socket_power_W": float(np.median(pw)) if pw else None,
+                "samples": int(mhz.size),
+                "source": "amdsmi GPU metrics (mean of the per-XCD current GFX clocks), fresh refreshes during "
+                          "a ~2.5 s run of back-to-back steps"}
+
+
+def clock_pass(torch, step, seconds=2.5):
+    """Runs `step` back to back for about `seconds` while sampling the clock."""
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+    return clock.summary()
+
+
+NOMINAL_CLOCK_MHZ = 2400.0     # the clock the 2.5 PFLOP/s bf16 peak assumes
+
+
+def copy_ceiling(torch, mib=4096, reps=5):
+    """HBM streaming ceiling: the best rate of a plain device copy of `mib` MiB
+    (bytes read + bytes written over the copy's event-timed duration)."""
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 1e30
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * n / (best * 1e-3) / 1e9, 1)
+
+
 # ---------------------------------------------------------------- prefill
 
 def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, kv_cap=None):
@@ -226,6 +335,8 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
     sh.timing(True, kinds=[dom])
     ms, dist = timed(torch, step, args.steps, 0, stream)
     dom_times = sh.timing_read()[dom]
+    sh.timing(False)
+    clk = clock_pass(torch, step)
     sh.timing(True)
     ms_marked, _ = timed(torch, step, args.steps, 0, stream)
     ktimes = sh.timing_read()
@@ -244,7 +355,12 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
     dom_us = 1e3 * dom_times[0] / dom_times[1]
     achieved = gemm[dom] / (dom_us * 1e-6) / 1e12
     d, hl, kvl, fl = dims(hidden, heads, kv_heads, ffn, t)
+    roof_clock = {}
+    if clk:
+        peak_clk = PEAK_BF16_TFLOPS * clk["median_MHz"] / NOMINAL_CLOCK_MHZ
+        roof_clock = {"peak_at_measured_clock": round(peak_clk, 1), "frac_at_measured_clock": round(achieved / peak_clk, 4)}
     return {
+        "clock": clk,
         "workload": name,
         "ms_per_step": round(ms, 4),
         "step_ms": dist,
@@ -259,7 +375,8 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(roof_key, "gemm_bf16.hip"),
                      "kernel": f"gemm (gate/up projection + SwiGLU epilogue), M={B * S} N={2 * fl} K={hidden}",
-                     "avg_us": round(dom_us, 3), "launches": dom_times[1], "flops_per_launch": gemm[dom]},
+                     "avg_us": round(dom_us, 3), "launches": dom_times[1], "flops_per_launch": gemm[dom],
+                     **roof_clock},
     }
 
 
@@ -441,8 +558,11 @@ def run_7b(args, torch):
     raw = synth.draw_workload(w)
     dev = {k: synth.to_storage(v, "bf16").cuda() for k, v in raw.items()}
     wdev = {k: v for k, v in dev.items() if k != "x"}
-    pre = bench_prefill(args, torch, "7b-t2-prefill", w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, dev["x"],
-                        True, "gemm_up_7b_t2")
+    pre = bench_prefill(args, torch,
+                        "7b-t2-prefill: rank 0 of a 7B-shaped layer split t=2 (hidden 4096, 16 of 32 heads x 128, "
+                        "SwiGLU 5504 of 11008), bf16, batch 1 x seq 2048, causal; the other rank's partials computed "
+                        "by its own shard", w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, dev["x"], True,
+                        "gemm_up_7b_t2")
     pre["sequence_parallel"] = bench_sp(args, torch, w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, dev["x"])
     del dev, wdev
     return pre, (w, raw)
@@ -524,7 +644,23 @@ def allreduce_model_us(nbytes):
     return ALLREDUCE_LATENCY_US + nbytes / (XGMI_LINK_GBPS * 1e9) * 1e6
 
 
+def kernel_avgs(shards):
+    """{kernel kind: mean µs per launch} over the shards' event timers (then
+    switched off)."""
+    agg = {}
+    for sh in shards:
+        for k, (tot, n) in sh.timing_read().items():
+            a = agg.setdefault(k, [0.0, 0])
+            a[0] += tot
+            a[1] += n
+        sh.timing(False)
+    return {k: round(1e3 * v[0] / v[1], 2) for k, v in agg.items()}
+
+
 def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
+    """Prefill of B x S tokens and decode of one token per sequence at cache
+    length S: mean, median and p10/p90 over the timed steps, then one more
+    pass with every kernel bracketed by events for the per-kernel means."""
     from tensor_transformer_layer_tp_amd import synth
     stream = torch.cuda.current_stream()
     x = synth.draw_normal_device((B, S, hidden), 1000 + B * 10000 + S)
@@ -538,8 +674,12 @@ def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
     est = time.perf_counter() - t0
     n = max(3, min(args.steps, int(0.5 / max(est, 1e-6))))
     ms, dist = timed(torch, step, n, 1, stream)
+    sh.timing(True)
+    timed(torch, step, n, 0, stream)
+    pre_k = kernel_avgs([sh])
     gemm, attn = prefill_flops(hidden, heads, kv_heads, ffn, t, B, S)
-    pre = {"ms": ms, "median_ms": dist["median"], "tflops": (sum(gemm.values()) + attn) / (ms * 1e-3) / 1e12}
+    pre = {"ms": ms, "dist": dist, "kernels_us": pre_k,
+           "tflops": (sum(gemm.values()) + attn) / (ms * 1e-3) / 1e12}
     del step
     # decode one token per sequence from cache length S over the cache this
     # prefill left, through enough layer copies to span >= 1 GB of weights
@@ -552,11 +692,16 @@ def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
     del x
     x0 = synth.draw_normal_device((B, hidden), 7)
     dstep = decode_step_fn(torch, layers, hidden, t, B, x0)
-    nd = max(3, min(args.steps, 10))
-    dms, _ = timed(torch, dstep, nd, 2, stream)
+    nd = max(3, min(args.steps, 6))
+    dms, ddist = timed(torch, dstep, nd, 2, stream)
+    for s_, _ in layers:
+        s_.timing(True)
+    timed(torch, dstep, 1, 0, stream)
+    dec_k = kernel_avgs([s_ for s_, _ in layers])
     us = 1e3 * dms / nl
     nbytes, _ = decode_bytes(hidden, heads, kv_heads, ffn, t, B, S + 2 + nd // 2)
-    dec = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
+    dec = {"us": us, "dist_us": {k: round(1e3 * v / nl, 2) for k, v in ddist.items()}, "kernels_us": dec_k,
+           "GBps": nbytes / (us * 1e-6) / 1e9}
     for s_, k_ in layers:
         k_.close()
         s_.close()
@@ -588,9 +733,13 @@ def run_sweep(args, torch):
             table.append({
                 "B": B, "S": S,
                 "prefill_ms_t2": round(p2["ms"], 4), "prefill_ms_t1": round(p1["ms"], 4),
+                "prefill_step_ms_t2": p2["dist"], "prefill_step_ms_t1": p1["dist"],
+                "prefill_kernels_us_t2": p2["kernels_us"], "prefill_kernels_us_t1": p1["kernels_us"],
                 "prefill_ratio": round(p2["ms"] / p1["ms"], 3),
                 "prefill_tflops_t2": round(p2["tflops"], 1), "prefill_tflops_t1": round(p1["tflops"], 1),
                 "decode_us_t2": round(d2["us"], 2), "decode_us_t1": round(d1["us"], 2),
+                "decode_step_us_t2": d2["dist_us"], "decode_step_us_t1": d1["dist_us"],
+                "decode_kernels_us_t2": d2["kernels_us"], "decode_kernels_us_t1": d1["kernels_us"],
                 "decode_ratio": round(d2["us"] / d1["us"], 3),
                 "decode_GBps_t2": round(d2["GBps"], 1), "decode_GBps_t1": round(d1["GBps"], 1),
                 "model_allreduce_us_prefill_t2": round(2 * allreduce_model_us(msg_pre), 1),
@@ -629,6 +778,62 @@ def cpu_baseline(state):
     return steps, t_tot, threads
 
 
+def cpu_baseline_70b():
+    """The CPU oracle (NumPy float64) on a bounded sample of the headline
+    workload: one of the four sequences (S = 4096) of the 70B t=8 rank-0
+    step, whole -- ATTN stage, reduce over eight partials, MLP stage,
+    reduce -- repeated until 10 s.  The seven other ranks' partials are
+    seeded stand-ins made before timing (the reduce's arithmetic is the
+    same).  Only rank 0's blocks of the full weight matrices are drawn and
+    read; the oracle slices them out of full-shape arrays itself."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import layer as O
+    from tensor_transformer_layer_tp_amd import synth
+    w = synth.WORKLOADS["70b-t8-prefill"]
+    spec = O.Spec(w.hidden, w.heads, w.kv_heads, w.ffn)
+    d, hl, kvl, fl = dims(w.hidden, w.heads, w.kv_heads, w.ffn, w.tp)
+    h = w.hidden
+    rng = np.random.default_rng(0)
+
+    def draw(shape, scale):
+        return O.bf16_round(rng.standard_normal(shape) * scale)
+
+    W = {k: np.empty(shp) for k, shp in (("wq", (w.heads * d, h)), ("wk", (w.kv_heads * d, h)),
+                                         ("wv", (w.kv_heads * d, h)), ("wo", (h, w.heads * d)),
+                                         ("w_gate", (w.ffn, h)), ("w_up", (w.ffn, h)), ("w_down", (h, w.ffn)))}
+    W["wq"][:hl * d] = draw((hl * d, h), 0.02)
+    W["wk"][:kvl * d] = draw((kvl * d, h), 0.02)
+    W["wv"][:kvl * d] = draw((kvl * d, h), 0.02)
+    W["wo"][:, :hl * d] = draw((h, hl * d), 0.02)
+    W["w_gate"][:fl] = draw((fl, h), 0.02)
+    W["w_up"][:fl] = draw((fl, h), 0.02)
+    W["w_down"][:, :fl] = draw((h, fl), 0.02)
+    W["g1"] = np.ones(h)
+    W["g2"] = np.ones(h)
+    x = draw((1, w.seq, h), 1.0)
+    other = rng.standard_normal((1, w.seq, h)) * 0.1      # stand-in partial of each other rank
+    steps, t_tot = 0, 0.0
+    while steps < 5 and (t_tot < 10.0 or steps == 0):
+        t0 = time.perf_counter()
+        a0 = O.attn_stage(x, W, spec, w.tp, 0)["partial"]
+        hh = O.reduce([a0] + [other] * (w.tp - 1), x, spec)
+        m0 = O.mlp_stage(hh, W, spec, w.tp, 0)["partial"]
+        O.reduce([m0] + [other] * (w.tp - 1), hh, spec)
+        t_tot += time.perf_counter() - t0
+        steps += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    gemm, attn = prefill_flops(w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, 1, w.seq)
+    flops = sum(gemm.values()) + attn
+    return {
+        "value": round(flops * steps / t_tot / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{steps} run(s) of one of the four sequences (1 x 4096 tokens, {flops / 1e9:.0f} GFLOP each) of "
+                  f"the 70B t=8 rank-0 prefill step (ATTN stage, reduce over 8 partials, MLP stage, reduce) in "
+                  f"NumPy float64, {t_tot:.1f} s on {cpu_model()}",
+    }
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -641,22 +846,48 @@ def cpu_model():
 
 # ---------------------------------------------------------------- profile summaries
 
-# kernels whose HBM traffic is summarised: key -> (source file, name pattern,
-# algorithmic bytes per launch).  Template argument MODE 2 is the SwiGLU
-# epilogue, which only the gate/up projection uses.
-TRAFFIC_KERNELS = {
-    "gemm_up_7b_t2": ("gemm_bf16.hip", r"gemm_\w+_kernel<(?:[^>]*, )?2>",
+# The roofline kernels the profile summaries cover: key -> (source file,
+# kernel kind, shape, where the bench line reports it, dispatches of that
+# kernel made before the warmup steps, algorithmic bytes per launch).  A
+# projection GEMM's kernel name follows from its launch plan; the gate/up
+# projection is the only one with the SwiGLU epilogue (template MODE 2).
+ROOF_KERNELS = {
+    "gemm_up_70b_t8": ("gemm_bf16.hip", "gemm", (16384, 7168, 8192), ("roofline",), 0,
+                       2 * (16384 * 8192 + 7168 * 8192 + 16384 * 3584)),
+    "gemm_up_7b_t2": ("gemm_bf16.hip", "gemm", (2048, 11008, 4096), ("prefill_7b", "roofline"), 1,
                       2 * (2048 * 4096 + 11008 * 4096 + 2048 * 5504)),
-    "gemv_up_7b_t4": ("decode.hip", r"gemv_kernel<1, \d+, \d+, 2, true, false, \d+>",
+    "gemv_up_7b_t4": ("decode.hip", "gemv", (5504, 4096), ("decode", "roofline"), 0,
                       2 * (5504 * 4096 + 4096 + 2752)),
+    "gemv_up_70b_t8": ("decode.hip", "gemv", (7168, 8192), ("decode_70b", "roofline"), 0,
+                       2 * (7168 * 8192 + 8192 + 3584)),
 }
+# tile configuration -> the kernel template it launches (the planner's choices)
+CFG_KERNEL = {11: "gemm_vgpr_kernel<256, 256, 2, 4, ", 12: "gemm_vgpr_kernel<256, 128, 4, 2, ",
+              13: "gemm_vgpr_kernel<256, 192, 8, 1, ", 14: "gemm_ws_kernel<256, 256, 2, 4, ",
+              15: "gemm_ws_kernel<256, 192, 8, 1, ", 16: "gemm_ws_kernel<256, 128, 4, 2, "}
+
+
+def roof_patterns(key):
+    """Regexes of the launch kinds of one roofline kernel."""
+    import re
+    _, kind, shape, _, _, _ = ROOF_KERNELS[key]
+    if kind == "gemv":
+        # batch-1 bf16 GEMV with the SwiGLU epilogue and the fused norm; its
+        # NI (16-byte chunks per thread) follows from K
+        kc = shape[1] // 8
+        ni = 1 if kc <= 256 else (kc + 255) // 256
+        return [r"gemv_kernel<1, \d+, " + str(ni) + r", 2, true, false, \d+>"]
+    from tensor_transformer_layer_tp_amd import gemm_plan
+    return [re.escape(CFG_KERNEL[c] + "2>") if c in CFG_KERNEL else r"gemm_\w+_kernel<[^>]*, 2>"
+            for c, _ in gemm_plan(*shape, "swiglu")]
 
 
 def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
     """Per-launch HBM bytes of the roofline kernels from two rocprofv3 --pmc
     runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by
     the same counter's reading for the known-size copy (--calib-copy), and
-    a kernel-duration table from the --kernel-trace --stats run."""
+    a kernel-duration table from the --kernel-trace --stats run of the same
+    bench command, next to the live event timings of its JSON line."""
     import csv
     import glob
     import re
@@ -668,28 +899,36 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
             out.extend(csv.DictReader(open(f)))
         return out
 
+    def dig(obj, path):
+        for k in path:
+            obj = obj.get(k) if isinstance(obj, dict) else None
+        return obj
+
     calib = calib_mib * 1024 * 1024
     traffic, facts = {}, {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rs = [r for r in rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        rs = sorted((r for r in rows(d, "counter_collection.csv") if r["Counter_Name"] == counter),
+                    key=lambda r: int(r["Dispatch_Id"]))
+        # the calibration copies are the run's first three large copies (--calib-copy
+        # makes them before anything else; the copy-ceiling copies come later)
         copies = [float(r["Counter_Value"]) * 1024 for r in rs
-                  if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 > calib / 2]
-        if not copies:
-            raise SystemExit(f"no calibration copy found in {d}")
+                  if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 > calib / 8][:3]
+        if len(copies) < 3:
+            raise SystemExit(f"no calibration copies found in {d}")
         factor = calib / statistics.median(copies)
         facts[counter] = factor
-        for key, (_, pat, _) in TRAFFIC_KERNELS.items():
+        for key in ROOF_KERNELS:
             # one projection may run as several launches (a column split): bytes per
             # projection = all matching dispatches / dispatches of one launch kind
             names = {}
             for r in rs:
-                if re.search(pat, r["Kernel_Name"]):
+                if any(re.search(p, r["Kernel_Name"]) for p in roof_patterns(key)):
                     names.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024 * factor)
             if names:
                 calls = max(len(v) for v in names.values())
                 traffic.setdefault(key, {})[counter] = (sum(sum(v) for v in names.values()) / calls, calls)
     rec = {}
-    for key, (src, pat, alg) in TRAFFIC_KERNELS.items():
+    for key, (src, _, _, _, _, alg) in ROOF_KERNELS.items():
         if key not in traffic or len(traffic[key]) != 2:
             continue
         f, nf = traffic[key]["FETCH_SIZE"]
@@ -705,51 +944,59 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_json, calib_mib):
     # kernel durations from the trace run, next to the bench's live event timings
     stats = rows(trace_dir, "kernel_stats.csv")
     line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    disp = sorted(rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
     md = ["| kernel | calls | avg µs | min µs | max µs | % time |", "|---|---:|---:|---:|---:|---:|"]
-    for r in stats[:24]:
+    for r in stats[:30]:
         name = r["Name"].replace("|", "/")
         name = name if len(name) <= 110 else name[:107] + "..."
         md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     live = []
-    up = [r for r in stats if re.search(TRAFFIC_KERNELS["gemm_up_7b_t2"][1], r["Name"])]
-    rocprof_up = sum(float(r["AverageNs"]) for r in up) / 1e3
-    kinds = [re.search(r"gemm_\w+_kernel<[^>]*>", r["Name"]).group(0) for r in up]
-    # the timed window: the 7B t=2 prefill stack runs the other rank's MLP once, then
-    # `warmup` untimed steps, then the `steps` timed ones (one projection each)
-    disp = sorted(rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
-    lo, k = 1 + int(line["warmup"]), int(line["steps"])
-    window = 0.0
-    for r in up:
-        d = [int(x["End_Timestamp"]) - int(x["Start_Timestamp"]) for x in disp if x["Kernel_Name"] == r["Name"]]
-        window += statistics.mean(d[lo:lo + k]) / 1e3 if len(d) >= lo + k else float("nan")
-    live.append(f"- prefill roofline kernel ({line['roofline']['kernel']}): live HIP-event average "
-                f"{line['roofline']['avg_us']} µs over the {line['roofline']['launches']} timed projections; "
-                f"rocprof over the same {k} dispatches (after the {line['warmup']} warmup steps): {window:.1f} µs, "
-                f"over all {up[0]['Calls'] if up else 0} dispatches of the run: {rocprof_up:.1f} µs "
-                f"(sum over its {len(up)} launch kind(s): {', '.join(kinds)})")
-    if "decode" in line:
-        dk = line["decode"]["kernels"].get("gemv_up")
-        gv = [r for r in stats if re.search(TRAFFIC_KERNELS["gemv_up_7b_t4"][1], r["Name"])]
-        if dk and gv:
-            live.append(f"- decode roofline kernel ({line['decode']['roofline']['kernel']}): live HIP-event "
-                        f"average {dk['avg_us']} µs over {dk['launches']} launches; rocprof "
-                        f"{float(gv[0]['AverageNs']) / 1e3:.1f} µs (events bracketing every short kernel "
-                        f"under the tracer inflate the live figure)")
+    lo_w, k = int(line["warmup"]), int(line["steps"])
+    for key, (_, kind, _, path, skip, _) in ROOF_KERNELS.items():
+        roof = dig(line, path)
+        if not roof:
+            continue
+        pats = roof_patterns(key)
+        kinds = [r for r in stats if any(re.search(p, r["Name"]) for p in pats)]
+        if not kinds:
+            continue
+        if kind == "gemm":
+            # the timed window: `skip` earlier launches, `warmup` untimed steps,
+            # then the `steps` timed ones (one projection per step)
+            window = 0.0
+            for r in kinds:
+                d = [int(x["End_Timestamp"]) - int(x["Start_Timestamp"]) for x in disp if x["Kernel_Name"] == r["Name"]]
+                lo = skip + lo_w
+                window += statistics.mean(d[lo:lo + k]) / 1e3 if len(d) >= lo + k else float("nan")
+            allavg = sum(float(r["AverageNs"]) for r in kinds) / 1e3
+            names = ", ".join(re.search(r"gemm_\w+_kernel<[^>]*>", r["Name"]).group(0) for r in kinds)
+            live.append(f"- `{key}` ({roof['kernel']}): live HIP-event average {roof['avg_us']} µs over the "
+                        f"{roof['launches']} timed projections; rocprof over the same {k} dispatches (after "
+                        f"{skip} earlier launch(es) and the {lo_w} warmup steps): {window:.1f} µs; over all "
+                        f"{kinds[0]['Calls']} dispatches of the run: {allavg:.1f} µs "
+                        f"({names})")
+        else:
+            dk = dig(line, path[:-1] + ("kernels",)) or {}
+            gv = dk.get("gemv_up", {})
+            live.append(f"- `{key}` ({roof['kernel']}): live HIP-event average {gv.get('avg_us')} µs over "
+                        f"{gv.get('launches')} launches; rocprof {float(kinds[0]['AverageNs']) / 1e3:.1f} µs (events "
+                        f"bracketing every short kernel under the tracer inflate the live figure)")
     with open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w") as fh:
-        fh.write("# Kernel durations of `bench.py --no-cpu --no-70b` (rocprofv3 --kernel-trace --stats)\n\n")
-        fh.write("Commands: see profiles/README.md.  Bench line of the same run:\n\n")
+        fh.write("# Kernel durations of `bench.py` (rocprofv3 --kernel-trace --stats)\n\n")
+        fh.write("Command: profiles/README.md, command 1.  Bench line of the same run: "
+                 f"{line['config']['workload'][:60]}... {line['value']} TFLOP/s, {line['ms_per_step']} ms per "
+                 f"step ({line['steps']} steps after {line['warmup']} warmup steps).\n\n")
         fh.write("\n".join(live) + "\n\n" + "\n".join(md) + "\n")
     print(json.dumps(rec, indent=1))
 
 
-def summarize_mfma(pmc_dir):
-    """MFMA evidence for the prefill kernels of the 7B t=2 step from one
-    rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE run: per kernel
-    kind the dispatch count, mean duration, rocprofv3's MfmaUtil (MFMA busy
-    cycles / (active cycles x SIMDs)), the executed bf16 MFMA FLOPs per
-    dispatch and the clock the kernel ran at (active cycles per XCD over the
-    duration)."""
+def summarize_mfma(pmc_dir, out_name):
+    """MFMA evidence for the prefill kernels from one rocprofv3 --pmc MfmaUtil
+    MfmaFlopsBF16 GRBM_GUI_ACTIVE run: per kernel kind the dispatch count,
+    mean duration, rocprofv3's MfmaUtil (MFMA busy cycles / (active cycles x
+    SIMDs)), the executed bf16 MFMA FLOPs per dispatch and the clock the
+    kernel ran at (active cycles per XCD over the duration)."""
     import csv
     import glob
     import re
@@ -772,12 +1019,9 @@ def summarize_mfma(pmc_dir):
     kinds = {}
     for d in disp.values():
         kinds.setdefault(d["name"], []).append(d)
-    w = synth_workload("7b-t2-prefill")
-    gemm, attn = prefill_flops(w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, w.batch, w.seq)
     mode_of = {"0": "fp32 partial (out and down projections)", "1": "Q/K/V + rotary", "2": "gate/up + SwiGLU"}
     md = ["| kernel | dispatches | mean µs | MfmaUtil % | executed bf16 MFMA GFLOP per dispatch | clock GHz |",
           "|---|---:|---:|---:|---:|---:|"]
-    up_flops = 0.0
     for name, ds in sorted(kinds.items(), key=lambda kv: -statistics.mean(x["us"] for x in kv[1])):
         us = statistics.mean(x["us"] for x in ds)
         util = statistics.mean(x.get("MfmaUtil", float("nan")) for x in ds)
@@ -790,20 +1034,55 @@ def summarize_mfma(pmc_dir):
             label = f"attn_prefill_kernel<{a.group(1)}, {a.group(2)}> (causal GQA attention)"
         if m:
             label += f" ({mode_of.get(m.group(1), '')})"
-            if m.group(1) == "2":
-                up_flops += gf
         md.append(f"| `{label[:90]}` | {len(ds)} | {us:.1f} | {util:.1f} | {gf:.2f} | {ghz:.2f} |")
-    lines = ["# MFMA counters of the 7B t=2 prefill kernels (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE)",
-             "",
-             "Command: see profiles/README.md (command 4). MfmaUtil is rocprofv3's derived counter: MFMA busy cycles "
-             "over active cycles times SIMDs, at the clock the kernel ran at; executed FLOPs are "
-             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; the clock is GRBM_GUI_ACTIVE per XCD over the dispatch duration.",
-             "",
-             f"- gate/up projection: {up_flops:.2f} GFLOP executed by its launch kinds per projection against "
-             f"{gemm['gemm_up'] / 1e9:.2f} algorithmic (zero padding of ragged tiles is the difference)",
-             "",
-             *md]
-    with open(os.path.join(ROOT, "profiles", "mfma_counters.md"), "w") as fh:
+    notes = []
+    for key, (_, kind, shape, _, _, _) in ROOF_KERNELS.items():
+        if kind != "gemm":
+            continue
+        ex = sum(statistics.mean(x.get("MfmaFlopsBF16", 0.0) for x in kinds[n]) for n in kinds
+                 if any(re.search(p, n) for p in roof_patterns(key))) / 1e9
+        if ex:
+            M, N, K = shape
+            notes.append(f"- `{key}` (M={M} N={N} K={K}): {ex:.2f} GFLOP executed by its launch kinds per projection "
+                         f"against {2 * M * N * K / 1e9:.2f} algorithmic (zero padding of ragged tiles is the difference)")
+    lines = ["# MFMA counters of the prefill kernels (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE)", "",
+             "Command: profiles/README.md. MfmaUtil is rocprofv3's derived counter: MFMA busy cycles over active "
+             "cycles times SIMDs, at the clock the kernel ran at; executed FLOPs are SQ_INSTS_VALU_MFMA_MOPS_BF16 x "
+             "512; the clock is GRBM_GUI_ACTIVE per XCD over the dispatch duration.", "", *notes, "", *md]
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_warmup(pmc_dir, key, out_name):
+    """The first dispatches of one roofline GEMM in a fresh process, from a
+    rocprofv3 --pmc GRBM_GUI_ACTIVE run: duration and clock (active cycles
+    per XCD over the duration) per dispatch, in launch order."""
+    import csv
+    import glob
+    import re
+    import statistics
+    rows = []
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        rows.extend(csv.DictReader(open(f)))
+    pats = roof_patterns(key)
+    ds = sorted(({"id": int(r["Dispatch_Id"]), "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
+                  "cyc": float(r["Counter_Value"])} for r in rows
+                 if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and any(re.search(p, r["Kernel_Name"]) for p in pats)),
+                key=lambda d: d["id"])
+    _, _, shape, _, _, _ = ROOF_KERNELS[key]
+    flops = 2.0 * shape[0] * shape[1] * shape[2]
+    md = ["| dispatch | µs | clock GHz | TFLOP/s |", "|---:|---:|---:|---:|"]
+    for i, d in enumerate(ds[:40]):
+        md.append(f"| {i} | {d['us']:.1f} | {d['cyc'] / 8 / (d['us'] * 1e3):.3f} | {flops / (d['us'] * 1e-6) / 1e12:.0f} |")
+    tail = ds[10:40]
+    lines = [f"# First dispatches of `{key}` in a fresh process (rocprofv3 --pmc GRBM_GUI_ACTIVE)", "",
+             "Command: profiles/README.md.  Clock = GRBM_GUI_ACTIVE / 8 XCDs / duration.", ""]
+    if tail:
+        lines.append(f"- dispatches 10-39: mean {statistics.mean(d['us'] for d in tail):.1f} µs; dispatch 0: "
+                     f"{ds[0]['us']:.1f} µs, dispatches 1-4: {statistics.mean(d['us'] for d in ds[1:5]):.1f} µs")
+    lines += ["", *md]
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -834,8 +1113,11 @@ def main():
     if args.summarize:
         summarize(*args.summarize, args.calib_copy or 1024)
         return
+    if args.summarize_warmup:
+        summarize_warmup(*args.summarize_warmup)
+        return
     if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma[0])
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
@@ -853,47 +1135,65 @@ def main():
                                    "all-reduces a real t=2 layer adds, not a measurement",
                           "points": table}), flush=True)
         return
-    pre, state = run_7b(args, torch)
-    dec = None if args.no_decode else run_7b_decode(args, torch)
     big = None if args.no_70b else run_70b(args, torch)
-    w = state[0]
+    small = None if args.no_7b else run_7b(args, torch)
+    dec = None if (args.no_decode or args.no_7b) else run_7b_decode(args, torch)
+    if big is None and small is None:
+        print("nothing to run (--no-7b and --no-70b)", file=sys.stderr)
+        sys.exit(2)
+    if big is not None:
+        head = big[0]
+        config = {
+            "workload": "70b-t8-prefill: rank 0 of a 70B-shaped GQA layer split t=8 (hidden 8192, 8 of 64 query heads "
+                        "+ 1 of 8 KV heads x 128, SwiGLU 3584 of 28672, RMSNorm, RoPE), bf16, batch 4 x seq 4096, "
+                        "causal; step = ATTN stage + reduce of 8 partials + MLP stage + reduce of 8 partials",
+            "global_batch": 4, "seq_len": 4096, "parallelism": "tp8 shard (rank 0) on 1 GPU",
+        }
+    else:
+        head = small[0]
+        w = small[1][0]
+        config = {
+            "workload": "7b-t2-prefill: rank 0 of a 7B-shaped layer split t=2 (hidden 4096, 16 of 32 heads x 128, "
+                        "SwiGLU 5504 of 11008, RMSNorm, RoPE), bf16, batch 1 x seq 2048, causal; step = ATTN stage "
+                        "+ reduce + MLP stage + reduce",
+            "global_batch": w.batch, "seq_len": w.seq, "parallelism": "tp2 shard (rank 0) on 1 GPU",
+        }
     line = {
         "metric": METRIC,
-        "value": pre["tflops"],
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pre["ms_per_step"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random-init)",
-        "config": {
-            "workload": "7b-t2-prefill: rank 0 of a 7B-shaped layer split t=2 (hidden 4096, 16 of 32 heads x 128, "
-                        "SwiGLU 5504 of 11008, RMSNorm, RoPE), bf16, batch 1 x seq 2048, causal; step = ATTN stage "
-                        "+ reduce + MLP stage + reduce",
-            "global_batch": w.batch, "seq_len": w.seq, "parallelism": "tp2 shard (rank 0) on 1 GPU",
-        },
+        "config": config,
     }
     for k in ("step_ms", "mfma_frac", "flops_per_step", "gemm_tflops", "gemm_mfma_frac",
-              "ms_per_step_all_kernels_bracketed", "kernels", "roofline", "sequence_parallel"):
-        line[k] = pre[k]
+              "ms_per_step_all_kernels_bracketed", "kernels", "clock", "roofline"):
+        line[k] = head[k]
+    line["hbm_copy_GBps"] = copy_ceiling(torch)
+    if big is not None and small is not None:
+        line["prefill_7b"] = small[0]
+    if big is not None and big[1] is not None:
+        line["decode_70b"], line["decode_70b_fp8"] = big[1]
     if dec is not None:
         line["decode"], line["decode_fp8"], line["decode_paged"] = dec
-    if big is not None:
-        line["prefill_70b"] = big[0]
-        if big[1] is not None:
-            line["decode_70b"], line["decode_70b_fp8"] = big[1]
     if not args.no_cpu:
-        steps, secs, threads = cpu_baseline(state)
-        line["cpu_baseline"] = {
-            "value": round(pre["flops_per_step"] * steps / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{steps} full rank-0 prefill step(s) of the same workload (B=1, S=2048) in NumPy float64, "
-                      f"{secs:.1f} s on {cpu_model()}",
-        }
+        if big is not None:
+            line["cpu_baseline"] = cpu_baseline_70b()
+        else:
+            steps, secs, threads = cpu_baseline(small[1])
+            line["cpu_baseline"] = {
+                "value": round(head["flops_per_step"] * steps / secs / 1e12, 5), "unit": "TFLOP/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{steps} full rank-0 prefill step(s) of the same workload (B=1, S=2048) in NumPy "
+                          f"float64, {secs:.1f} s on {cpu_model()}",
+            }
     print(json.dumps(line), flush=True)
 
 
