@@ -7,12 +7,15 @@ Prints ONE JSON line.  The headline step is the whole prefill hot path of
 rank 0 of a 70B-shaped GQA layer split eight ways (hidden 8192, 8 of 64
 query heads + 1 of 8 KV heads x 128, SwiGLU 3584 of 28672, RMSNorm, RoPE,
 bf16, batch 4 x 4096 tokens, causal) -- the largest single-GPU prefill
-configuration: ATTN stage (RMSNorm, Q/K/V projection with RoPE and KV-cache
-write, causal attention, row-parallel output projection) -> reduce of the
-eight ranks' partials + residual -> MLP stage (RMSNorm, gate/up projection
-with SwiGLU, row-parallel down projection) -> reduce.  The other ranks'
-partials are seeded stand-ins, resident in HBM before timing (they stand
-for the other GPUs' contributions).
+configuration, as a layer of a stack runs it: ATTN stage (Q/K/V projection
+of the normalised input with RoPE and KV-cache write, causal attention,
+row-parallel output projection) -> reduce of the eight ranks' partials +
+residual, fused with the MLP stage's RMSNorm -> MLP stage (gate/up
+projection with SwiGLU, row-parallel down projection) -> reduce fused with
+the RMSNorm of the next layer's input.  Every norm of a layer is in the
+step; the first layer input's norm is made once before timing.  The other
+ranks' partials are seeded stand-ins, resident in HBM before timing (they
+stand for the other GPUs' contributions).
 
 `value` is the step's algorithmic FLOPs (GEMMs + causal attention) per
 second.  `roofline` covers the dominant kernel (the gate/up projection GEMM),
@@ -279,7 +282,7 @@ def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others,
     """Rank 0's shard plus the buffers of one prefill step.  The other
     ranks' partials are either computed by their own shards once
     (exact_others) or seeded N(0, 0.1^2) stand-ins (timing only)."""
-    from tensor_transformer_layer_tp_amd import ATTN, MLP, Shard, partial_reduce
+    from tensor_transformer_layer_tp_amd import ATTN, MLP, PRENORM, Shard, partial_reduce
     B, S = int(x.shape[0]), int(x.shape[1])
     sh = Shard(hidden, heads, kv_heads, ffn, t, 0)
     sh.load_weights(wdev)
@@ -289,6 +292,8 @@ def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others,
     pm = [torch.empty((B, S, hidden), dtype=torch.float32, device="cuda") for _ in range(t)]
     hbuf = torch.empty_like(x)
     ybuf = torch.empty_like(x)
+    n2buf = torch.empty_like(x)
+    n1next = torch.empty_like(x)
     if exact_others:
         for r in range(1, t):
             o = Shard(hidden, heads, kv_heads, ffn, t, r)
@@ -310,13 +315,18 @@ def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others,
         for r in range(1, t):
             pa[r].normal_(0.0, 0.1, generator=g)
             pm[r].normal_(0.0, 0.1, generator=g)
+    # the layer input's norm, made once: in a stack of layers the previous
+    # layer's last reduce produces it (as every step below does for the next)
+    n1 = sh.norm(1, x)
     torch.cuda.synchronize()
 
     def step():
-        sh.prefill(ATTN, x, kv, out=pa[0])
-        partial_reduce(pa, residual=x, out=hbuf)
-        sh.prefill(MLP, hbuf, out=pm[0])
-        partial_reduce(pm, residual=hbuf, out=ybuf)
+        # ATTN stage on the normalised input, the reduce with the MLP stage's
+        # norm, the MLP stage, the reduce with the next layer's input norm
+        sh.prefill(ATTN | PRENORM, n1, kv, out=pa[0])
+        sh.reduce_norm(2, pa, residual=x, out=hbuf, norm_out=n2buf)
+        sh.prefill(MLP | PRENORM, n2buf, out=pm[0])
+        sh.reduce_norm(1, pm, residual=hbuf, out=ybuf, norm_out=n1next)
 
     return sh, kv, step
 
@@ -1146,7 +1156,8 @@ def main():
         config = {
             "workload": "70b-t8-prefill: rank 0 of a 70B-shaped GQA layer split t=8 (hidden 8192, 8 of 64 query heads "
                         "+ 1 of 8 KV heads x 128, SwiGLU 3584 of 28672, RMSNorm, RoPE), bf16, batch 4 x seq 4096, "
-                        "causal; step = ATTN stage + reduce of 8 partials + MLP stage + reduce of 8 partials",
+                        "causal; step = ATTN stage + reduce of 8 partials with the MLP norm + MLP stage + reduce of "
+                        "8 partials with the next layer's input norm",
             "global_batch": 4, "seq_len": 4096, "parallelism": "tp8 shard (rank 0) on 1 GPU",
         }
     else:
@@ -1155,7 +1166,7 @@ def main():
         config = {
             "workload": "7b-t2-prefill: rank 0 of a 7B-shaped layer split t=2 (hidden 4096, 16 of 32 heads x 128, "
                         "SwiGLU 5504 of 11008, RMSNorm, RoPE), bf16, batch 1 x seq 2048, causal; step = ATTN stage "
-                        "+ reduce + MLP stage + reduce",
+                        "+ reduce with the MLP norm + MLP stage + reduce with the next layer's input norm",
             "global_batch": w.batch, "seq_len": w.seq, "parallelism": "tp2 shard (rank 0) on 1 GPU",
         }
     line = {

@@ -277,6 +277,26 @@ int tp_partial_reduce(const float *const *partials, int t,
                       const void *residual, void *out, long long n,
                       int out_dtype, void *stream);
 
+/* tp_shard_reduce_norm -- the reduce of a stage's partials together with
+ * the RMSNorm that the next stage applies to its result, in one pass over
+ * `rows` rows of `hidden` values:
+ *   out[i]      = (sum_{r<t} partials[r][i]) + residual[i]      (as tp_partial_reduce)
+ *   norm_out[i] = RMSNorm(out[i]) * gain                       (as tp_shard_norm)
+ * with the shard's gain g1 (which = 1: the input of an ATTN stage, e.g. the
+ * next layer's) or g2 (which = 2: this layer's MLP stage); both stored in the
+ * shard's dtype, the norm taken of the stored out.  The partials must be
+ * combined before the layer can go on (byteledger "Tensor Parallelism:
+ * Splitting One Layer Across GPUs", "Communication is the constraint"), and
+ * the next stage's first step normalises exactly that result, so the two
+ * share one read of it.  Feed norm_out to the next stage with
+ * TP_STAGE_PRENORM.  bf16 shards with hidden <= 8192 take one fused kernel
+ * whose results equal the two separate calls bit for bit; other shards run
+ * those two calls.  Layout and alignment as tp_partial_reduce (partials: HOST
+ * array of t device pointers to [rows, hidden] fp32; residual may be NULL);
+ * TP_E_STATE before tp_shard_load_weights; rows == 0 touches nothing. */
+int tp_shard_reduce_norm(tp_shard *s, int which, const float *const *partials, int t, const void *residual,
+                         void *out, void *norm_out, long long rows, void *stream);
+
 /* tp_shard_fp8_view -- device addresses of the E4M3 copy of a packed weight
  * (which = 0 Q/K/V [(heads+2 kv_heads)/t * d, hidden], 1 W_o block
  * [hidden, heads/t * d], 2 gate/up [2 ffn/t (ffn/t for GELU), hidden],
@@ -337,7 +357,8 @@ int tp_shard_debug_view(tp_shard *s, int which, void **ptr);
 #define TP_K_GEMV_OUT     8
 #define TP_K_GEMV_UP      9
 #define TP_K_GEMV_DOWN    10
-#define TP_K_COUNT        11
+#define TP_K_REDUCE_NORM  11
+#define TP_K_COUNT        12
 #define TP_K_MASK(k)      (1 << (k))
 int tp_shard_timing(tp_shard *s, int enable);
 int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *launches);

@@ -238,6 +238,35 @@ class Shard:
                 "tp_shard_norm")
         return out
 
+    def reduce_norm(self, which: int, partials, residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    norm_out: torch.Tensor | None = None, stream=None):
+        """out = (sum of the fp32 partials in rank order) + residual, and
+        norm_out = RMSNorm(out) with gain g1 (which=1) or g2 (which=2), in one
+        pass; partials [..., hidden].  Returns (out, norm_out)."""
+        partials = list(partials)
+        if not partials:
+            raise ValueError("need at least one partial")
+        shape = tuple(partials[0].shape)
+        if shape[-1] != self.hidden:
+            raise ValueError("partials must end in hidden")
+        rows = partials[0].numel() // self.hidden
+        ptrs = (C.c_void_p * len(partials))(*[_dev(p, f"partial[{i}]", torch.float32, shape).value
+                                              for i, p in enumerate(partials)])
+        if residual is not None:
+            _dev(residual, "residual", self.torch_dtype)
+            if residual.numel() != rows * self.hidden:
+                raise ValueError("residual size differs from the partials")
+        if out is None:
+            out = torch.empty(shape, dtype=self.torch_dtype, device=partials[0].device)
+        if norm_out is None:
+            norm_out = torch.empty_like(out)
+        N.check(N.lib().tp_shard_reduce_norm(self._h, which, ptrs, len(partials),
+                                             C.c_void_p(residual.data_ptr()) if residual is not None else None,
+                                             _dev(out, "out", self.torch_dtype, shape),
+                                             _dev(norm_out, "norm_out", self.torch_dtype, shape), rows,
+                                             _stream(stream)), "tp_shard_reduce_norm")
+        return out, norm_out
+
     def fp8_weights(self, which: str, stream=None):
         """Copies of the E4M3 codes (uint8 [rows, cols], packed row order) and
         row scales (fp32 [rows]) of 'qkv', 'o', 'up' or 'down'."""

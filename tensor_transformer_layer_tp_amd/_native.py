@@ -21,7 +21,7 @@ TP_ACT_SWIGLU, TP_ACT_GELU = 0, 1
 TP_PROJ_PARTIAL, TP_PROJ_QKV, TP_PROJ_SWIGLU, TP_PROJ_GELU = 0, 1, 2, 3
 # kernel kinds of the shard's event timer (TP_K_*)
 KERNEL_KINDS = ["rmsnorm", "gemm_qkv", "attn_prefill", "gemm_out", "gemm_up", "gemm_down", "gemv_qkv",
-                "attn_decode", "gemv_out", "gemv_up", "gemv_down"]
+                "attn_decode", "gemv_out", "gemv_up", "gemv_down", "reduce_norm"]
 
 
 class tp_opts(C.Structure):
@@ -54,6 +54,8 @@ SIGNATURES = [
     ("tp_shard_debug_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),
     ("tp_kv_create_paged", C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_void_p)]),
     ("tp_kv_set_block_table", C.c_int, [C.c_void_p, C.c_void_p]),
+    ("tp_shard_reduce_norm", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p), C.c_int, C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_longlong, C.c_void_p]),
     ("tp_partial_reduce_scatter", C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_longlong,
                                             C.c_int, C.c_int, C.c_void_p]),
     ("tp_all_gather", C.c_int, [C.c_void_p, C.c_int, C.c_longlong, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),

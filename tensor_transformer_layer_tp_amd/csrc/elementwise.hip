@@ -14,63 +14,74 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
     return red[0] + red[1] + red[2] + red[3];
 }
 
+// bf16 pair <-> floats
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf(float a, float b) {
+    return (uint32_t)f2bf_bits(a) | ((uint32_t)f2bf_bits(b) << 16);
+}
+
 // n = x / sqrt(mean(x^2) + eps) * g, one row per work-group, fp32 arithmetic,
-// bf16 result rounded to nearest even.  Requires n % 8 == 0.  With MAXC > 0
-// the row (at most 2048 * MAXC elements) is read once and kept in registers;
-// MAXC = 0 reads it twice, for any width.
-template <int MAXC>
+// bf16 result rounded to nearest even.  Thread t owns the 4-value groups
+// t + 256 j of the row (8-byte loads, a wave's load covering 512 contiguous
+// bytes) and sums the squares of its groups in order; reduce_norm_bf16_kernel
+// uses the same ownership and order, so the two agree bit for bit.  With
+// MAXJ > 0 the row (at most 1024 * MAXJ values) is read once and kept in
+// registers; MAXJ = 0 reads it twice, for any width.  Requires n % 4 == 0.
+template <int MAXJ>
 __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const bf16* __restrict__ x,
                                                            const bf16* __restrict__ g,
                                                            bf16* __restrict__ out, int n, float eps) {
     __shared__ float red[4];
     const bf16* xr = x + (long long)blockIdx.x * n;
     bf16* orow = out + (long long)blockIdx.x * n;
-    const int nc = n / 8;
+    const int nq = n / 4;
     float ss = 0.f;
-    if constexpr (MAXC > 0) {
-        u16x8 v[MAXC], w[MAXC];
+    if constexpr (MAXJ > 0) {
+        uint2 v[MAXJ], w[MAXJ];
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int c = min((int)threadIdx.x + 256 * i, nc - 1);   // clamped: issued and in bounds
-            v[i] = *(const u16x8*)(xr + c * 8);
-            w[i] = *(const u16x8*)(g + c * 8);
+        for (int j = 0; j < MAXJ; ++j) {
+            const int q = min((int)threadIdx.x + 256 * j, nq - 1);   // clamped: issued and in bounds
+            v[j] = *(const uint2*)(xr + 4 * q);
+            w[j] = *(const uint2*)(g + 4 * q);
         }
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i)
-            if ((int)threadIdx.x + 256 * i < nc)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = bfbits2f(v[i][e]);
-                    ss += f * f;
-                }
+        for (int j = 0; j < MAXJ; ++j)
+            if ((int)threadIdx.x + 256 * j < nq) {
+                const float f0 = lo_bf(v[j].x), f1 = hi_bf(v[j].x), f2 = lo_bf(v[j].y), f3 = hi_bf(v[j].y);
+                ss += f0 * f0;
+                ss += f1 * f1;
+                ss += f2 * f2;
+                ss += f3 * f3;
+            }
         const float rs = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int c = threadIdx.x + 256 * i;
-            if (c < nc) {
-                u16x8 o;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = f2bf_bits(bfbits2f(v[i][e]) * rs * bfbits2f(w[i][e]));
-                *(u16x8*)(orow + c * 8) = o;
+        for (int j = 0; j < MAXJ; ++j) {
+            const int q = threadIdx.x + 256 * j;
+            if (q < nq) {
+                uint2 o;
+                o.x = pack_bf(lo_bf(v[j].x) * rs * lo_bf(w[j].x), hi_bf(v[j].x) * rs * hi_bf(w[j].x));
+                o.y = pack_bf(lo_bf(v[j].y) * rs * lo_bf(w[j].y), hi_bf(v[j].y) * rs * hi_bf(w[j].y));
+                *(uint2*)(orow + 4 * q) = o;
             }
         }
     } else {
-        for (int c = threadIdx.x; c < nc; c += 256) {
-            u16x8 v = *(const u16x8*)(xr + c * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float f = bfbits2f(v[e]);
-                ss += f * f;
-            }
+        for (int q = threadIdx.x; q < nq; q += 256) {
+            const uint2 v = *(const uint2*)(xr + 4 * q);
+            const float f0 = lo_bf(v.x), f1 = hi_bf(v.x), f2 = lo_bf(v.y), f3 = hi_bf(v.y);
+            ss += f0 * f0;
+            ss += f1 * f1;
+            ss += f2 * f2;
+            ss += f3 * f3;
         }
         const float rs = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
-        for (int c = threadIdx.x; c < nc; c += 256) {
-            u16x8 v = *(const u16x8*)(xr + c * 8);
-            u16x8 w = *(const u16x8*)(g + c * 8);
-            u16x8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = f2bf_bits(bfbits2f(v[e]) * rs * bfbits2f(w[e]));
-            *(u16x8*)(orow + c * 8) = o;
+        for (int q = threadIdx.x; q < nq; q += 256) {
+            const uint2 v = *(const uint2*)(xr + 4 * q);
+            const uint2 w = *(const uint2*)(g + 4 * q);
+            uint2 o;
+            o.x = pack_bf(lo_bf(v.x) * rs * lo_bf(w.x), hi_bf(v.x) * rs * hi_bf(w.x));
+            o.y = pack_bf(lo_bf(v.y) * rs * lo_bf(w.y), hi_bf(v.y) * rs * hi_bf(w.y));
+            *(uint2*)(orow + 4 * q) = o;
         }
     }
 }
@@ -172,6 +183,75 @@ __global__ __launch_bounds__(256) void reduce_kernel(Parts parts, int t, const v
     }
 }
 
+// The reduce and the next stage's RMSNorm in one pass, one row of n values
+// per work-group: out = bf16(sum_r parts[r] + residual) exactly as
+// reduce_kernel stores it (fp32 adds in rank order, then the residual, then
+// RNE), and nout = bf16(out * rsqrt(mean(out^2) + eps) * g) exactly as
+// rmsnorm_bf16_kernel<MAXJ> computes it from the stored out (same 4-value
+// group ownership, same order of the sum of squares), so the fused pass
+// equals the two separate launches bit for bit.  Each partial is read with
+// one 16-byte load per lane, a wave covering 1 KB of contiguous fp32; the
+// row's bf16 values stay in registers between the two halves.
+// n % 4 == 0, n <= 1024 * MAXJ.
+template <int TT, int MAXJ>
+__global__ __launch_bounds__(256) void reduce_norm_bf16_kernel(Parts parts, int t, const bf16* __restrict__ residual,
+                                                               bf16* __restrict__ out, const bf16* __restrict__ g,
+                                                               bf16* __restrict__ nout, int n, float eps) {
+    __shared__ float red[4];
+    const long long row0 = (long long)blockIdx.x * n;
+    const int nq = n / 4;
+    uint2 hv[MAXJ];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+        const int q = threadIdx.x + 256 * j;
+        if (q < nq) {
+            const long long e = row0 + 4LL * q;
+            f32x4 s;
+            if constexpr (TT > 0) {
+                f32x4 v[TT];
+#pragma unroll
+                for (int r = 0; r < TT; ++r) v[r] = __builtin_nontemporal_load((const f32x4*)(parts.p[r] + e));
+                s = v[0];
+#pragma unroll
+                for (int r = 1; r < TT; ++r) s += v[r];
+            } else {
+                s = __builtin_nontemporal_load((const f32x4*)(parts.p[0] + e));
+                for (int r = 1; r < t; ++r) s += __builtin_nontemporal_load((const f32x4*)(parts.p[r] + e));
+            }
+            if (residual != nullptr) {
+                const uint2 rv = *(const uint2*)(residual + e);
+                s[0] += lo_bf(rv.x);
+                s[1] += hi_bf(rv.x);
+                s[2] += lo_bf(rv.y);
+                s[3] += hi_bf(rv.y);
+            }
+            uint2 h;
+            h.x = pack_bf(s[0], s[1]);
+            h.y = pack_bf(s[2], s[3]);
+            *(uint2*)(out + e) = h;
+            hv[j] = h;
+            const float f0 = lo_bf(h.x), f1 = hi_bf(h.x), f2 = lo_bf(h.y), f3 = hi_bf(h.y);
+            ss += f0 * f0;
+            ss += f1 * f1;
+            ss += f2 * f2;
+            ss += f3 * f3;
+        }
+    }
+    const float rs = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+        const int q = threadIdx.x + 256 * j;
+        if (q < nq) {
+            const uint2 w = *(const uint2*)(g + 4LL * q);
+            uint2 o;
+            o.x = pack_bf(lo_bf(hv[j].x) * rs * lo_bf(w.x), hi_bf(hv[j].x) * rs * hi_bf(w.x));
+            o.y = pack_bf(lo_bf(hv[j].y) * rs * lo_bf(w.y), hi_bf(hv[j].y) * rs * hi_bf(w.y));
+            *(uint2*)(nout + row0 + 4LL * q) = o;
+        }
+    }
+}
+
 // All-gather on one device: out = rank-order concatenation of t pieces of
 // `units` 16-byte vectors each (pieces and out 16-byte aligned).
 struct Pieces {
@@ -215,10 +295,10 @@ void rope_turns(double* rev, int d, float theta, hipStream_t st) {
 
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st) {
     if (rows <= 0 || n <= 0) return;
-    if (n <= 2048 * 2)
-        hipLaunchKernelGGL(rmsnorm_bf16_kernel<2>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
-    else if (n <= 2048 * 4)
+    if (n <= 1024 * 4)
         hipLaunchKernelGGL(rmsnorm_bf16_kernel<4>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
+    else if (n <= 1024 * 8)
+        hipLaunchKernelGGL(rmsnorm_bf16_kernel<8>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
     else
         hipLaunchKernelGGL(rmsnorm_bf16_kernel<0>, dim3(rows), dim3(256), 0, st, x, g, out, n, eps);
 }
@@ -266,6 +346,33 @@ void partial_reduce(const float* const* parts, int t, const void* residual, void
         }
     }
 #undef TP_RED
+}
+
+bool reduce_norm_bf16(const float* const* parts, int t, const bf16* residual, bf16* out, const bf16* g, bf16* nout,
+                      int rows, int n, float eps, hipStream_t st) {
+    if (n % 4 || n > 1024 * 8) return false;   // the caller takes the two separate launches
+    if (rows <= 0) return true;
+    Parts P;
+    for (int r = 0; r < 64; ++r) P.p[r] = r < t ? parts[r] : nullptr;
+    // the same group ownership as rmsnorm_bf16 (MAXJ 4 up to 4096 values, else 8)
+#define TP_RN(TT, MC) hipLaunchKernelGGL((reduce_norm_bf16_kernel<TT, MC>), dim3(rows), dim3(256), 0, st, P, t, residual, \
+                                         out, g, nout, n, eps)
+#define TP_RN_T(MC)                         \
+    switch (t) {                            \
+        case 1: TP_RN(1, MC); break;        \
+        case 2: TP_RN(2, MC); break;        \
+        case 4: TP_RN(4, MC); break;        \
+        case 8: TP_RN(8, MC); break;        \
+        default: TP_RN(0, MC); break;       \
+    }
+    if (n <= 1024 * 4) {
+        TP_RN_T(4)
+    } else {
+        TP_RN_T(8)
+    }
+#undef TP_RN_T
+#undef TP_RN
+    return true;
 }
 
 void rope_table(float* cos_t, float* sin_t, double* rev, int npos, int d, float theta, hipStream_t st) {

@@ -137,6 +137,11 @@ void attn_f32(const float* Q, const float* K, const float* V, float* O, int B, i
 // ---- shared ----
 void partial_reduce(const float* const* parts, int t, const void* residual, void* out, long long n,
                     int bf16_out, hipStream_t st);
+// partial_reduce of rows x n values (bf16 out) and rmsnorm_bf16 of the result
+// in one pass, bit-equal to the two launches; false (nothing launched) when
+// n is not a multiple of 4 or exceeds 8192
+bool reduce_norm_bf16(const float* const* parts, int t, const bf16* residual, bf16* out, const bf16* g, bf16* nout,
+                      int rows, int n, float eps, hipStream_t st);
 // cos/sin of p * theta_i for p < npos, i < d/2 ([npos, d/2] fp32), and rev[i] =
 // theta_i / (2 pi) in double (the rotation per position in turns)
 void rope_table(float* cos_t, float* sin_t, double* rev, int npos, int d, float theta, hipStream_t st);

@@ -844,6 +844,36 @@ int tp_partial_reduce(const float* const* partials, int t, const void* residual,
     return TP_OK;
 }
 
+int tp_shard_reduce_norm(tp_shard* s, int which, const float* const* partials, int t, const void* residual, void* out,
+                         void* norm_out, long long rows, void* stream) {
+    if (!s || (which != 1 && which != 2) || !partials || t < 1 || t > 64 || rows < 0) return TP_E_ARG;
+    if (rows == 0) return TP_OK;
+    if (!out || !norm_out || !aligned16(out) || !aligned16(norm_out) || (residual && !aligned16(residual)) ||
+        rows > INT32_MAX)
+        return TP_E_ARG;
+    for (int r = 0; r < t; ++r)
+        if (!partials[r] || !aligned16(partials[r])) return TP_E_ARG;
+    if (!s->loaded) return TP_E_STATE;
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf = s->o.dtype == TP_BF16;
+    const void* g = which == 1 ? s->g1 : s->g2;
+    KTimer kt(s, TP_K_REDUCE_NORM, st);
+    if (bf && s->o.rmsnorm &&
+        reduce_norm_bf16(partials, t, (const bf16*)residual, (bf16*)out, (const bf16*)g, (bf16*)norm_out, (int)rows,
+                         s->hidden, s->o.eps, st)) {
+        LAUNCH_CHECK("reduce_norm");
+        return TP_OK;
+    }
+    // other widths and the fp32 path: the reduce, then the norm (a copy without one)
+    partial_reduce(partials, t, residual, out, rows * s->hidden, bf, st);
+    LAUNCH_CHECK("partial_reduce");
+    if (!s->o.rmsnorm) {
+        HIP_TRY(hipMemcpyAsync(norm_out, out, (size_t)rows * s->hidden * s->esz, hipMemcpyDeviceToDevice, st));
+        return TP_OK;
+    }
+    return launch_norm(s, out, g, norm_out, rows, st);
+}
+
 int tp_partial_reduce_scatter(const float* const* partials, int t, int rank, const void* residual_rows,
                               void* out_rows, long long rows, int cols, int out_dtype, void* stream) {
     if (!partials || t < 1 || t > 64 || rows < 0 || cols <= 0 || cols % 8) return TP_E_ARG;

@@ -170,6 +170,69 @@ def test_partial_reduce(dtype, t, n):
     assert_close(to_np(out2), want2, "reduce no residual", dtype)
 
 
+@pytest.mark.parametrize("hidden,heads,kv,t,rows,dtype", [
+    (512, 4, 4, 2, 300, "bf16"),      # two 8-value chunks per thread (the norm's MAXC 2), ragged rows
+    (1536, 12, 3, 3, 77, "bf16"),     # a run-time rank count (the generic summation loop)
+    (4096, 32, 32, 1, 5, "bf16"),     # one rank: the reduce is a cast plus the residual
+    (8192, 64, 8, 8, 257, "bf16"),    # the 70B width, eight ranks (MAXC 4)
+    (9216, 72, 8, 2, 33, "bf16"),     # wider than the fused kernel: reduce, then norm
+    (512, 4, 4, 2, 40, "f32"),        # the fp32 path: reduce, then norm
+])
+def test_reduce_norm(hidden, heads, kv, t, rows, dtype):
+    """tp_shard_reduce_norm (the reduce with the next stage's RMSNorm) bit for
+    bit against tp_partial_reduce followed by tp_shard_norm, and against the
+    oracle: the reduce of the same partials, then the norm of the stored
+    result, with both gains."""
+    announce(f"reduce + RMSNorm hidden={hidden} t={t} rows={rows} {dtype}")
+    L = Layer(hidden, heads, kv, 512 * t, dtype=dtype, seq=0, gamma_noise=True, seed=41)
+    sh = L.shard(t, 0)
+    parts64 = [synth.draw_normal((rows, hidden), 42 + r, 3.0) for r in range(t)]
+    parts = [torch.from_numpy(p).cuda() for p in parts64]
+    res = synth.to_storage(synth.draw_normal((rows, hidden), 50), dtype)
+    for which, norm_ref in ((1, O.norm1), (2, O.norm2)):
+        out, nout = sh.reduce_norm(which, parts, residual=res.cuda())
+        h = partial_reduce(parts, residual=res.cuda())
+        n = sh.norm(which, h)
+        torch.cuda.synchronize()
+        assert torch.equal(out, h), "fused reduce differs from tp_partial_reduce"
+        assert torch.equal(nout, n), "fused norm differs from tp_shard_norm"
+        h_np = to_np(out)
+        assert_close(h_np, O.reduce([p.astype(np.float64) for p in parts64], res.float().numpy(), L.spec),
+                     f"reduce (which={which})", dtype)
+        assert_close(to_np(nout), norm_ref(h_np, L.W, L.spec), f"norm of the reduce (which={which})", dtype)
+    # no residual
+    out, nout = sh.reduce_norm(2, parts)
+    torch.cuda.synchronize()
+    assert_close(to_np(out), O.reduce([p.astype(np.float64) for p in parts64], np.zeros((rows, hidden)), L.spec),
+                 "reduce without a residual", dtype)
+
+
+def test_fused_norm_chain_equals_plain_chain():
+    """A layer chained through the fused reduce-norms (norm of x once, then
+    ATTN|PRENORM, reduce+norm2, MLP|PRENORM, reduce+norm1 of y) gives the
+    plain chain's partials, h and y bit for bit, and the norm of y that the
+    next layer's ATTN stage would compute."""
+    announce("layer through the fused reduce-norms vs the plain chain, t=2")
+    B, S, hid = 2, 96, 1024
+    L = Layer(hid, 8, 4, 2816, batch=B, seq=S, gamma_noise=True, seed=43)
+    shards = [L.shard(2, r) for r in range(2)]
+    x = L.dev["x"]
+    pa = [sh.prefill(ATTN, x) for sh in shards]
+    h = partial_reduce(pa, residual=x)
+    pm = [sh.prefill(MLP, h) for sh in shards]
+    y = partial_reduce(pm, residual=h)
+    n1 = shards[0].norm(1, x)
+    pa_f = [sh.prefill(ATTN | PRENORM, n1) for sh in shards]
+    h_f, n2_f = shards[0].reduce_norm(2, pa_f, residual=x)
+    pm_f = [sh.prefill(MLP | PRENORM, n2_f) for sh in shards]
+    y_f, n1_next = shards[0].reduce_norm(1, pm_f, residual=h_f)
+    n1_y = shards[0].norm(1, y)
+    torch.cuda.synchronize()
+    for a, b in zip(pa + pm, pa_f + pm_f):
+        assert torch.equal(a, b)
+    assert torch.equal(h, h_f) and torch.equal(y, y_f) and torch.equal(n1_y, n1_next)
+
+
 # ---------------------------------------------------------------- whole layers, small
 
 def test_tiny_f32_layer_two_ranks():
