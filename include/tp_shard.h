@@ -411,12 +411,22 @@ int tp_tune_set_gemm_split(int cfg0, int cfg1, int cols0);
  * TP_E_ARG outside 0..2. */
 int tp_tune_set_attn_groups(int kg);
 
-/* tp_tune_set_decode_chunk -- tuning hook for bf16 decode attention with
- * query groups (query heads > KV heads): 16, 32 or 64 cached positions per
- * chunk work-group (32 at least for head dim 64), or 0 to restore the choice
- * by grid size.  The workspace follows the chunk size on the next call.
- * Process-wide, not thread-safe; TP_E_ARG for other values. */
+/* tp_tune_set_decode_chunk -- tuning hook for bf16 decode attention: 16, 32
+ * or 64 cached positions per chunk work-group (32 at least for head dim 64;
+ * the split kernel for one query head per KV head always takes 64), or 0 to
+ * restore the choice by grid size.  The workspace follows the chunk size on
+ * the next call.  Process-wide, not thread-safe; TP_E_ARG for other values. */
 int tp_tune_set_decode_chunk(int ch);
+
+/* tp_tune_set_decode_attn -- tuning hook for bf16 decode attention:
+ * 1 runs chunk work-groups that cover all query heads of a KV head, then a
+ * merge launch; 2 runs one query head per chunk work-group and merges in
+ * the same launch (the last chunk work-group of each sequence and head,
+ * found with a device-scope release and an atomic count, merges the head's
+ * chunks); 3 (also what 0, the default, restores) runs one query head per
+ * chunk work-group, then a merge launch.  Same result up to rounding order.
+ * Process-wide, not thread-safe; TP_E_ARG outside 0..3. */
+int tp_tune_set_decode_attn(int mode);
 
 void tp_shard_destroy(tp_shard *s);
 void tp_kv_destroy(tp_kv *kv);

@@ -421,6 +421,12 @@ def set_decode_chunk(ch: int) -> None:
     N.check(N.lib().tp_tune_set_decode_chunk(int(ch)), "tp_tune_set_decode_chunk")
 
 
+def set_decode_attn(mode: int) -> None:
+    """Tuning hook: decode attention merge (0 = automatic, 1 = a second launch,
+    2 = in the same launch)."""
+    N.check(N.lib().tp_tune_set_decode_attn(int(mode)), "tp_tune_set_decode_attn")
+
+
 def set_attn_groups(kg: int) -> None:
     """Tuning hook: prefill attention key groups (0 = automatic, 1 or 2)."""
     N.check(N.lib().tp_tune_set_attn_groups(int(kg)), "tp_tune_set_attn_groups")

@@ -68,6 +68,7 @@ SIGNATURES = [
                                     C.POINTER(C.c_int)]),
     ("tp_tune_set_gemm_split", C.c_int, [C.c_int, C.c_int, C.c_int]),
     ("tp_tune_set_decode_chunk", C.c_int, [C.c_int]),
+    ("tp_tune_set_decode_attn", C.c_int, [C.c_int]),
     ("tp_shard_timing", C.c_int, [C.c_void_p, C.c_int]),
     ("tp_shard_timing_read", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),
     ("tp_shard_destroy", None, [C.c_void_p]),

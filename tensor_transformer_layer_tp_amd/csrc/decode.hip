@@ -614,6 +614,189 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
                       O + ((long long)b * hl + head) * D, lds);
 }
 
+// Merge with every load in one round: thread (dim, part) of a (head,
+// sequence) work-group of D * P threads owns the chunks c = part + P i
+// (at most MAXI of them) and loads their maxima, sums and its dim's
+// outputs at once; a block maximum gives the reference M, then each thread
+// weights its chunks by exp2(m_c - M) and the parts meet in LDS.
+template <int D, int P, int MAXI>
+__global__ __launch_bounds__(D * P) void attn_decode_merge(const float* __restrict__ scr, bf16* __restrict__ O, int hl,
+                                                          int stride, const int* __restrict__ len_dev, int ld_seq,
+                                                          int CH) {
+    constexpr int NT = D * P, NW = NT / 64;
+    __shared__ float sred[NW];
+    __shared__ float spart[P][D];
+    __shared__ float sl[P];
+    const int head = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int dim = tid % D, part = tid / D;
+    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by the chunk kernel
+    const float* st = scr + ((long long)b * hl + head) * stride * (D + 2);
+    float mv[MAXI], lv[MAXI], ov[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int c = min(part + P * i, nchunks - 1);   // clamped: every load issued, in bounds
+        const float* r = st + (long long)c * (D + 2);
+        mv[i] = r[D];
+        lv[i] = r[D + 1];
+        ov[i] = r[dim];
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i)
+        if (part + P * i < nchunks) m = fmaxf(m, mv[i]);
+    m = wave_max_dpp(m);
+    if (lane == 0) sred[wave] = m;
+    __syncthreads();
+    float M = sred[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sred[w]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i)
+        if (part + P * i < nchunks) {
+            const float wgt = __builtin_amdgcn_exp2f(mv[i] - M);
+            acc += wgt * ov[i];
+            lsum += wgt * lv[i];
+        }
+    spart[part][dim] = acc;
+    if (dim == 0) sl[part] = lsum;
+    __syncthreads();
+    if (part == 0) {
+        float o = 0.f, L = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            o += spart[p][dim];
+            L += sl[p];
+        }
+        O[((long long)b * hl + head) * D + dim] = f2bf(o / L);
+    }
+}
+
+// Split-KV decode attention with the merge in the same launch.  Work-group
+// (chunk, query head, sequence) attends one query head (GQA: its KV head is
+// head / G, so the G heads of a KV head read the same chunk; the grid's
+// chunk count is a multiple of 8, which puts them on one XCD and its L2)
+// over CH cached positions: thread (key, segment) dots SD = D / SEG dims of
+// its key with the query, the SEG threads of a key sum by shuffles, wave 0
+// takes the chunk's softmax pieces, thread (8-dim chunk, key group) sums
+// P V over its keys and the groups meet in LDS.  The chunk's record (D
+// unnormalised outputs, max, sum) is published with a device-scope release
+// and counted on the (sequence, head)'s counter; the work-group that brings
+// the count to the number of chunks holding positions merges the head's
+// records (device-scope acquire first) and resets the counter for the next
+// call.  Chunks at or past the device-resident cache length exit at once,
+// uncounted.
+template <int D, int CH, bool MERGE>
+__global__ __launch_bounds__(256) void attn_decode_fused(const bf16* __restrict__ q, const bf16* __restrict__ K,
+                                                         const bf16* __restrict__ V, float* __restrict__ scr,
+                                                         int* __restrict__ cnt, bf16* __restrict__ O, int hl, int kvl,
+                                                         const int* __restrict__ len_dev, int ld_seq,
+                                                         float scale_log2, const int* __restrict__ table, int bsz,
+                                                         int max_blocks) {
+    constexpr int SEG = 256 / CH, SD = D / SEG;          // score threads per key, dims per score thread
+    constexpr int DC = D / 8, KG = 256 / DC, KPG = CH / KG;  // P V thread = (8-dim chunk, key group)
+    static_assert(SD % 8 == 0 && SEG <= 64 && KPG >= 1, "chunk shape");
+    __shared__ float sq[D];
+    __shared__ float sp[CH];
+    __shared__ float pg[KG][D];
+    __shared__ float mrg[merge_lds_floats<D, 256>()];
+    __shared__ int last;
+    const int G = hl / kvl;
+    const int chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+    const int kvh = head / G;
+    const int nch = gridDim.x;   // record stride
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int k0 = chunk * CH;
+    const int key = tid / SEG, seg = tid % SEG;
+    const int dc = tid % DC, kg = tid / DC;
+    // every load before the cache length arrives: rows clamped to the capacity
+    u16x8 kraw[SD / 8], vraw[KPG], qraw;
+    {
+        const bf16* krow = K + kv_row(b, kvh, min(k0 + key, ld_seq - 1), kvl, ld_seq, D, table, bsz, max_blocks);
+#pragma unroll
+        for (int c = 0; c < SD / 8; ++c) kraw[c] = *(const u16x8*)(krow + seg * SD + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < KPG; ++i) {
+        const int gk = min(k0 + kg * KPG + i, ld_seq - 1);
+        vraw[i] = *(const u16x8*)(V + kv_row(b, kvh, gk, kvl, ld_seq, D, table, bsz, max_blocks) + dc * 8);
+    }
+    qraw = *(const u16x8*)(q + ((long long)b * hl + head) * D + 8 * min(tid, DC - 1));
+    const int len = min(*len_dev + 1, ld_seq);
+    if (k0 >= len) return;   // no positions in this chunk (uniform per work-group)
+    if (tid < DC)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq[8 * tid + e] = bfbits2f(qraw[e]);
+    __syncthreads();
+    {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < SD / 8; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += bfbits2f(kraw[c][e]) * sq[seg * SD + c * 8 + e];
+#pragma unroll
+        for (int off = 1; off < SEG; off <<= 1) s += __shfl_xor(s, off, 64);
+        if (seg == 0) sp[key] = k0 + key < len ? s * scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    float m = 0.f, l = 0.f;   // the chunk's max and sum (wave 0)
+    if (wave == 0) {
+        const float sv = lane < CH ? sp[lane] : -INFINITY;
+        m = wave_max_dpp(sv);
+        const float p = lane < CH ? __builtin_amdgcn_exp2f(sv - m) : 0.f;
+        l = wave_sum_dpp(p);
+        if (lane < CH) sp[lane] = p;   // zero past the length (exp2 of -inf)
+    }
+    __syncthreads();
+    {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < KPG; ++i) {
+            const int kk = kg * KPG + i;
+            const float p = sp[kk];
+            const bool ok = k0 + kk < len;   // rows past the length may hold stale values
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += p * (ok ? bfbits2f(vraw[i][e]) : 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pg[kg][dc * 8 + e] = o[e];
+    }
+    __syncthreads();
+    // wave 0 stores the record (D / 64 outputs per lane, then max and sum)
+    float* rec = scr + (((long long)b * hl + head) * nch + chunk) * (D + 2);
+    if (wave == 0) {
+#pragma unroll
+        for (int h = 0; h < D / 64; ++h) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < KG; ++k) a += pg[k][64 * h + lane];
+            rec[64 * h + lane] = a;
+        }
+        if (lane == 0) {
+            rec[D] = m;
+            rec[D + 1] = l;
+        }
+        // release (an L2 write-back) by the one wave that stored the record, so
+        // that it is visible device-wide before it is counted; no acquire here:
+        // an invalidation would drop the other work-groups' cached K/V lines
+        if constexpr (MERGE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
+    if constexpr (!MERGE) return;   // a merge launch follows
+    __syncthreads();
+    const int nact = (len + CH - 1) / CH;   // chunks holding positions
+    int* c = cnt + (long long)b * hl + head;
+    if (tid == 0) last = atomicAdd(c, 1) == nact - 1;
+    __syncthreads();
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // every other chunk's record
+    merge_head<D, 256>(scr + ((long long)b * hl + head) * nch * (D + 2), nact, O + ((long long)b * hl + head) * D,
+                       mrg);
+    if (tid == 0) *c = 0;   // the count starts from zero on the next call
+}
+
 // ---------------------------------------------------------------------------
 // Skinny GEMM for small decode batches (2..64 sequences), split over K.
 //
@@ -817,12 +1000,14 @@ void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part,
     }
 }
 
-// Positions per chunk: 64; query groups take fewer when 64 leaves fewer
-// than 128 chunk work-groups (few KV heads and sequences), down to 16 (32
-// for d = 64).
-int g_decode_chunk = 0;   // 0: automatic; 16, 32, 64: forced for query groups
+// Split kernels (the merge a second launch): positions per chunk 64; query
+// groups take fewer when 64 leaves fewer than 128 chunk work-groups (few KV
+// heads and sequences), down to 16 (32 for d = 64).
+int g_decode_chunk = 0;   // 0: automatic; 16, 32, 64: forced
+int g_decode_mode = 0;    // 0: automatic; 1: split kernels + merge launch; 2: fused merge;
+                          // 3: one-head chunk kernel + merge launch
 
-int decode_chunk(int B, int hl, int kvl, int cap, int d) {
+int split_chunk(int B, int hl, int kvl, int cap, int d) {
     int ch = 64;
     if (hl == kvl) return ch;
     const int lo = d == 128 ? 16 : 32;
@@ -831,21 +1016,56 @@ int decode_chunk(int B, int hl, int kvl, int cap, int d) {
     return ch;
 }
 
+struct DecodeAttnPlan {
+    bool fused;     // one query head per work-group (attn_decode_fused)
+    bool merge_in;  // ... with the merge in the same launch
+    int ch;         // positions per chunk
+    int nch;        // chunk work-groups per (sequence, head) = record stride
+};
+
+// The fused kernel (one query head per work-group) takes 64 positions per
+// chunk, halved while the grid would have fewer than 256 work-groups; it is
+// used while a head has at most 256 chunks, whose records its last
+// work-group merges, and while the workspace's counters cover batch x heads.
+DecodeAttnPlan decode_attn_plan(int B, int hl, int kvl, int cap, int d) {
+    const int lo = d == 128 ? 16 : 32;
+    int ch = 64;
+    if (g_decode_chunk)
+        ch = std::max(g_decode_chunk, lo);
+    else
+        while (ch > lo && (long long)((cap + ch - 1) / ch) * hl * B < 256) ch >>= 1;
+    const int n = (cap + ch - 1) / ch;
+    const bool fits = (long long)B * hl <= kDecodeCounters;
+    if (g_decode_mode == 2 && fits) return {true, true, ch, (n + 7) / 8 * 8};
+    if (g_decode_mode == 0 || g_decode_mode == 3) return {true, false, ch, (n + 7) / 8 * 8};
+    const int chs = split_chunk(B, hl, kvl, cap, d);
+    return {false, false, chs, (cap + chs - 1) / chs};
+}
+
 void set_decode_chunk(int ch) { g_decode_chunk = ch; }
+void set_decode_attn_mode(int mode) { g_decode_mode = mode; }
 
 size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d) {
-    const int ch = decode_chunk(B, hl, kvl, cap, d);
-    const int nchunks = (cap + ch - 1) / ch;
-    return (size_t)B * hl * nchunks * (d + 2) * sizeof(float);
+    const DecodeAttnPlan p = decode_attn_plan(B, hl, kvl, cap, d);
+    return (size_t)B * hl * p.nch * (d + 2) * sizeof(float);
 }
 
 template <int D, int CHT>
-void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
-                        int kvl, const int* len_dev, int ld_seq, const int* table, int bsz, int mb, hipStream_t st) {
-    const int nchunks = (ld_seq + CHT - 1) / CHT;
+void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int* counters, int B,
+                        int hl, int kvl, const int* len_dev, int ld_seq, const int* table, int bsz, int mb,
+                        const DecodeAttnPlan& p, hipStream_t st) {
+    const int nchunks = p.nch;
     const int G = hl / kvl;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    if (G == 1) {
+    if (p.fused && p.merge_in) {
+        hipLaunchKernelGGL((attn_decode_fused<D, CHT, true>), dim3(nchunks, hl, B), dim3(256), 0, st, q, K, V,
+                           scratch, counters, O, hl, kvl, len_dev, ld_seq, scale_log2, table, bsz, mb);
+        return;
+    }
+    if (p.fused) {
+        hipLaunchKernelGGL((attn_decode_fused<D, CHT, false>), dim3(nchunks, hl, B), dim3(256), 0, st, q, K, V,
+                           scratch, counters, O, hl, kvl, len_dev, ld_seq, scale_log2, table, bsz, mb);
+    } else if (G == 1) {
         // LDS: q [D], scores [64], per-head partial sums [256/(D/8)][D]
         const size_t lds = ((size_t)D + 64 + (size_t)(256 / (D / 8)) * D) * sizeof(float);
         hipLaunchKernelGGL(attn_decode_chunk_mha<D>, dim3(nchunks, kvl, B), dim3(256), lds, st, q, K, V, scratch, hl,
@@ -856,20 +1076,27 @@ void launch_decode_attn(const bf16* q, const bf16* K, const bf16* V, bf16* O, fl
         hipLaunchKernelGGL((attn_decode_chunk<D, CHT>), dim3(nchunks, kvl, B), dim3(256), lds, st, q, K, V, scratch,
                            hl, kvl, len_dev, ld_seq, scale_log2, table, bsz, mb);
     }
-    // long chunk lists are summed by more threads
-    if (nchunks > 32)
-        hipLaunchKernelGGL((attn_decode_combine<D, 512>), dim3(hl, B), dim3(512), 0, st, scratch, O, hl, nchunks,
+    // up to 128 chunks: every load in one round (4 or 8 parts of up to 16
+    // chunks per thread); longer chunk lists: the tiled merge
+    if (nchunks <= 64)
+        hipLaunchKernelGGL((attn_decode_merge<D, 4, 16>), dim3(hl, B), dim3(D * 4), 0, st, scratch, O, hl, nchunks,
+                           len_dev, ld_seq, CHT);
+    else if (nchunks <= 128)
+        hipLaunchKernelGGL((attn_decode_merge<D, 8, 16>), dim3(hl, B), dim3(D * 8), 0, st, scratch, O, hl, nchunks,
                            len_dev, ld_seq, CHT);
     else
-        hipLaunchKernelGGL((attn_decode_combine<D, D>), dim3(hl, B), dim3(D), 0, st, scratch, O, hl, nchunks, len_dev,
-                           ld_seq, CHT);
+        hipLaunchKernelGGL((attn_decode_combine<D, 512>), dim3(hl, B), dim3(512), 0, st, scratch, O, hl, nchunks,
+                           len_dev, ld_seq, CHT);
 }
 
-void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B, int hl,
-                      int kvl, const int* len_dev, int ld_seq, int d, const int* table, int bsz, int mb,
+void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int* counters, int B,
+                      int hl, int kvl, const int* len_dev, int ld_seq, int d, const int* table, int bsz, int mb,
                       hipStream_t st) {
-    const int ch = decode_chunk(B, hl, kvl, ld_seq, d);
-#define TP_DA(DD, CC) launch_decode_attn<DD, CC>(q, K, V, O, scratch, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, st)
+    const DecodeAttnPlan p = decode_attn_plan(B, hl, kvl, ld_seq, d);
+    // the G = 1 split kernel is built for 64-position chunks
+    const int ch = !p.fused && hl == kvl ? 64 : p.ch;
+#define TP_DA(DD, CC) \
+    launch_decode_attn<DD, CC>(q, K, V, O, scratch, counters, B, hl, kvl, len_dev, ld_seq, table, bsz, mb, p, st)
     if (d == 128) {
         if (ch == 64) TP_DA(128, 64);
         else if (ch == 32) TP_DA(128, 32);

@@ -287,7 +287,16 @@ __global__ void rope_turns_kernel(double* rev, int d, double theta) {
     if (i < d / 2) rev[i] = pow(theta, -2.0 * i / (double)d) * 0.15915494309189535;
 }
 
+__global__ void zero_ints_kernel(int* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
 }  // namespace
+
+void zero_ints(int* p, int n, hipStream_t st) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(std::min((n + 255) / 256, 1024)), dim3(256), 0, st, p, n);
+}
 
 void rope_turns(double* rev, int d, float theta, hipStream_t st) {
     hipLaunchKernelGGL(rope_turns_kernel, dim3(1), dim3(64), 0, st, rev, d, (double)theta);

@@ -113,14 +113,18 @@ void quant_rows_e4m3(const bf16* W, int N, int K, uint8_t* Q, float* scale, hipS
 // decode attention over positions [0, *len_dev + 1) (capped at ld_seq); the
 // grid and the scratch are sized for ld_seq positions so that one launch
 // stays valid while the device length grows (graph replay)
-void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int B,
+// `counters` (kDecodeCounters ints) must be zero before the first call; each
+// call leaves them zero again
+constexpr int kDecodeCounters = 16384;
+void attn_decode_bf16(const bf16* q, const bf16* K, const bf16* V, bf16* O, float* scratch, int* counters, int B,
                       int hl, int kvl, const int* len_dev, int ld_seq, int d, const int* table, int bsz,
                       int max_blocks, hipStream_t st);
 // copy K and V [B, kvl, S, d] (contiguous) into a paged pool at positions 0..S-1
 void kv_to_pages(const bf16* k, const bf16* v, bf16* kpool, bf16* vpool, int B, int kvl, int S, int d,
                  const int* table, int bsz, int max_blocks, hipStream_t st);
 size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d);
-void set_decode_chunk(int ch);   // decode attention chunk for query groups: 0 automatic, 16/32/64 forced
+void set_decode_chunk(int ch);   // decode attention positions per chunk: 0 automatic, 16/32/64 forced
+void set_decode_attn_mode(int mode);   // 0 automatic, 1 split kernels + merge launch, 2 fused merge
 // small decode batches (2..64): split-K MFMA projection + epilogue pass; part
 // is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
 void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,
@@ -145,6 +149,8 @@ bool reduce_norm_bf16(const float* const* parts, int t, const bf16* residual, bf
 // cos/sin of p * theta_i for p < npos, i < d/2 ([npos, d/2] fp32), and rev[i] =
 // theta_i / (2 pi) in double (the rotation per position in turns)
 void rope_table(float* cos_t, float* sin_t, double* rev, int npos, int d, float theta, hipStream_t st);
+// p[0, n) = 0 (a fill kernel: callers may be under graph capture)
+void zero_ints(int* p, int n, hipStream_t st);
 // rev[i] = theta_i / (2 pi) alone (d <= 128): what the bf16 kernels rotate with
 void rope_turns(double* rev, int d, float theta, hipStream_t st);
 // out = rank-order concatenation of t pieces of piece_bytes each (multiple of 16, 16-byte aligned)

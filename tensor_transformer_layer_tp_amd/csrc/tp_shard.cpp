@@ -108,6 +108,12 @@ int scratch_setup(int device) {
     void* p = nullptr;
     const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    // the array's workspace starts with the decode merge counters: zero them once
+    zero_ints((int*)p, kDecodeCounters, nullptr);
+    const hipError_t z = hipGetLastError();
+    if (z != hipSuccess) return hip_fail(z, "zero counters");
+    const hipError_t sy = hipDeviceSynchronize();
+    if (sy != hipSuccess) return hip_fail(sy, "hipDeviceSynchronize");
     g_scratch_dev[device] = (char*)p;
     return TP_OK;
 }
@@ -118,7 +124,11 @@ char* scratch_of(int device) {
     return g_scratch_dev[device];
 }
 
-int ensure_ws(tp_shard* s, size_t bytes) {
+// The workspace starts with the decode attention's merge counters, which
+// must be zero before a call (every call leaves them zero again).
+constexpr size_t kCounterBytes = (size_t)kDecodeCounters * sizeof(int);
+
+int ensure_ws(tp_shard* s, size_t bytes, hipStream_t st) {
     if (bytes <= s->ws_bytes) return TP_OK;
     if (s->ws) {
         hipError_t e = hipFree(s->ws);  // waits for work that may still use it
@@ -134,6 +144,8 @@ int ensure_ws(tp_shard* s, size_t bytes) {
         return TP_E_NOMEM;
     }
     s->ws_bytes = b;
+    zero_ints((int*)s->ws, kDecodeCounters, st);
+    LAUNCH_CHECK("zero counters");
     return TP_OK;
 }
 
@@ -166,14 +178,15 @@ int ensure_rope(tp_shard* s, int npos, hipStream_t st) {
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout for T tokens: n | q | o | k,v (when no cache) | act | decode scratch
+// Workspace layout for T tokens: merge counters | n | q | o | k,v (when no
+// cache) | act | decode scratch
 struct Layout {
     size_t n, q, o, kv, act, scr, total;
 };
 Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) {
     Layout L;
     size_t e = s->esz;
-    L.n = 0;
+    L.n = al(kCounterBytes);
     L.q = L.n + al((size_t)T * s->hidden * e);
     L.o = L.q + al((size_t)T * s->hl * s->d * e);
     L.kv = L.o + al((size_t)T * s->hl * s->d * e);
@@ -478,7 +491,9 @@ int tp_shard_fp8_view(tp_shard* s, int which, void** codes, float** scales, int*
 int tp_shard_reserve(tp_shard* s, long long max_tokens) {
     if (!s || max_tokens <= 0) return TP_E_ARG;
     Layout L = layout(s, max_tokens, 0, 0);
-    return ensure_ws(s, L.total);
+    TRY(ensure_ws(s, L.total, nullptr));
+    HIP_TRY(hipDeviceSynchronize());   // the counters are zero before any stream uses the workspace
+    return TP_OK;
 }
 
 int tp_kv_create(const tp_shard* s, int batch, int max_seq, tp_kv** out) {
@@ -607,7 +622,7 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
     }
     if (s->o.dtype == TP_F32 && stage == TP_STAGE_ATTN && seq > 16000) return TP_E_ARG;
     Layout L = layout(s, T, 0, 0);
-    TRY(ensure_ws(s, L.total));
+    TRY(ensure_ws(s, L.total, st));
     char* ws = s->ws;
     s->dbg_base = ws;
     s->off_n = L.n;
@@ -723,7 +738,7 @@ int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, fl
         ws = scratch_of(s->device);
         if (ws == nullptr) return TP_E_STATE;
     } else {
-        TRY(ensure_ws(s, lay.total));
+        TRY(ensure_ws(s, lay.total, st));
         ws = s->ws;
     }
     s->dbg_base = ws;
@@ -756,7 +771,7 @@ int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, fl
             KTimer kt(s, TP_K_ATTN_DECODE, st);
             if (bf)
                 attn_decode_bf16((const bf16*)qbuf, (const bf16*)kv->k, (const bf16*)kv->v, (bf16*)(ws + lay.o),
-                                 (float*)(ws + lay.scr), batch, s->hl, s->kvl, kv->dlen, kv->max_seq, s->d, kv->table,
+                                 (float*)(ws + lay.scr), (int*)ws, batch, s->hl, s->kvl, kv->dlen, kv->max_seq, s->d, kv->table,
                                  kv->block_size, kv->max_blocks, st);
             else
                 attn_f32((const float*)qbuf, (const float*)kv->k, (const float*)kv->v, (float*)(ws + lay.o), batch,
@@ -996,6 +1011,12 @@ int tp_tune_set_gemm_split(int cfg0, int cfg1, int cols0) {
 int tp_tune_set_decode_chunk(int ch) {
     if (ch != 0 && ch != 16 && ch != 32 && ch != 64) return TP_E_ARG;
     set_decode_chunk(ch);
+    return TP_OK;
+}
+
+int tp_tune_set_decode_attn(int mode) {
+    if (mode < 0 || mode > 3) return TP_E_ARG;
+    set_decode_attn_mode(mode);
     return TP_OK;
 }
 

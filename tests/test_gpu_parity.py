@@ -381,13 +381,18 @@ def test_decode_gemv_shapes(hidden, heads, kv, ffn, tp, B):
     assert_close(to_np(pm), refm["partial"][:, 0], "decode mlp partial", "bf16")
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("ch", [16, 32, 64])
-@pytest.mark.parametrize("hidden,heads,kv,B,S", [(2048, 32, 8, 3, 200), (1024, 16, 2, 2, 137)])
-def test_decode_chunk_sizes(ch, hidden, heads, kv, B, S):
-    """Query-group decode attention with each chunk length forced (head dims
-    64 and 128; ragged last chunk), against the oracle."""
-    from tensor_transformer_layer_tp_amd import set_decode_chunk
-    announce(f"decode chunk {ch}: hidden={hidden} heads={heads}/{kv} B={B} S={S}")
+@pytest.mark.parametrize("hidden,heads,kv,B,S", [(2048, 32, 8, 3, 200), (1024, 16, 2, 2, 137), (1024, 8, 8, 2, 150)])
+def test_decode_chunk_sizes(mode, ch, hidden, heads, kv, B, S):
+    """Decode attention with each chunk length forced (head dims 64 and 128;
+    query groups of 4 and 8 and one query head per KV head; ragged last
+    chunk), with each attention form: one query head per chunk work-group
+    and a merge launch (mode 0, the default), the KV-head chunk kernels and a
+    merge launch (mode 1), the merge in the same launch (mode 2); against
+    the oracle: the attention output o and the partial."""
+    from tensor_transformer_layer_tp_amd import set_decode_attn, set_decode_chunk
+    announce(f"decode attention mode {mode} chunk {ch}: hidden={hidden} heads={heads}/{kv} B={B} S={S}")
     tp, r = 2, 1
     L = Layer(hidden, heads, kv, 2 * hidden, batch=B, seq=S + 1, gamma_noise=True, seed=31)
     sh = L.shard(tp, r)
@@ -395,17 +400,22 @@ def test_decode_chunk_sizes(ch, hidden, heads, kv, B, S):
     sh.prefill(ATTN, L.dev["x"][:, :S].contiguous(), kvc)
     try:
         set_decode_chunk(ch)
+        set_decode_attn(mode)
         p = sh.decode(ATTN, L.dev["x"][:, S].contiguous(), kvc, out=nan_like((B, hidden)))
+        o = sh.debug_tensor("o", (B, heads // tp * (hidden // heads)))
         torch.cuda.synchronize()
     finally:
         set_decode_chunk(0)
+        set_decode_attn(0)
     pre = O.attn_stage(L.exact["x"][:, :S], L.W, L.spec, tp, r)
     ref = O.decode_attn_stage(L.exact["x"][:, S], pre["k"], pre["v"], L.W, L.spec, tp, r)
-    assert_close(to_np(p), ref["partial"], f"decode attn partial (chunk {ch})", "bf16")
+    assert_close(to_np(o), ref["o"].reshape(B, -1), f"decode o (mode {mode}, chunk {ch})", "bf16")
+    assert_close(to_np(p), ref["partial"], f"decode attn partial (mode {mode}, chunk {ch})", "bf16")
 
 
+@pytest.mark.parametrize("mode", [0, 2])
 @pytest.mark.parametrize("L_len", [1023, 70000])
-def test_decode_long_cache(L_len):
+def test_decode_long_cache(L_len, mode):
     """Decode against a cache written directly (seeded bf16 values), long
     enough that the split-KV merge covers more than 1024 chunks of 64."""
     announce(f"bf16 decode over a written cache of {L_len} positions")
@@ -418,8 +428,13 @@ def test_decode_long_cache(L_len):
     vc = synth.to_storage(synth.draw_normal(shape, 25), "bf16")
     kvc.write(kc.cuda(), vc.cuda())
     kvc.length = L_len
-    p = sh.decode(ATTN, L.dev["x"][:, 0].contiguous(), kvc, out=nan_like((B, hidden)))
-    torch.cuda.synchronize()
+    from tensor_transformer_layer_tp_amd import set_decode_attn
+    try:
+        set_decode_attn(mode)   # 70000 positions: automatic = merge launch; forced: the in-launch merge
+        p = sh.decode(ATTN, L.dev["x"][:, 0].contiguous(), kvc, out=nan_like((B, hidden)))
+        torch.cuda.synchronize()
+    finally:
+        set_decode_attn(0)
     kn = kc.float().numpy()[:, :, :L_len]
     vn = vc.float().numpy()[:, :, :L_len]
     ref = O.decode_attn_stage(L.exact["x"][:, 0], kn, vn, L.W, L.spec, 1, 0)
