@@ -137,7 +137,7 @@ def decode_bytes(hidden, heads, kv_heads, ffn, t, B, L, fp8=False):
 def source_sha(name):
     """Hash of a kernel source together with the headers it includes."""
     h = hashlib.sha256()
-    for f in (name, "common.h", "kernels.h"):
+    for f in (name, "common.h", "kernels.h", "types.h"):
         h.update(open(os.path.join(ROOT, "tensor_transformer_layer_tp_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -17,7 +17,7 @@
 // match the accumulator's register order, so each A-operand fragment is one
 // 16-byte LDS read.  Grouped-query attention maps query head j to KV head
 // j / (Hl / Hkvl).
-#include "kernels.h"
+#include "common.h"
 
 namespace tp {
 

@@ -1,18 +1,13 @@
-// Shared device/host helpers for the gfx950 shard kernels.
+// Device helpers of the gfx950 shard kernels (included by the .hip sources;
+// host code includes kernels.h alone).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace tp {
+#include "kernels.h"
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+namespace tp {
 
 // fp32 -> bf16, round to nearest even: gfx950 converts in hardware
 // (v_cvt_pk_bf16_f32, RNE under the default rounding mode, NaN kept NaN).
@@ -67,6 +62,46 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(i, 32)), __int_as_float(__builtin_amdgcn_readlane(i, 48))));
 }
 
-inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+// Address of cache row (sequence b, kv head h, position p) in a contiguous
+// cache [B, kvl, ld_seq, d] or, with a block table, in a paged pool.
+// The paged form is split in two steps (table read, then the row address)
+// so that callers can issue the table reads of several rows together.  The
+// block size is a power of two (checked when a paged cache is created).
+__device__ __forceinline__ int kv_block(int b, int p, const int* table, int bsz, int max_blocks) {
+    const int blk = p >> (31 - __builtin_clz(bsz));
+    return table[(long long)b * max_blocks + min(blk, max_blocks - 1)];   // clamped: in bounds
+}
+__device__ __forceinline__ long long kv_row_in_block(int blk, int h, int p, int kvl, int bsz, int d) {
+    return (((long long)blk * kvl + h) * bsz + (p & (bsz - 1))) * d;
+}
+__device__ __forceinline__ long long kv_row(int b, int h, int p, int kvl, int ld_seq, int d, const int* table,
+                                            int bsz, int max_blocks) {
+    if (table == nullptr) return (((long long)b * kvl + h) * ld_seq + p) * d;
+    return kv_row_in_block(kv_block(b, p, table, bsz, max_blocks), h, p, kvl, bsz, d);
+}
+
+__device__ __forceinline__ void apply_len_update(const LenUpdate& u) {
+    if (u.ptr == nullptr) return;
+    if (u.value >= 0) {
+        *u.ptr = u.value;
+        if (u.overflow != nullptr) *u.overflow = 0;
+    } else {
+        const int v = *u.ptr;
+        if (v < u.cap) *u.ptr = v + 1;
+        else if (u.overflow != nullptr) *u.overflow = 1;
+    }
+}
+
+// Packed column layout shared by the projection kernels: for Q/K/V heads and
+// for the gate/up pair, every 64-row group of the packed weight holds two
+// 32-row halves that belong together: (dims i, i + d/2) of one head for the
+// rotary embedding, or (gate j, up j) for SwiGLU.  Packed row p of a head's
+// block maps to head dim:  g = p / 64, w = p % 64,
+//   dim = 32 g + w            (w < 32)
+//   dim = d/2 + 32 g + w - 32 (w >= 32).
+__host__ __device__ inline int packed_to_dim(int p, int d) {
+    int g = p >> 6, w = p & 63;
+    return w < 32 ? 32 * g + w : (d >> 1) + 32 * g + (w - 32);
+}
 
 }  // namespace tp

@@ -6,7 +6,7 @@
 // Slower"): at batch 1..8 every projection reads its weight slice once and
 // does ~1 FLOP per byte, so these kernels are organised around streaming
 // the weights from HBM with 16-byte coalesced loads, not around MFMA.
-#include "kernels.h"
+#include "common.h"
 
 #include <algorithm>
 

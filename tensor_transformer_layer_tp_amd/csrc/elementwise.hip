@@ -1,5 +1,5 @@
 // Bandwidth-bound helpers: RMSNorm, the rank-partial reduce, the RoPE table.
-#include "kernels.h"
+#include "common.h"
 
 namespace tp {
 

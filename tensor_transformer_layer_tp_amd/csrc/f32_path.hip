@@ -4,7 +4,7 @@
 // the same packed weight layout, causal attention with grouped KV heads --
 // on plain FMA arithmetic.  These kernels serve correctness at fp32; the
 // bf16 MFMA kernels are the throughput path.
-#include "kernels.h"
+#include "common.h"
 
 namespace tp {
 

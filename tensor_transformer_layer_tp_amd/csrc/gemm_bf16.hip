@@ -26,7 +26,7 @@
 // fragment reads of 16 consecutive rows hit distinct bank groups.  Work-groups
 // are remapped so that each XCD (hardware places work-group i on XCD i % 8)
 // receives a contiguous, L2-friendly block of tiles.
-#include "kernels.h"
+#include "common.h"
 
 #include <stdint.h>
 

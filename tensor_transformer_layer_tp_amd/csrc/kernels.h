@@ -1,7 +1,9 @@
-// Internal launch API of the shard kernels (not part of the C ABI).
+// Internal launch API of the shard kernels (not part of the C ABI): the
+// epilogue and cache descriptors and the launchers.  Host-safe: the host
+// runtime includes it alone; device helpers live in common.h.
 #pragma once
 
-#include "common.h"
+#include "types.h"
 
 namespace tp {
 
@@ -34,24 +36,6 @@ struct QKVDest {
     int bsz, max_blocks;
 };
 
-// Address of cache row (sequence b, kv head h, position p) in a contiguous
-// cache [B, kvl, ld_seq, d] or, with a block table, in a paged pool.
-// The paged form is split in two steps (table read, then the row address)
-// so that callers can issue the table reads of several rows together.  The
-// block size is a power of two (checked when a paged cache is created).
-__device__ __forceinline__ int kv_block(int b, int p, const int* table, int bsz, int max_blocks) {
-    const int blk = p >> (31 - __builtin_clz(bsz));
-    return table[(long long)b * max_blocks + min(blk, max_blocks - 1)];   // clamped: in bounds
-}
-__device__ __forceinline__ long long kv_row_in_block(int blk, int h, int p, int kvl, int bsz, int d) {
-    return (((long long)blk * kvl + h) * bsz + (p & (bsz - 1))) * d;
-}
-__device__ __forceinline__ long long kv_row(int b, int h, int p, int kvl, int ld_seq, int d, const int* table,
-                                            int bsz, int max_blocks) {
-    if (table == nullptr) return (((long long)b * kvl + h) * ld_seq + p) * d;
-    return kv_row_in_block(kv_block(b, p, table, bsz, max_blocks), h, p, kvl, bsz, d);
-}
-
 // Update of a device-resident cache length, done by one thread of the
 // projection that follows the last reader of the length in a stage.
 struct LenUpdate {
@@ -70,30 +54,6 @@ struct Epilogue {
     LenUpdate len;
     int col0;           // GEMM launches over a column range: its first column (multiple of 64)
 };
-
-__device__ __forceinline__ void apply_len_update(const LenUpdate& u) {
-    if (u.ptr == nullptr) return;
-    if (u.value >= 0) {
-        *u.ptr = u.value;
-        if (u.overflow != nullptr) *u.overflow = 0;
-    } else {
-        const int v = *u.ptr;
-        if (v < u.cap) *u.ptr = v + 1;
-        else if (u.overflow != nullptr) *u.overflow = 1;
-    }
-}
-
-// Packed column layout shared by the projection kernels: for Q/K/V heads and
-// for the gate/up pair, every 64-row group of the packed weight holds two
-// 32-row halves that belong together: (dims i, i + d/2) of one head for the
-// rotary embedding, or (gate j, up j) for SwiGLU.  Packed row p of a head's
-// block maps to head dim:  g = p / 64, w = p % 64,
-//   dim = 32 g + w            (w < 32)
-//   dim = d/2 + 32 g + w - 32 (w >= 32).
-__host__ __device__ inline int packed_to_dim(int p, int d) {
-    int g = p >> 6, w = p & 63;
-    return w < 32 ? 32 * g + w : (d >> 1) + 32 * g + (w - 32);
-}
 
 // ---- bf16 path (gfx950 MFMA) ----
 void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M, int N, int K,

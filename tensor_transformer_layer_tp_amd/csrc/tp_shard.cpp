@@ -28,7 +28,7 @@ using namespace tp;
 // that the code object brings along on every device the library runs on.
 // In host code its name is a host-side stand-in, never a device address:
 // host code uses only the per-device address looked up once at set-up.
-static __device__ __align__(256) char scratch[TP_NOALLOC_SCRATCH_BYTES];
+static __device__ __attribute__((aligned(256))) char scratch[TP_NOALLOC_SCRATCH_BYTES];
 
 struct tp_shard {
     int hidden, heads, kv_heads, ffn, t, rank;
