@@ -463,9 +463,11 @@ def decode_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, B, L0, cap, copie
     return layers
 
 
-def decode_step_fn(torch, layers, hidden, t, B, x0):
+def decode_step_fn(torch, layers, hidden, t, B, x0, fused=True):
     """One decode token for B sequences through every layer copy: ATTN stage,
-    reduce, MLP stage, reduce (other ranks' partials are fixed stand-ins)."""
+    reduce, MLP stage, reduce (other ranks' partials are fixed stand-ins).
+    fused: each stage's reduce folded into its row-parallel projection
+    (tp_shard_forward_decode_reduce); else the stage, then tp_partial_reduce."""
     from tensor_transformer_layer_tp_amd import ATTN, MLP, partial_reduce
     g = torch.Generator(device="cuda")
     g.manual_seed(98)
@@ -474,15 +476,20 @@ def decode_step_fn(torch, layers, hidden, t, B, x0):
     pm = torch.empty_like(pa)
     hb = torch.empty_like(x0)
     yb = [torch.empty_like(x0) for _ in range(2)]
+    slots = [None, *others]   # rank 0's own slot
 
     def step():
         x = x0
         for i, (sh, kv) in enumerate(layers):
-            sh.decode(ATTN, x, kv, out=pa)
-            partial_reduce([pa, *others], residual=x, out=hb)
-            sh.decode(MLP, hb, out=pm)
             y = yb[i & 1]
-            partial_reduce([pm, *others], residual=hb, out=y)
+            if fused:
+                sh.decode_reduce(ATTN, x, slots, residual=x, kv=kv, out=hb)
+                sh.decode_reduce(MLP, hb, slots, residual=hb, out=y)
+            else:
+                sh.decode(ATTN, x, kv, out=pa)
+                partial_reduce([pa, *others], residual=x, out=hb)
+                sh.decode(MLP, hb, out=pm)
+                partial_reduce([pm, *others], residual=hb, out=y)
             x = y
 
     return step
@@ -514,6 +521,12 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
     g = capture(torch, step)
     gms, gdist = timed(torch, g.replay, args.steps, args.warmup, torch.cuda.current_stream())
     del g
+    # the same step with each reduce as its own launch, for comparison
+    step2 = decode_step_fn(torch, layers, hidden, t, 1, x0, fused=False)
+    step2()
+    g2 = capture(torch, step2)
+    g2ms, _ = timed(torch, g2.replay, args.steps, args.warmup, torch.cuda.current_stream())
+    del g2
     for sh, _ in layers:
         sh.timing(True)
     timed(torch, step, args.steps, 0, stream)
@@ -545,6 +558,7 @@ def bench_decode(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, L0, f
         "us_per_token_layer": round(best, 3),
         "us_per_token_layer_eager": round(us, 3),
         "us_per_token_layer_graph": round(us_graph, 3),
+        "us_per_token_layer_graph_separate_reduce": round(1e3 * g2ms / nl, 3),
         "step_ms": dist,
         "step_ms_graph": gdist,
         "bytes_per_token_layer": nbytes,

@@ -225,6 +225,29 @@ class Shard:
             _dev(out, "partial", torch.float32, (B, self.hidden)), _stream(stream)), "tp_shard_forward_decode")
         return out
 
+    def decode_reduce(self, stage: int, x: torch.Tensor, partials, residual: torch.Tensor | None = None,
+                      kv: KVCache | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """One decode stage and the reduce of its partial with the other ranks'
+        ``partials`` (a list of ``tp`` fp32 [B, hidden] tensors; entry ``rank`` is
+        not read and may be None), plus ``residual``: returns the reduced
+        [B, hidden] in the shard's dtype."""
+        if x.dim() != 2 or x.shape[1] != self.hidden:
+            raise ValueError("x must be [batch, hidden]")
+        B = int(x.shape[0])
+        if len(partials) != self.tp:
+            raise ValueError("partials must hold one entry per rank")
+        ptrs = (C.c_void_p * self.tp)()
+        for r, p in enumerate(partials):
+            ptrs[r] = None if (p is None or r == self.rank) else _dev(p, f"partials[{r}]", torch.float32,
+                                                                     (B, self.hidden)).value
+        if out is None:
+            out = torch.empty((B, self.hidden), dtype=self.torch_dtype, device=x.device)
+        res = None if residual is None else _dev(residual, "residual", self.torch_dtype, (B, self.hidden))
+        N.check(N.lib().tp_shard_forward_decode_reduce(
+            self._h, stage, _dev(x, "x", self.torch_dtype), B, kv._h if kv is not None else None, ptrs, res,
+            _dev(out, "out", self.torch_dtype, (B, self.hidden)), _stream(stream)), "tp_shard_forward_decode_reduce")
+        return out
+
     def norm(self, which: int, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         """RMSNorm of rows of x [..., hidden] with the shard's gain g1 (which=1)
         or g2 (which=2): the per-rank norm of the sequence-parallel flow."""

@@ -49,6 +49,8 @@ SIGNATURES = [
                                           C.c_void_p]),
     ("tp_shard_forward_decode_noalloc", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
                                                   C.c_void_p, C.c_void_p]),
+    ("tp_shard_forward_decode_reduce", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
+                                                 C.POINTER(C.c_void_p), C.c_void_p, C.c_void_p, C.c_void_p]),
     ("tp_partial_reduce", C.c_int, [C.POINTER(C.c_void_p), C.c_int, C.c_void_p, C.c_void_p, C.c_longlong, C.c_int,
                                     C.c_void_p]),
     ("tp_shard_debug_view", C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),

@@ -14,6 +14,47 @@ namespace tp {
 
 namespace {
 
+// The all-reduce's sum in a row-parallel projection's epilogue (EPI_SUM):
+// the other ranks' partials and the residual at rows r1 and r1 + 32 of
+// sequence b (slot `self` and ranks past t read nothing), ...
+__device__ __forceinline__ void sum_load(const Epilogue& epi, int b, int r1, float (&v1)[kSumMaxRanks],
+                                         float (&v2)[kSumMaxRanks], float& res1, float& res2, bool on = true) {
+    const SumDest& s = epi.sum;
+    const long long o = (long long)b * epi.ldo;
+#pragma unroll
+    for (int j = 0; j < kSumMaxRanks; ++j) {
+        const bool ld = on && j < s.t && j != s.self;
+        v1[j] = ld ? s.p[j][o + r1] : 0.f;
+        v2[j] = ld ? s.p[j][o + r1 + 32] : 0.f;
+    }
+    const bool hr = on && s.residual != nullptr;
+    res1 = hr ? bf2f(s.residual[o + r1]) : 0.f;
+    res2 = hr ? bf2f(s.residual[o + r1 + 32]) : 0.f;
+}
+
+// ... and h = (sum over ranks, in rank order, of the partials) + residual,
+// the order and rounding of the reduce kernel, with this projection's own
+// results y1, y2 in slot `self`.
+__device__ __forceinline__ void sum_store(const Epilogue& epi, int b, int r1, float y1, float y2,
+                                          const float (&v1)[kSumMaxRanks], const float (&v2)[kSumMaxRanks],
+                                          float res1, float res2) {
+    const SumDest& s = epi.sum;
+    float a1 = s.self == 0 ? y1 : v1[0], a2 = s.self == 0 ? y2 : v2[0];
+#pragma unroll
+    for (int j = 1; j < kSumMaxRanks; ++j)
+        if (j < s.t) {
+            a1 += j == s.self ? y1 : v1[j];
+            a2 += j == s.self ? y2 : v2[j];
+        }
+    if (s.residual != nullptr) {   // added only when present, so that a -0 sum stays -0
+        a1 += res1;
+        a2 += res2;
+    }
+    bf16* out = (bf16*)epi.out + (long long)b * epi.ldo;
+    out[r1] = f2bf(a1);
+    out[r1 + 32] = f2bf(a2);
+}
+
 // Stores output rows r1 and r1 + 32 (partners in one packed 64-row group) of
 // sequence b: fp32 partial, bf16 (GELU), SwiGLU of the (gate, up) pair, or
 // the rotary embedding of the (i, i + d/2) pair scattered to q and to the
@@ -25,6 +66,10 @@ __device__ __forceinline__ void pair_store(const Epilogue& epi, int b, int r1, f
         float* o = (float*)epi.out + (long long)b * epi.ldo;
         o[r1] = y1;
         o[r2] = y2;
+    } else if constexpr (MODE == EPI_SUM) {
+        float v1[kSumMaxRanks], v2[kSumMaxRanks], res1, res2;
+        sum_load(epi, b, r1, v1, v2, res1, res2);
+        sum_store(epi, b, r1, y1, y2, v1, v2, res1, res2);
     } else if constexpr (MODE == EPI_STORE || MODE == EPI_GELU) {
         bf16* o = (bf16*)epi.out + (long long)b * epi.ldo;
         o[r1] = f2bf(MODE == EPI_GELU ? gelu_erf_f(y1) : y1);
@@ -123,6 +168,12 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
 #pragma unroll
             for (int h = 0; h < XC; ++h) gv[i][h] = *(const u16x8*)(gamma + cofs[i] * CW + 8 * h);
     }
+    // EPI_SUM: the epilogue thread's other-rank partials and residual are
+    // loaded before the weights, so that their latency is spent while the
+    // weights stream instead of at the end of the work-group
+    float sv1[kSumMaxRanks], sv2[kSumMaxRanks], sr1 = 0.f, sr2 = 0.f;
+    if constexpr (MODE == EPI_SUM)
+        sum_load(epi, tid % NB, rbase + min(tid / NB, P - 1), sv1, sv2, sr1, sr2, tid < P * NB);
     // Weight rows are read once per call: non-temporal loads stream them
     // without displacing the activations and partials from the caches.
     u32x4 wv[R][NI];
@@ -233,7 +284,8 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
         y1 *= wscale[rbase + e];
         y2 *= wscale[rbase + 32 + e];
     }
-    pair_store<MODE>(epi, b, rbase + e, y1, y2);
+    if constexpr (MODE == EPI_SUM) sum_store(epi, b, rbase + e, y1, y2, sv1, sv2, sr1, sr2);
+    else pair_store<MODE>(epi, b, rbase + e, y1, y2);
 }
 
 // Per-row E4M3 quantisation of a bf16 matrix [N, K]: one work-group per
@@ -918,6 +970,7 @@ void gemv_mode(const bf16* x, const bf16* gamma, float eps, const void* W, const
     dim3 g(N / (2 * P)), b(T);
     switch (epi.mode) {
         case EPI_F32: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_F32, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
+        case EPI_SUM: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_SUM, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
         case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_QKV, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
         case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_SWIGLU, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
         case EPI_GELU: hipLaunchKernelGGL((gemv_kernel<NB, P, NI, EPI_GELU, NORM, W8, T>), g, b, 0, st, x, gamma, eps, W, ws, N, K, epi); break;
@@ -993,6 +1046,7 @@ void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part,
     const dim3 fg(cdiv(B * (N >> 1), 256));
     switch (epi.mode) {
         case EPI_F32: hipLaunchKernelGGL(skinny_fixup<EPI_F32>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
+        case EPI_SUM: hipLaunchKernelGGL(skinny_fixup<EPI_SUM>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
         case EPI_QKV: hipLaunchKernelGGL(skinny_fixup<EPI_QKV>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
         case EPI_SWIGLU: hipLaunchKernelGGL(skinny_fixup<EPI_SWIGLU>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;
         case EPI_GELU: hipLaunchKernelGGL(skinny_fixup<EPI_GELU>, fg, dim3(256), 0, st, part, ks, B, N, epi); break;

@@ -14,6 +14,19 @@ enum EpiMode {
     EPI_SWIGLU = 2,  // act[m, j] = SiLU(gate) * up, gate/up interleaved in 32-column blocks
     EPI_GELU = 3,    // act[m, n] = GELU_erf(acc)
     EPI_STORE = 4,   // out[m, n] = acc in the storage type
+    EPI_SUM = 5,     // out[m, n] = bf16(sum of the t ranks' partials in rank order + residual), with acc as
+                     // the partial of rank `self` (decode GEMV and split-K paths only)
+};
+
+// The all-reduce's sum folded into a row-parallel projection's epilogue: the
+// other ranks' fp32 partials [rows, ldo] (p[self] is not read), an optional
+// bf16 residual of the same layout.
+constexpr int kSumMaxRanks = 8;
+struct SumDest {
+    const float* p[kSumMaxRanks];
+    const bf16* residual;   // nullptr: none
+    int t;                  // 1 <= t <= kSumMaxRanks
+    int self;               // the rank whose partial is the accumulator
 };
 
 struct QKVDest {
@@ -53,6 +66,7 @@ struct Epilogue {
     QKVDest qkv;
     LenUpdate len;
     int col0;           // GEMM launches over a column range: its first column (multiple of 64)
+    SumDest sum;        // EPI_SUM only
 };
 
 // ---- bf16 path (gfx950 MFMA) ----

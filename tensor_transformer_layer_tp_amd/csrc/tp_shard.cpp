@@ -179,9 +179,10 @@ int ensure_rope(tp_shard* s, int npos, hipStream_t st) {
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout for T tokens: merge counters | n | q | o | k,v (when no
-// cache) | act | decode scratch
+// cache) | act | decode scratch | decode partial (the fused-sum entry point's
+// own partial where its epilogue cannot take the sum)
 struct Layout {
-    size_t n, q, o, kv, act, scr, total;
+    size_t n, q, o, kv, act, scr, part, total;
 };
 Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) {
     Layout L;
@@ -199,7 +200,8 @@ Layout layout(const tp_shard* s, long long T, int len_decode, int batch_decode) 
                                   {s->hidden, s->fl}};
         for (const auto& nk : shapes) scr = std::max(scr, skinny_scratch_bytes(batch_decode, nk[0], nk[1]));
     }
-    L.total = L.scr + al(scr);
+    L.part = L.scr + al(scr);
+    L.total = L.part + (batch_decode > 0 ? al((size_t)batch_decode * s->hidden * sizeof(float)) : 0);
     return L;
 }
 
@@ -697,16 +699,26 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
 
 namespace {
 
+// The all-reduce's sum of a fused-sum decode call: the t ranks' partials
+// (slot `self` unused), the residual and the reduced output.
+struct FuseSum {
+    const float* const* parts;
+    const void* residual;
+    void* out;
+};
+
 // One decode stage over the workspace at `base`: the library's own workspace
 // (grown on demand) or, for the allocation-free entry point, the device's
-// static scratch array.
+// static scratch array.  With `fuse`, the stage's row-parallel projection
+// also takes the reduce over the ranks: in its epilogue on the GEMV and
+// split-K paths, else as a reduce of its partial (kept in the workspace).
 int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial, void* stream,
-                 bool noalloc) {
+                 bool noalloc, const FuseSum* fuse = nullptr) {
     const bool prenorm = (stage & TP_STAGE_PRENORM) != 0;
     stage &= ~TP_STAGE_PRENORM;
-    if (!s || !x || !partial || batch <= 0) return TP_E_ARG;
+    if (!s || !x || (!partial && !fuse) || batch <= 0) return TP_E_ARG;
     if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return TP_E_ARG;
-    if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
+    if (!aligned16(x) || (partial && !aligned16(partial))) return TP_E_ARG;
     if (!s->loaded) return TP_E_STATE;
     hipStream_t st = (hipStream_t)stream;
     const bool bf = s->o.dtype == TP_BF16;
@@ -745,6 +757,28 @@ int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, fl
     s->off_n = lay.n;
     s->off_o = lay.o;
     s->off_act = lay.act;
+    // the sum goes into the GEMV or split-K epilogue (bf16, up to kSumMaxRanks
+    // ranks); otherwise the stage writes its partial into the workspace and a
+    // reduce follows
+    const bool sum_epi = fuse && use_gemv && s->t <= kSumMaxRanks;
+    float* own = fuse ? (float*)(ws + lay.part) : partial;
+    auto set_sum = [&](Epilogue& e) {
+        e.mode = EPI_SUM;
+        e.out = fuse->out;
+        e.ldo = s->hidden;
+        for (int r = 0; r < kSumMaxRanks; ++r) e.sum.p[r] = r < s->t && r != s->rank ? fuse->parts[r] : nullptr;
+        e.sum.residual = (const bf16*)fuse->residual;
+        e.sum.t = s->t;
+        e.sum.self = s->rank;
+    };
+    auto reduce_own = [&]() -> int {
+        if (!fuse || sum_epi) return TP_OK;
+        const float* ptrs[64];
+        for (int r = 0; r < s->t; ++r) ptrs[r] = r == s->rank ? own : fuse->parts[r];
+        partial_reduce(ptrs, s->t, fuse->residual, fuse->out, (long long)batch * s->hidden, bf, st);
+        LAUNCH_CHECK("partial_reduce");
+        return TP_OK;
+    };
     if (stage == TP_STAGE_ATTN) {
         if (!noalloc) TRY(ensure_rope(s, kv->max_seq + 1, st));   // fp32: a query at position max_seq stays in range
         void* qbuf = ws + lay.q;
@@ -781,17 +815,19 @@ int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, fl
         if (use_gemv) {
             Epilogue epi{};
             epi.mode = EPI_F32;
-            epi.out = partial;
+            epi.out = own;
             epi.ldo = s->hidden;
             epi.len = LenUpdate{kv->dlen, -1, kv->max_seq, kv->dlen + 1};
+            if (sum_epi) set_sum(epi);
             KTimer kt(s, TP_K_GEMV_OUT, st);
             TRY(launch_gemv(s, ws + lay.o, batch, nullptr, s->w_o, s->hidden, s->hl * s->d, epi, ws + lay.n,
                             ws + lay.scr, st, 1));
         } else {
             KTimer kt(s, TP_K_GEMM_OUT, st);
-            TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
+            TRY(launch_proj(s, ws + lay.o, batch, s->hl * s->d, s->w_o, s->hidden, EPI_F32, own, s->hidden, st,
                             LenUpdate{kv->dlen, -1, kv->max_seq, kv->dlen + 1}));
         }
+        TRY(reduce_own());
         if (!capturing) kv->len = L + 1;
         s->attn_seen = true;
     } else {
@@ -808,8 +844,9 @@ int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, fl
             }
             Epilogue e2{};
             e2.mode = EPI_F32;
-            e2.out = partial;
+            e2.out = own;
             e2.ldo = s->hidden;
+            if (sum_epi) set_sum(e2);
             KTimer kt(s, TP_K_GEMV_DOWN, st);
             TRY(launch_gemv(s, ws + lay.act, batch, nullptr, s->w_down, s->hidden, s->fl, e2, ws + lay.n,
                             ws + lay.scr, st, 3));
@@ -825,8 +862,9 @@ int decode_stage(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, fl
                 TRY(launch_proj(s, xin, batch, s->hidden, s->w_up, s->nup, mode, ws + lay.act, s->fl, st));
             }
             KTimer kt(s, TP_K_GEMM_DOWN, st);
-            TRY(launch_proj(s, ws + lay.act, batch, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
+            TRY(launch_proj(s, ws + lay.act, batch, s->fl, s->w_down, s->hidden, EPI_F32, own, s->hidden, st));
         }
+        TRY(reduce_own());
     }
     return TP_OK;
 }
@@ -843,6 +881,20 @@ int tp_shard_forward_decode(tp_shard* s, int stage, const void* x, int batch, tp
 int tp_shard_forward_decode_noalloc(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv, float* partial,
                                     void* stream) {
     return decode_stage(s, stage, x, batch, kv, partial, stream, true);
+}
+
+int tp_shard_forward_decode_reduce(tp_shard* s, int stage, const void* x, int batch, tp_kv* kv,
+                                   const float* const* partials, const void* residual, void* out, void* stream) {
+    if (!s || !x || !partials || !out || batch <= 0) return TP_E_ARG;
+    for (int r = 0; r < s->t; ++r)
+        if (r != s->rank && (!partials[r] || !aligned16(partials[r]))) return TP_E_ARG;
+    if (!aligned16(out) || (residual && !aligned16(residual))) return TP_E_ARG;
+    // the projections read all of x while the epilogue writes out
+    const uintptr_t xb = (uintptr_t)x, ob = (uintptr_t)out;
+    const uintptr_t xe = xb + (size_t)batch * s->hidden * s->esz, oe = ob + (size_t)batch * s->hidden * s->esz;
+    if (xb < oe && ob < xe) return TP_E_ARG;
+    const FuseSum f{partials, residual, out};
+    return decode_stage(s, stage, x, batch, kv, nullptr, stream, false, &f);
 }
 
 int tp_partial_reduce(const float* const* partials, int t, const void* residual, void* out, long long n,

@@ -199,6 +199,24 @@ void flow(const Shape& sh, int dtype, int act, int fp8) {
     EXPECT_RC(tp_shard_forward_decode_noalloc(s, TP_STAGE_ATTN, x.p, B, kv, part.as<float>(), nullptr), want_noalloc);
     EXPECT_RC(tp_shard_forward_decode_noalloc(s, TP_STAGE_MLP | TP_STAGE_PRENORM, x.p, B, nullptr, part.as<float>(),
                                               nullptr), want_noalloc);
+    // decode with the reduce folded in: the GEMV / split-K epilogue, or the
+    // workspace partial and a reduce (GEMM path, fp32 shards)
+    {
+        const float* others[2] = {part.as<float>(), part2.as<float>()};
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_ATTN, x.p, B, kv, others, x.p, out.p, nullptr), TP_OK);
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, out.p, B, nullptr, others, out.p, nout.p, nullptr),
+                  TP_OK);
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, out.p, B, nullptr, others, nullptr, nout.p,
+                                                 nullptr), TP_OK);
+        const float* lost_other[2] = {sh.rank == 0 ? part.as<float>() : nullptr,
+                                      sh.rank == 1 ? part.as<float>() : nullptr};
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, out.p, B, nullptr, lost_other, out.p, nout.p,
+                                                 nullptr), TP_E_ARG);   // the other rank's partial is missing
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, out.p, B, nullptr, others, out.p,
+                                                 out.as<char>() + 64, nullptr), TP_E_ARG);   // out overlaps x
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, out.p, B, nullptr, nullptr, out.p, nout.p,
+                                                 nullptr), TP_E_ARG);
+    }
     // the cache fills up: an eager call on a full cache is refused up front
     EXPECT_RC(tp_kv_set_len(kv, cap + 1), TP_E_ARG);
     EXPECT_RC(tp_kv_set_len(kv, cap), TP_OK);
@@ -221,6 +239,17 @@ void flow(const Shape& sh, int dtype, int act, int fp8) {
         EXPECT_RC(tp_kv_create(s, BB, 8, &kvb), TP_OK);
         EXPECT_RC(tp_shard_forward_decode(s, TP_STAGE_ATTN, xb.p, BB, kvb, pb.as<float>(), nullptr), TP_OK);
         EXPECT_RC(tp_shard_forward_decode(s, TP_STAGE_MLP, xb.p, BB, nullptr, pb.as<float>(), nullptr), TP_OK);
+        Dev pb2((size_t)BB * h * 4), hb((size_t)BB * h * esz);
+        const float* others[2] = {pb.as<float>(), pb2.as<float>()};
+        EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, xb.p, BB, nullptr, others, xb.p, hb.p, nullptr),
+                  TP_OK);
+        {
+            // batch 1 through the GEMV epilogue (the E4M3 one on an fp8 shard)
+            Dev x1((size_t)h * esz), p1((size_t)h * 4), p2((size_t)h * 4), h1((size_t)h * esz);
+            const float* o1[2] = {p1.as<float>(), p2.as<float>()};
+            EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, x1.p, 1, nullptr, o1, x1.p, h1.p, nullptr),
+                      TP_OK);
+        }
         tp_kv_destroy(kvb);
     }
     if (fp8) {

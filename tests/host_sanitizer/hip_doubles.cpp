@@ -158,6 +158,16 @@ void epilogue_ranges(const Epilogue& e, long long rows, int n, size_t esz) {
         case EPI_STORE:
             in_alloc(e.out, ((rows - 1) * e.ldo + col_end) * (long long)esz, "projection output");
             break;
+        case EPI_SUM: {
+            const long long n = (rows - 1) * e.ldo + col_end;
+            if (e.sum.t < 1 || e.sum.t > kSumMaxRanks || e.sum.self < 0 || e.sum.self >= e.sum.t)
+                fail("fused sum: rank count or slot", e.out, 0);
+            in_alloc(e.out, n * 2, "reduced output");
+            for (int j = 0; j < e.sum.t; ++j)
+                if (j != e.sum.self) in_alloc(e.sum.p[j], n * 4, "other rank's partial");
+            if (e.sum.residual) in_alloc(e.sum.residual, n * 2, "residual");
+            break;
+        }
         default: {
             const QKVDest& q = e.qkv;
             const long long B = rows / q.S;

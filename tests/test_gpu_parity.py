@@ -443,6 +443,115 @@ def test_decode_long_cache(L_len, mode):
     assert_close(o, ref["o"].reshape(B, -1), "decode o", "bf16")
 
 
+def _fused_pair(L, tp, r, fp8):
+    """Two identical shards (the E4M3 variant with fp8)."""
+    def make():
+        if not fp8:
+            return L.shard(tp, r)
+        s = L.spec
+        sh = Shard(s.hidden, s.heads, s.kv_heads, s.ffn, tp, r, decode_fp8=True)
+        sh.load_weights({k: v for k, v in L.dev.items() if k not in ("x", "k_cache", "v_cache", "x_dec")})
+        return sh
+    return make(), make()
+
+
+@pytest.mark.parametrize("dtype,B,tp,r,fp8,res", [
+    ("bf16", 1, 2, 1, False, True),    # GEMV epilogue
+    ("bf16", 1, 8, 0, False, True),    # eight ranks, own slot first
+    ("bf16", 1, 8, 7, True, True),     # E4M3 GEMV, own slot last
+    ("bf16", 3, 4, 2, False, False),   # split-K epilogue, no residual
+    ("bf16", 70, 2, 0, False, True),   # GEMM path: workspace partial, then the reduce
+    ("f32", 2, 2, 1, False, True),     # fp32 shard: workspace partial, then the reduce
+])
+def test_decode_reduce_equals_two_calls(dtype, B, tp, r, fp8, res):
+    """tp_shard_forward_decode_reduce against tp_shard_forward_decode followed
+    by tp_partial_reduce with the same other-rank partials: h and y bit for
+    bit and the caches bit for bit, for both stages; h also against the
+    oracle's reduce of the oracle's decode partial and the same other-rank
+    partials."""
+    announce(f"decode with the reduce folded in: {dtype} B={B} t={tp} rank {r} fp8={fp8} residual={res}")
+    hid, S = 1024, 48
+    L = Layer(hid, 16, 8, 4096, dtype=dtype, batch=B, seq=S + 1, gamma_noise=True, seed=51)
+    sh_a, sh_b = _fused_pair(L, tp, r, fp8)
+    kv_a, kv_b = sh_a.kv_cache(B, S + 4), sh_b.kv_cache(B, S + 4)
+    pre = L.dev["x"][:, :S].contiguous()
+    sh_a.prefill(ATTN, pre, kv_a)
+    sh_b.prefill(ATTN, pre, kv_b)
+    x = L.dev["x"][:, S].contiguous()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    oth_a = [torch.randn((B, hid), generator=g, device="cuda") for _ in range(tp)]
+    oth_m = [torch.randn((B, hid), generator=g, device="cuda") for _ in range(tp)]
+    resid = (lambda t: t) if res else (lambda t: None)
+    pa = sh_a.decode(ATTN, x, kv_a)
+    h_ref = partial_reduce([pa if j == r else oth_a[j] for j in range(tp)], residual=resid(x), dtype=dtype)
+    pm = sh_a.decode(MLP, h_ref)
+    y_ref = partial_reduce([pm if j == r else oth_m[j] for j in range(tp)], residual=resid(h_ref), dtype=dtype)
+    h = sh_b.decode_reduce(ATTN, x, [None if j == r else oth_a[j] for j in range(tp)], residual=resid(x), kv=kv_b)
+    y = sh_b.decode_reduce(MLP, h, [None if j == r else oth_m[j] for j in range(tp)], residual=resid(h))
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_ref), "h differs from decode + partial_reduce"
+    assert torch.equal(y, y_ref), "y differs from decode + partial_reduce"
+    ka, va = kv_a.read()
+    kb, vb = kv_b.read()
+    torch.cuda.synchronize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+    assert kv_b.length == S + 1
+    if not fp8:
+        pre_o = O.attn_stage(L.exact["x"][:, :S], L.W, L.spec, tp, r)
+        ref = O.decode_attn_stage(L.exact["x"][:, S], pre_o["k"], pre_o["v"], L.W, L.spec, tp, r)
+        parts = [ref["partial"] if j == r else to_np(oth_a[j]) for j in range(tp)]
+        resid_np = L.exact["x"][:, S] if res else np.zeros((B, hid))
+        assert_close(to_np(h), O.reduce(parts, resid_np, L.spec), "fused h vs the oracle's reduce", dtype)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_decode_reduce_graph_replay(B):
+    """A decode step made of the two fused calls, captured in a HIP graph and
+    replayed with new inputs, against eager twins (bit for bit)."""
+    announce(f"fused decode step in a HIP graph, B={B}: 3 replays against eager twins")
+    S, hid, tp, r = 24, 512, 2, 1
+    L = Layer(hid, 4, 2, 1024, batch=B, seq=S + 4, gamma_noise=True, seed=61)
+    sh_e, sh_g = L.shard(tp, r), L.shard(tp, r)
+    kv_e, kv_g = sh_e.kv_cache(B, S + 8), sh_g.kv_cache(B, S + 8)
+    pre = L.dev["x"][:, :S].contiguous()
+    sh_e.prefill(ATTN, pre, kv_e)
+    sh_g.prefill(ATTN, pre, kv_g)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    oth = [[torch.randn((B, hid), generator=g, device="cuda") for _ in range(tp)] for _ in range(2)]
+    xbuf = torch.empty((B, hid), dtype=torch.bfloat16, device="cuda")
+    hbuf, ybuf = torch.empty_like(xbuf), torch.empty_like(xbuf)
+
+    def step():
+        sh_g.decode_reduce(ATTN, xbuf, oth[0], residual=xbuf, kv=kv_g, out=hbuf)
+        sh_g.decode_reduce(MLP, hbuf, oth[1], residual=hbuf, out=ybuf)
+
+    def eager(i):
+        h = sh_e.decode_reduce(ATTN, L.dev["x"][:, S + i].contiguous(), oth[0],
+                               residual=L.dev["x"][:, S + i].contiguous(), kv=kv_e)
+        return h, sh_e.decode_reduce(MLP, h, oth[1], residual=h)
+
+    xbuf.copy_(L.dev["x"][:, S])
+    step()
+    he, ye = eager(0)
+    torch.cuda.synchronize()
+    assert torch.equal(hbuf, he) and torch.equal(ybuf, ye)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        xbuf.copy_(L.dev["x"][:, S + i])
+        graph.replay()
+        he, ye = eager(i)
+        torch.cuda.synchronize()
+        assert torch.equal(hbuf, he), f"replay {i}: h differs from the eager call"
+        assert torch.equal(ybuf, ye), f"replay {i}: y differs from the eager call"
+        assert kv_g.length == S + 1 + i
+    del graph
+
+
 @pytest.mark.parametrize("B", [1, 3, 70])   # GEMV, split-K and GEMM projection paths
 def test_decode_graph_replay(B):
     """A decode step (ATTN + MLP stage) captured in a HIP graph and replayed
