@@ -991,6 +991,15 @@ void gemv_ni(const bf16* x, const bf16* gamma, float eps, const void* W, const f
             return;
         }
     }
+    // few rows (the 70B-shaped Q/K/V at t=8: 1280): 2 rows per work-group, so
+    // that the grid still spreads evenly over the CUs
+    if constexpr (NB == 1) {
+        if (N / 4 < 512) {
+            if (gamma) gemv_mode<NB, 1, NI, true, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
+            else gemv_mode<NB, 1, NI, false, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
+            return;
+        }
+    }
     if (gamma) gemv_mode<NB, 2, NI, true, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
     else gemv_mode<NB, 2, NI, false, W8, T>(x, gamma, eps, W, ws, N, K, epi, st);
 }
