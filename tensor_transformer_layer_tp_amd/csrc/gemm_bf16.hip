@@ -841,9 +841,9 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
     // Fragments of the next k-slice are read while the current one's MFMAs
-    // run, where the register budget allows two sets (not with 128
-    // accumulators); the compiler otherwise reads each fragment right before
-    // its MFMA.
+    // run: into a second set where the register budget allows two (not with
+    // 128 accumulators), else into the registers of the current set that its
+    // MFMAs have finished with.
     constexpr bool DB = FM * FN * 16 + 8 * (FM + FN) <= 152;
     bf16x8 fa[DB ? 2 : 1][FM], fb[DB ? 2 : 1][FN];
     auto rd = [&](int st, int kk, int buf) {
@@ -886,6 +886,58 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
                 rd(st ^ 1, 0, 0);   // the next tile's first slice, published by the barrier
             }
         }
+    } else if constexpr (FN == 2) {
+        // One fragment set, read ahead into the registers the current
+        // slice's MFMAs are done with: in B-major order fb[0] is free after
+        // the first FM MFMAs of a slice and fa[i] after MFMA (i, 1), so the
+        // next slice's fragments are read while the slice's second half runs.
+        // The tile's last slice starts with the barrier (its fragments are
+        // already in registers), and its MFMAs cover the first reads of the
+        // next tile.  Same MFMAs per accumulator, in the same k order.
+        auto rd_a = [&](int st, int kk, int i) {
+            const bf16* a_s = smem + st * STAGE + (wm * TM + frow) * BK;
+            fa[0][i] = *(const bf16x8*)(a_s + i * 32 * BK + (swz<8>(frow, 2 * kk + khalf) << 3));
+        };
+        auto rd_b = [&](int st, int kk, int j) {
+            const bf16* b_s = smem + st * STAGE + BM * BK + (wn * TN + frow) * BK;
+            fb[0][j] = *(const bf16x8*)(b_s + j * 32 * BK + (swz<8>(frow, 2 * kk + khalf) << 3));
+        };
+        // the slice's MFMAs, reading slice (st_n, kk_n) into the freed registers
+        auto slice = [&](int st_n, int kk_n) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][0], acc[i][0], 0, 0, 0);
+            rd_b(st_n, kk_n, 0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][1], acc[i][1], 0, 0, 0);
+                rd_a(st_n, kk_n, i);
+            }
+            rd_b(st_n, kk_n, 1);
+#pragma unroll
+            for (int q = 0; q < FM; ++q) __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);                                // DS read
+#pragma unroll
+            for (int q = 0; q < FM; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);       // DS read
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        rd(0, 0, 0);
+        for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int kk = 0; kk < KK - 1; ++kk) slice(st, kk + 1);
+                __syncthreads();       // publishes tile kt + st + 1 in the other stage
+                slice(st ^ 1, 0);      // (past the last tile: a read whose result is unused)
+            }
+        }
+        // no fragment read of this wave is still in flight when its epilogue
+        // writes its part of LDS
+        __builtin_amdgcn_s_waitcnt(0xc07f);
     } else {
         for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
