@@ -1144,8 +1144,8 @@ def main():
         summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
-              "build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs one rank's shard per "
+              "device, and the ranks' collectives are not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
