@@ -298,32 +298,18 @@ __device__ __forceinline__ void epilogue_staged(f32x16 (&acc)[FM][FN], const Epi
     }
 }
 
-// Direct-to-LDS load of one 16-byte chunk per lane: lane i of the wave lands
-// at LDS byte m0 + 16 i.  The compiler does not see this as an LDS write, so
-// it adds no conservative waits; the caller waits on vmcnt before the barrier
-// that publishes a stage.  M0 is saved and restored around the load.
-__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %4\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-        : "memory");
+// Direct-to-LDS load of one 16-byte chunk per lane (buffer_load_dwordx4 ...
+// lds): lane i of the wave lands at LDS byte lds + 16 i.  The caller waits on
+// vmcnt before the barrier that publishes a stage.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(uintptr_t)lds, 16, (int)voff, (int)soff, 0, 0);
 }
 
-
-__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    u32x4_t r;
-    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    r[2] = __builtin_amdgcn_readfirstlane(bytes);
-    r[3] = 0x00020000u;
-    return r;
+// Buffer resource over `bytes` bytes from base (raw, no stride): reads past
+// the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
 // The MFMAs of one LDS stage.  Fragments of k-slice kk+1 are read before the
@@ -388,8 +374,8 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ 
     const int m0 = tm * BM, n0 = tn * BN;
 
     // rows past M / N fall outside the resources and read as zeros
-    const u32x4_t rsa = make_rsrc(A + (long long)m0 * lda, (uint32_t)(min(BM, M - m0) * lda * 2));
-    const u32x4_t rsb = make_rsrc(B + (long long)n0 * ldb, (uint32_t)(min(BN, N - n0) * ldb * 2));
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A + (long long)m0 * lda, (uint32_t)(min(BM, M - m0) * lda * 2));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B + (long long)n0 * ldb, (uint32_t)(min(BN, N - n0) * ldb * 2));
     const int lrow = lane / CPR, lslot = lane % CPR;
     uint32_t va[IA], vb[IB];
 #pragma unroll
@@ -469,8 +455,8 @@ __global__ __launch_bounds__(256) void gemm_dma_pipe_kernel(const bf16* __restri
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const u32x4_t rsa = make_rsrc(A + (long long)m0 * lda, (uint32_t)(min(BM, M - m0) * lda * 2));
-    const u32x4_t rsb = make_rsrc(B + (long long)n0 * ldb, (uint32_t)(min(BN, N - n0) * ldb * 2));
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A + (long long)m0 * lda, (uint32_t)(min(BM, M - m0) * lda * 2));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B + (long long)n0 * ldb, (uint32_t)(min(BN, N - n0) * ldb * 2));
     const int lrow = lane / CPR, lslot = lane % CPR;
     uint32_t vab[IA + IB];
 #pragma unroll
