@@ -1098,9 +1098,14 @@ DecodeAttnPlan decode_attn_plan(int B, int hl, int kvl, int cap, int d) {
     else
         while (ch > lo && (long long)((cap + ch - 1) / ch) * hl * B < 256) ch >>= 1;
     const int n = (cap + ch - 1) / ch;
+    // With several query heads per KV head, a multiple of 8 chunks puts the
+    // heads' work-groups for one chunk on one XCD (its L2 serves the shared
+    // K/V rows); one query head per KV head, or a short cache, gains nothing
+    // from it and would only launch empty work-groups.
+    const int nf = hl / kvl > 1 && n >= 8 ? (n + 7) / 8 * 8 : n;
     const bool fits = (long long)B * hl <= kDecodeCounters;
-    if (g_decode_mode == 2 && fits) return {true, true, ch, (n + 7) / 8 * 8};
-    if (g_decode_mode == 0 || g_decode_mode == 3) return {true, false, ch, (n + 7) / 8 * 8};
+    if (g_decode_mode == 2 && fits) return {true, true, ch, nf};
+    if (g_decode_mode == 0 || g_decode_mode == 3) return {true, false, ch, nf};
     const int chs = split_chunk(B, hl, kvl, cap, d);
     return {false, false, chs, (cap + chs - 1) / chs};
 }
