@@ -111,6 +111,36 @@ def test_forward_before_weights_is_state_error():
         lib.tp_shard_destroy(h)
 
 
+def test_decode_reduce_argument_and_state_errors():
+    """tp_shard_forward_decode_reduce validates on the host before any
+    device call: missing pointers, a lost other rank, misalignment and an
+    output overlapping the input are argument errors; a shard without
+    weights is a state error."""
+    lib = N.lib()
+    h = C.c_void_p()
+    assert lib.tp_shard_create(4096, 32, 8, 11008, 2, 1, None, C.byref(h)) == N.TP_OK
+    x, out, p0 = 0x100000, 0x200000, 0x300000
+    parts = (C.c_void_p * 2)(p0, None)          # rank 1's own slot may be NULL
+    f = lib.tp_shard_forward_decode_reduce
+    try:
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, parts, None, C.c_void_p(out), None) == N.TP_E_STATE
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, None, None, C.c_void_p(out), None) == N.TP_E_ARG
+        lost = (C.c_void_p * 2)(None, p0)       # rank 0's partial missing
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, lost, None, C.c_void_p(out), None) == N.TP_E_ARG
+        mis = (C.c_void_p * 2)(p0 + 4, None)
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, mis, None, C.c_void_p(out), None) == N.TP_E_ARG
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, parts, None, C.c_void_p(out + 8), None) == N.TP_E_ARG
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, parts, C.c_void_p(x + 2), C.c_void_p(out),
+                 None) == N.TP_E_ARG                                    # misaligned residual
+        # out overlapping x (4096 bf16 values = 8 KB per sequence)
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, parts, None, C.c_void_p(x + 4096), None) == N.TP_E_ARG
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 2, None, parts, None, C.c_void_p(x + 8192), None) == N.TP_E_ARG
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 1, None, parts, None, C.c_void_p(x + 8192), None) == N.TP_E_STATE
+        assert f(h, N.TP_STAGE_MLP, C.c_void_p(x), 0, None, parts, None, C.c_void_p(out), None) == N.TP_E_ARG
+    finally:
+        lib.tp_shard_destroy(h)
+
+
 def test_partial_reduce_argument_errors():
     lib = N.lib()
     fake = 0x10000
