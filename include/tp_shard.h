@@ -438,6 +438,15 @@ int tp_tune_set_gemm_split(int cfg0, int cfg1, int cols0);
  * TP_E_ARG outside 0..2. */
 int tp_tune_set_attn_groups(int kg);
 
+/* tp_tune_set_attn_kernel -- tuning hook for prefill attention: 1 runs the
+ * kernel that stages each key block through registers into one LDS stage per
+ * key group (two barriers per key block), 2 the software-pipelined kernel
+ * (the default: K and V loaded straight into two LDS stages each, one barrier
+ * per key block, the scores of the next block computed under the
+ * exponentials of this one), 0 restores the default.  Same results up to
+ * rounding order.  Process-wide, not thread-safe.  TP_E_ARG outside 0..2. */
+int tp_tune_set_attn_kernel(int k);
+
 /* tp_tune_set_decode_chunk -- tuning hook for bf16 decode attention: 16, 32
  * or 64 cached positions per chunk work-group (32 at least for head dim 64;
  * the split kernel for one query head per KV head always takes 64), or 0 to

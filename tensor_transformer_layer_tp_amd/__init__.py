@@ -453,3 +453,9 @@ def set_decode_attn(mode: int) -> None:
 def set_attn_groups(kg: int) -> None:
     """Tuning hook: prefill attention key groups (0 = automatic, 1 or 2)."""
     N.check(N.lib().tp_tune_set_attn_groups(int(kg)), "tp_tune_set_attn_groups")
+
+
+def set_attn_kernel(k: int) -> None:
+    """Tuning hook: prefill attention kernel (0 = default, 1 one LDS stage
+    per key group, 2 pipelined: the default)."""
+    N.check(N.lib().tp_tune_set_attn_kernel(int(k)), "tp_tune_set_attn_kernel")

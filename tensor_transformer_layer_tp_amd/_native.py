@@ -66,6 +66,7 @@ SIGNATURES = [
                                     C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     ("tp_tune_set_gemm_config", C.c_int, [C.c_int]),
     ("tp_tune_set_attn_groups", C.c_int, [C.c_int]),
+    ("tp_tune_set_attn_kernel", C.c_int, [C.c_int]),
     ("tp_tune_gemm_plan", C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int),
                                     C.POINTER(C.c_int)]),
     ("tp_tune_set_gemm_split", C.c_int, [C.c_int, C.c_int, C.c_int]),

@@ -313,11 +313,308 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_kernel(
     }
 }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: a wave fills 1 KB at
+// the (wave-uniform) LDS byte address lds, lane L at lds + 16 L.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 16, voff, 0, 0, 0);
+}
+
+// Software-pipelined form of the same computation.  K and V reach LDS by
+// direct loads (no register staging), each key group holding two stages of
+// each, so one barrier per key block suffices: after barrier i the waves
+// compute the scores of block i+1 from one K stage while the exponentials of
+// block i run, then P·V of block i from one V stage, while K of block i+2
+// and V of block i+1 land in the stages that blocks i and i-1 freed.
+//
+// V stays row-major in LDS and the P·V operand is read with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// i receives element i % 4 of the 8-byte rows that lanes i/4, i/4 + 4, i/4 +
+// 8 and i/4 + 12 of the group address.  Lane r of group g therefore points at
+// key 16 j + 4 (g / 2) + r / 4, dims 32 T + 16 (g % 2) + 4 (r % 4) .. + 3; two
+// such reads (keys + 8) give lane (col, h) the dims-32T+col column of the 8
+// keys that its P^T operand holds.
+//
+// The running max starts at a finite floor instead of -inf, so a key block
+// that is masked for every query of a wave contributes exp2(-inf) = 0 with no
+// branch around it; the row sum adds the bf16 probabilities that P·V uses.
+template <int D>
+__device__ __forceinline__ int vswz(int key) {   // 16-byte chunk XOR of a V row
+    return D == 128 ? (key & 3) << 2 : ((key >> 1) & 1) << 2;
+}
+
+template <int D, int KG>
+__global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_pipe(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
+    int hl, int kvl, int S, int ld_seq, float scale_log2, int B) {
+    constexpr int KC = D / 8;
+    constexpr int NT = D / 32;
+    constexpr int KSTEPS = D / 16;
+    constexpr int BLK = BKV * D;    // bf16 of one K or V block
+    constexpr int GBUF = 4 * BLK;   // per group: K stages 0, 1 and V stages 0, 1
+    constexpr int OROW = KG > 1 ? D + 8 : D;
+    constexpr int MERGE = (KG > 1 ? 4 * NT * 16 * 64 + 2 * 256 : 0) * 2;
+    constexpr int STAGE_O = 4 * 32 * OROW;
+    constexpr int SMEM = cmax(cmax(KG * GBUF, MERGE), STAGE_O);
+    __shared__ __attribute__((aligned(16))) bf16 smem[SMEM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = KG > 1 ? wave >> 2 : 0, qw = KG > 1 ? wave & 3 : wave;
+    bf16* const gbuf = smem + grp * GBUF;
+    const uint32_t gbuf_lds = (uint32_t)(uintptr_t)gbuf;
+    const int h = lane >> 5, col = lane & 31;
+    const int nqb = (S + BQ - 1) / BQ;
+    const int nhb = hl * B;
+    const int rank = blockIdx.x / nhb, hb = blockIdx.x - rank * nhb;
+    const int qb = nqb - 1 - rank;
+    const int head = hb % hl, b = hb / hl;
+    const int kvh = head / (hl / kvl);
+    const int q0 = qb * BQ + qw * 32;
+    const int qme = q0 + col;
+
+    const bf16* Kb = K + ((long long)b * kvl + kvh) * ld_seq * D;
+    const bf16* Vb = V + ((long long)b * kvl + kvh) * ld_seq * D;
+
+    bf16x8 qf[KSTEPS];
+    {
+        const int qrow = min(qme, S - 1);
+        const bf16* qp = Q + (((long long)b * hl + head) * S + qrow) * D + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+    }
+
+    f32x16 oacc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) oacc[i] = (f32x16){};
+    float m_run = -1e30f, l_run = 0.f;
+
+    const int kv_end = min(S, qb * BQ + BQ);
+    const int nkb = (kv_end + BKV - 1) / BKV;
+    const int nit = (nkb + KG - 1) / KG;
+
+    // Direct loads, 1 KB per wave instruction: lane L of instruction i of
+    // wave w fills slot L % KC of row (w NLD + i) RPK + L / KC and reads the
+    // chunk that the row's swizzle puts in that slot.
+    constexpr int NLD = BKV * KC / 256;   // direct loads per wave per block (K or V)
+    constexpr int RPK = 512 / D;          // rows per 1 KB
+    int kdoff[NLD], vdoff[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int row = (qw * NLD + i) * RPK + lane / KC, slot = lane % KC;
+        kdoff[i] = (row * D + kslot<KC>(row, slot) * 8) * 2;
+        vdoff[i] = (row * D + (slot ^ vswz<D>(row)) * 8) * 2;
+    }
+    // block j of this group starts at key (j KG + grp) BKV; rows at or past S
+    // (and whole blocks past it) read as zeros through the resource's extent
+    auto dma = [&](const bf16* base_ptr, const int (&off)[NLD], int j, int buf) {
+        const int k0 = (j * KG + grp) * BKV;
+        const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(BKV, S - k0)) * D * 2);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base_ptr + (long long)min(k0, S) * D), (short)0, bytes, 0x00020000);
+        const uint32_t lds = gbuf_lds + buf * BLK * 2 + qw * NLD * 1024;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) load_lds16(r, off[i], __builtin_amdgcn_readfirstlane(lds + i * 1024));
+    };
+    auto dma_k = [&](int j, int stage) { dma(Kb, kdoff, j, stage); };
+    auto dma_v = [&](int j, int stage) { dma(Vb, vdoff, j, 2 + stage); };
+
+    auto scores = [&](int stage, f32x16(&st)[2]) {
+        const bf16* sK = gbuf + stage * BLK;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[t] = (f32x16){};
+            const int krow = 32 * t + col;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const bf16x8 a = *(const bf16x8*)(sK + krow * D + (kslot<KC>(krow, 2 * kk + h) << 3));
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], st[t], 0, 0, 0);
+            }
+        }
+    };
+    // byte offset of this lane's transposed-read row for tile T of a V stage
+    // (key 16 j + 4 h + r / 4 of the group, + 8 for the second read)
+    const int r16 = lane & 15, gh = (lane >> 4) & 1;
+    const int vkey = 4 * h + (r16 >> 2);
+    int vtoff[NT];
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+        const int c = 4 * T + 2 * gh + ((r16 & 3) >> 1);
+        vtoff[T] = vkey * D * 2 + ((c ^ vswz<D>(vkey)) << 4) + ((r16 & 1) << 3);
+    }
+    // (the pointers derive from the shared array, so the compiler can tell
+    // these reads from the direct loads in flight to the other stages)
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    auto pv = [&](int stage, const bf16x8 (&pb)[BKV / 16]) {
+        const bf16* base = gbuf + (2 + stage) * BLK;
+#pragma unroll
+        for (int j = 0; j < BKV / 16; ++j)
+#pragma unroll
+            for (int T = 0; T < NT; ++T) {
+                const bf16* a0 = base + (vtoff[T] >> 1) + j * 16 * D;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * D));
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j], oacc[T], 0, 0, 0);
+            }
+    };
+
+    // prologue: K of blocks 0 and 1 and V of block 0 in LDS, scores of block
+    // 0 in registers.  Block i loads K of block i+2 into the stage that K of
+    // block i held, so every wave must have read the scores of block 0 first.
+    dma_k(0, 0);
+    dma_k(1, 1);
+    dma_v(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct loads have landed
+    __syncthreads();
+    f32x16 sa[2], sb[2];   // scores of the current and the next block, alternating
+    scores(0, sa);
+    __syncthreads();
+
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    // one key block; LAST is a constant at both call sites, so its branches fold
+    auto block = [&](int it, f32x16(&sc)[2], f32x16(&sn)[2], const bool LAST) __attribute__((always_inline)) {
+        const int k0 = (it * KG + grp) * BKV;
+        if (!LAST) {
+            // the last barrier freed the stages of K of block it and V of block it-1
+            if (it + 2 < nit) dma_k(it + 2, it & 1);
+            dma_v(it + 1, (it + 1) & 1);
+        }
+        if (k0 + BKV - 1 > q0) {   // causal mask where the block reaches past the wave's first query
+            const int lim = qme - k0 - 4 * h;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sc[t][r] = 32 * t + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : sc[t][r];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+        mx = half_max(mx) * scale_log2;
+        if (__any(mx > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) oacc[i] *= alpha;
+        }
+        const float neg_m = -m_run;
+        // scores of the next block (MFMA) under the exponentials of this one (VALU)
+        if (!LAST) scores((it + 1) & 1, sn);
+        float lsum = 0.f;
+        bf16x8 pb[BKV / 16];
+#pragma unroll
+        for (int j = 0; j < BKV / 16; ++j) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                pb[j][p] = f2bf(__builtin_amdgcn_exp2f(fmaf(sc[j >> 1][8 * (j & 1) + p], scale_log2, neg_m)));
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 0, 1), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 2, 3), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 4, 5), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 6, 7), ones, lsum, false);
+        }
+        l_run += lsum;
+        pv(it & 1, pb);
+        if (!LAST) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K of block it+2, V of block it+1 have landed
+            __syncthreads();
+        }
+    };
+    // two blocks per trip, so that the score registers alternate without copies
+    int it = 0;
+    for (; it + 2 < nit; it += 2) {
+        block(it, sa, sb, false);
+        block(it + 1, sb, sa, false);
+    }
+    if (it + 1 < nit) {
+        block(it, sa, sb, false);
+        block(it + 1, sb, sa, true);
+    } else {
+        block(it, sa, sb, true);
+    }
+
+    if constexpr (KG > 1) {
+        float* mo = (float*)smem;
+        float* mm = mo + 4 * NT * 16 * 64;
+        float* ml = mm + 256;
+        __syncthreads();
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mo[((qw * NT + i) * 16 + r) * 64 + lane] = oacc[i][r];
+            mm[qw * 64 + lane] = m_run;
+            ml[qw * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (grp == 0) {
+            const float m1 = mm[qw * 64 + lane], l1 = ml[qw * 64 + lane];
+            const float m = fmaxf(m_run, m1);
+            const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+            l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[i][r] = oacc[i][r] * a0 + mo[((qw * NT + i) * 16 + r) * 64 + lane] * a1;
+        }
+        __syncthreads();
+    } else {
+        __syncthreads();
+    }
+
+    if (grp == 0) {
+        const float l_tot = half_sum(l_run);
+        const float inv = 1.f / l_tot;
+        bf16* sO = smem + qw * 32 * OROW;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dim = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                sO[col * OROW + dim] = f2bf(oacc[i][r] * inv);
+            }
+    }
+    __syncthreads();
+    if (grp == 0) {
+        const bf16* sO = smem + qw * 32 * OROW;
+        const long long ldo = (long long)hl * D;
+#pragma unroll
+        for (int i = 0; i < 32 * KC / 64; ++i) {
+            const int idx = lane + 64 * i;
+            const int qr = idx / KC, dc = idx % KC;
+            const int q = q0 + qr;
+            if (q < S)
+                *(bf16x8*)(O + ((long long)b * S + q) * ldo + head * D + dc * 8) = *(const bf16x8*)(sO + qr * OROW + dc * 8);
+        }
+    }
+}
+
 int g_attn_groups = 0;   // 0: by grid size; 1 or 2: forced
+int g_attn_kernel = 0;   // 0 or 2: pipelined; 1: one LDS stage per key group, two barriers per key block
+
+template <int D, int KG>
+void launch_attn(dim3 grid, hipStream_t st, const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl,
+                 int kvl, int S, int ld_seq, float scale_log2) {
+    if (g_attn_kernel == 1)
+        hipLaunchKernelGGL((attn_prefill_kernel<D, KG>), grid, dim3(256 * KG), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
+                           scale_log2, B);
+    else
+        hipLaunchKernelGGL((attn_prefill_pipe<D, KG>), grid, dim3(256 * KG), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
+                           scale_log2, B);
+}
 
 }  // namespace
 
 void set_attn_groups(int kg) { g_attn_groups = kg; }
+void set_attn_kernel(int k) { g_attn_kernel = k; }
 
 void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int B, int hl, int kvl, int S,
                        int ld_seq, int d, hipStream_t st) {
@@ -329,19 +626,11 @@ void attn_prefill_bf16(const bf16* Q, const bf16* K, const bf16* V, bf16* O, int
     const long long wgs = grid.x;
     const int kg = g_attn_groups ? g_attn_groups : (wgs <= 512 ? 2 : 1);
     if (d == 128) {
-        if (kg == 2)
-            hipLaunchKernelGGL((attn_prefill_kernel<128, 2>), grid, dim3(512), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2, B);
-        else
-            hipLaunchKernelGGL((attn_prefill_kernel<128, 1>), grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2, B);
+        if (kg == 2) launch_attn<128, 2>(grid, st, Q, K, V, O, B, hl, kvl, S, ld_seq, scale_log2);
+        else launch_attn<128, 1>(grid, st, Q, K, V, O, B, hl, kvl, S, ld_seq, scale_log2);
     } else {
-        if (kg == 2)
-            hipLaunchKernelGGL((attn_prefill_kernel<64, 2>), grid, dim3(512), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2, B);
-        else
-            hipLaunchKernelGGL((attn_prefill_kernel<64, 1>), grid, dim3(256), 0, st, Q, K, V, O, hl, kvl, S, ld_seq,
-                               scale_log2, B);
+        if (kg == 2) launch_attn<64, 2>(grid, st, Q, K, V, O, B, hl, kvl, S, ld_seq, scale_log2);
+        else launch_attn<64, 1>(grid, st, Q, K, V, O, B, hl, kvl, S, ld_seq, scale_log2);
     }
 }
 

@@ -1078,6 +1078,12 @@ int tp_tune_set_attn_groups(int kg) {
     return TP_OK;
 }
 
+int tp_tune_set_attn_kernel(int k) {
+    if (k < 0 || k > 2) return TP_E_ARG;
+    set_attn_kernel(k);
+    return TP_OK;
+}
+
 void tp_shard_destroy(tp_shard* s) {
     if (!s) return;
     for (hipEvent_t e : s->ev)

@@ -240,6 +240,7 @@ void attn_f32(const float* Q, const float* K, const float* V, float* O, int B, i
     ++g_launches;
 }
 void set_attn_groups(int) {}
+void set_attn_kernel(int) {}
 void gemv_bf16(const bf16* x, int B, const bf16* gamma, float, const bf16* W, int N, int K, const Epilogue& epi,
                hipStream_t) {
     in_alloc(x, (long long)B * K * 2, "GEMV input");

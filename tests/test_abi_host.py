@@ -173,6 +173,9 @@ def test_tune_hook_range():
     assert lib.tp_tune_set_attn_groups(3) == N.TP_E_ARG
     assert lib.tp_tune_set_attn_groups(-1) == N.TP_E_ARG
     assert lib.tp_tune_set_attn_groups(0) == N.TP_OK
+    assert lib.tp_tune_set_attn_kernel(3) == N.TP_E_ARG
+    assert lib.tp_tune_set_attn_kernel(-1) == N.TP_E_ARG
+    assert lib.tp_tune_set_attn_kernel(0) == N.TP_OK
     assert lib.tp_tune_set_decode_chunk(48) == N.TP_E_ARG
     assert lib.tp_tune_set_decode_chunk(0) == N.TP_OK
 

@@ -263,15 +263,18 @@ def test_bf16_layer_ragged_gqa_two_ranks():
     assert_close(to_np(o), ref["o"].transpose(0, 2, 1, 3).reshape(600, 512), "attention output o", "bf16")
 
 
+@pytest.mark.parametrize("kern", [1, 2])
 @pytest.mark.parametrize("kg", [1, 2])
-@pytest.mark.parametrize("hidden,heads,kv,S", [(1024, 8, 4, 300), (512, 8, 2, 130)])
-def test_attention_key_groups(kg, hidden, heads, kv, S):
+@pytest.mark.parametrize("hidden,heads,kv,S", [(1024, 8, 4, 300), (512, 8, 2, 130), (1024, 8, 2, 1000),
+                                               (512, 4, 4, 64), (1024, 8, 8, 1)])
+def test_attention_key_groups(kern, kg, hidden, heads, kv, S):
     """Prefill attention with one group of waves over every key block and
     with two groups over alternate key blocks whose softmax states merge,
-    forced in turn (head dims 128 and 64, GQA, ragged S), against the
-    oracle's attention output."""
-    from tensor_transformer_layer_tp_amd import set_attn_groups
-    announce(f"attention key groups kg={kg} hidden={hidden} heads={heads}/{kv} S={S}")
+    forced in turn, each on the one-stage kernel (1) and on the pipelined
+    kernel (2): head dims 128 and 64, GQA and MHA, ragged S, one key block, a
+    single token, against the oracle's attention output."""
+    from tensor_transformer_layer_tp_amd import set_attn_groups, set_attn_kernel
+    announce(f"attention kernel {kern} key groups kg={kg} hidden={hidden} heads={heads}/{kv} S={S}")
     t, r, B = 2, 1, 2
     L = Layer(hidden, heads, kv, 2 * hidden, batch=B, seq=S, gamma_noise=True, seed=21)
     ref = O.attn_stage(L.exact["x"], L.W, L.spec, t, r)
@@ -279,12 +282,15 @@ def test_attention_key_groups(kg, hidden, heads, kv, S):
     hl, d = heads // t, hidden // heads
     try:
         set_attn_groups(kg)
+        set_attn_kernel(kern)
         sh.prefill(ATTN, L.dev["x"])
         o = sh.debug_tensor("o", (B * S, hl * d))
         torch.cuda.synchronize()
     finally:
         set_attn_groups(0)
-    assert_close(to_np(o), ref["o"].transpose(0, 2, 1, 3).reshape(B * S, hl * d), f"attention o kg={kg}", "bf16")
+        set_attn_kernel(0)
+    assert_close(to_np(o), ref["o"].transpose(0, 2, 1, 3).reshape(B * S, hl * d),
+                 f"attention o kernel {kern} kg={kg}", "bf16")
 
 
 def test_bf16_head_dim_64_unsharded():
