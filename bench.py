@@ -1035,7 +1035,7 @@ def summarize_mfma(pmc_dir, out_name):
     disp = {}
     for r in rows:
         name = r["Kernel_Name"]
-        if not re.search(r"gemm_\w+_kernel|attn_prefill_kernel", name):
+        if not re.search(r"gemm_\w+_kernel|attn_prefill_(kernel|pipe)", name):
             continue
         d = disp.setdefault((name, r["Dispatch_Id"]),
                             {"name": name, "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
@@ -1052,10 +1052,10 @@ def summarize_mfma(pmc_dir, out_name):
         gf = statistics.mean(x.get("MfmaFlopsBF16", float("nan")) for x in ds) / 1e9
         ghz = statistics.mean(x.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcc / (x["us"] * 1e3) for x in ds)
         m = re.search(r"gemm_\w+_kernel<(?:[^>]*, )?(\d)>", name)
-        label = (re.search(r"(gemm_\w+_kernel<[^>]*>|attn_prefill_kernel\w*)", name) or re.search(r".*", name)).group(0)
-        a = re.search(r"attn_prefill_kernelILi(\d+)ELi(\d+)E", name)
+        label = (re.search(r"(gemm_\w+_kernel<[^>]*>|attn_prefill_\w*)", name) or re.search(r".*", name)).group(0)
+        a = re.search(r"attn_prefill_(kernel|pipe)ILi(\d+)ELi(\d+)E", name)
         if a:
-            label = f"attn_prefill_kernel<{a.group(1)}, {a.group(2)}> (causal GQA attention)"
+            label = f"attn_prefill_{a.group(1)}<{a.group(2)}, {a.group(3)}> (causal GQA attention)"
         if m:
             label += f" ({mode_of.get(m.group(1), '')})"
         md.append(f"| `{label[:90]}` | {len(ds)} | {us:.1f} | {util:.1f} | {gf:.2f} | {ghz:.2f} |")
