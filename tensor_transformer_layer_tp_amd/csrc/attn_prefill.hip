@@ -6,17 +6,22 @@
 // column-parallel split of Q/K/V needs no communication inside attention).
 //
 // Work-group = 4 waves (or 2 x 4, see below) = 128 queries of one (batch,
-// head); each wave owns 32 queries.  Keys stream through LDS in blocks of 64.  The wave computes the
-// transposed score tile S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K block as
-// the A operand from LDS, the wave's Q fragment held in registers as the B
-// operand), so that every lane owns ONE query column: the online-softmax
+// head); each wave owns 32 queries.  Keys stream through LDS in blocks of
+// 64.  The wave computes the transposed score tile S^T = K Q^T
+// (v_mfma_f32_32x32x16_bf16, K block as the A operand from LDS, the wave's Q
+// fragment held in registers as the B operand), so that every lane owns ONE
+// query column: the online-softmax
 // row max / row sum is a per-lane reduction over 16 registers plus one
 // exchange between the two 32-lane halves.  The probabilities are then fed
 // straight from the accumulator registers as the B operand of
-// O^T += V^T P^T; V is stored transposed in LDS with its keys permuted to
-// match the accumulator's register order, so each A-operand fragment is one
-// 16-byte LDS read.  Grouped-query attention maps query head j to KV head
+// O^T += V^T P^T.  Grouped-query attention maps query head j to KV head
 // j / (Hl / Hkvl).
+//
+// Two kernels share this structure.  attn_prefill_pipe (the default) loads K
+// and V straight into two LDS stages each and reads the P·V operand from
+// row-major V with the transposing LDS read; attn_prefill_kernel stages each
+// block through registers into one LDS stage, with V stored transposed and
+// its keys permuted to the accumulator's register order.
 #include "common.h"
 
 namespace tp {
