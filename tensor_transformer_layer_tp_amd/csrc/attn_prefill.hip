@@ -449,8 +449,9 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void attn_prefill_pipe(
         const int c = 4 * T + 2 * gh + ((r16 & 3) >> 1);
         vtoff[T] = vkey * D * 2 + ((c ^ vswz<D>(vkey)) << 4) + ((r16 & 1) << 3);
     }
-    // (the pointers derive from the shared array, so the compiler can tell
-    // these reads from the direct loads in flight to the other stages)
+    // (the compiler cannot tell these reads from the destinations of direct
+    // loads in flight, so it waits for every outstanding one before the
+    // first of them; plain 16-byte reads of the shared array are not held)
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     auto pv = [&](int stage, const bf16x8 (&pb)[BKV / 16]) {
         const bf16* base = gbuf + (2 + stage) * BLK;
