@@ -293,6 +293,26 @@ def test_attention_key_groups(kern, kg, hidden, heads, kv, S):
                  f"attention o kernel {kern} kg={kg}", "bf16")
 
 
+@pytest.mark.parametrize("S", [65, 128, 129, 192, 257])
+@pytest.mark.parametrize("hidden,heads,kv", [(1024, 8, 8), (1024, 8, 2), (1024, 16, 2), (512, 8, 4)])
+def test_attention_block_counts(hidden, heads, kv, S):
+    """The default prefill attention over sequence lengths that give each
+    query block one, two, three or more key blocks per key group (odd and
+    even trip counts of the two-blocks-per-trip loop, ragged last blocks),
+    head dims 128 and 64, MHA and GQA up to four query heads per KV head,
+    against the oracle's attention output."""
+    announce(f"attention block counts hidden={hidden} heads={heads}/{kv} S={S}")
+    t, r, B = 2, 0, 2
+    L = Layer(hidden, heads, kv, 2 * hidden, batch=B, seq=S, gamma_noise=True, seed=31)
+    ref = O.attn_stage(L.exact["x"], L.W, L.spec, t, r)
+    sh = L.shard(t, r)
+    hl, d = heads // t, hidden // heads
+    sh.prefill(ATTN, L.dev["x"])
+    o = sh.debug_tensor("o", (B * S, hl * d))
+    torch.cuda.synchronize()
+    assert_close(to_np(o), ref["o"].transpose(0, 2, 1, 3).reshape(B * S, hl * d), "attention o", "bf16")
+
+
 def test_bf16_head_dim_64_unsharded():
     announce("bf16 layer head_dim 64, t=1, B=1, S=130")
     L = Layer(512, 8, 2, 1024, batch=1, seq=130, gamma_noise=True, seed=2)
