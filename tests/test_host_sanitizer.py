@@ -11,8 +11,8 @@ shards, the reduce calls, the allocation-free entry point, the timer, and a
 failure injected into each device allocation the weight loader, the
 workspace and the caches make (including the second of an E4M3 code/scale
 pair), each followed by a retry and a leak check.  The GPU kernels
-themselves are not part of this build (the parity tests cover them); only
-the host code is instrumented.
+themselves are not compiled into this sanitized executable (the parity
+tests cover them); only the host code is instrumented.
 """
 
 import os
