@@ -850,7 +850,8 @@ __global__ __launch_bounds__(256) void attn_decode_fused(const bf16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Skinny GEMM for small decode batches (2..64 sequences), split over K.
+// Skinny GEMM for small decode batches (2..64 sequences; the shard uses it
+// from 5), split over K.
 //
 // y[b, n] = sum_k W[n, k] x[b, k] with v_mfma_f32_32x32x16_bf16: the weight
 // rows are the A operand (32 rows per tile), the batch the B operand (32

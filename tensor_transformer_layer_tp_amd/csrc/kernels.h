@@ -100,8 +100,9 @@ void kv_to_pages(const bf16* k, const bf16* v, bf16* kpool, bf16* vpool, int B, 
 size_t attn_decode_scratch_bytes(int B, int hl, int kvl, int cap, int d);
 void set_decode_chunk(int ch);   // decode attention positions per chunk: 0 automatic, 16/32/64 forced
 void set_decode_attn_mode(int mode);   // 0 automatic, 1 split kernels + merge launch, 2 fused merge
-// small decode batches (2..64): split-K MFMA projection + epilogue pass; part
-// is fp32 scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
+// small decode batches (2..64; the shard runs 5..64 through it and up to 4
+// through gemv_bf16): split-K MFMA projection + epilogue pass; part is fp32
+// scratch of skinny_scratch_bytes(B, N, K); N and K multiples of 64
 void skinny_bf16(const bf16* x, int B, const bf16* W, int N, int K, float* part, const Epilogue& epi,
                  hipStream_t st);
 size_t skinny_scratch_bytes(int B, int N, int K);

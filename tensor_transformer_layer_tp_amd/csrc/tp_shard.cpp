@@ -267,11 +267,13 @@ int launch_norm(tp_shard* s, const void* x, const void* g, void* out, long long 
     return TP_OK;
 }
 
-// Decode projections stream each weight once.  One sequence: the GEMV kernel,
-// whose threads hold a whole input row in registers (K <= 16384).  2..64
-// sequences: RMSNorm (if any) into the workspace, then the split-K MFMA
-// projection and its epilogue pass.  More sequences take the GEMM path.
-constexpr int kGemvMaxBatch = 1;
+// Decode projections stream each weight once.  Up to four sequences: the
+// GEMV kernel, whose threads hold a whole input row of every sequence in
+// registers (K <= 16384), with the norm and the epilogue fused (one launch per
+// projection).  5..64 sequences: RMSNorm (if any) into the workspace, then the
+// split-K MFMA projection and its epilogue pass.  More sequences take the GEMM
+// path.
+constexpr int kGemvMaxBatch = 4;
 constexpr int kSkinnyMaxBatch = 64;
 constexpr int kGemvMaxK = 16384;
 
