@@ -222,6 +222,43 @@ __global__ __launch_bounds__(T) void gemv_kernel(const bf16* __restrict__ x, con
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         if (!valid[i]) continue;
+        if constexpr (!W8) {
+            // bf16 weights: packed-pair dot products (v_dot2c_f32_bf16) on the
+            // weight words as loaded and the activation words (normalised and
+            // rounded to bf16 first, as the staged activation of a GEMM is)
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                bf16x2 xp[4];
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float f0 = bfbits2f(xv[b][i][0][2 * j]) * rs[b] * bfbits2f(gv[i][0][2 * j]);
+                        const float f1 = bfbits2f(xv[b][i][0][2 * j + 1]) * rs[b] * bfbits2f(gv[i][0][2 * j + 1]);
+                        xp[j] = (bf16x2){f2bf(f0), f2bf(f1)};
+                    }
+                } else {
+                    // (vector elements are copied to scalars before the bit
+                    // casts: a cast of the element expression itself reads
+                    // element 0)
+                    const u32x4 w = __builtin_bit_cast(u32x4, xv[b][i][0]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t wj = w[j];
+                        xp[j] = __builtin_bit_cast(bf16x2, wj);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t wj = wv[r][i][j];
+                        acc[r][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wj), xp[j], acc[r][b],
+                                                                    false);
+                    }
+            }
+            continue;
+        }
         float wf[R][CW];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
