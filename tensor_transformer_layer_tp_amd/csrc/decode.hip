@@ -707,7 +707,10 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const float* __restric
 // sequence) work-group of D * P threads owns the chunks c = part + P i
 // (at most MAXI of them) and loads their maxima, sums and its dim's
 // outputs at once; a block maximum gives the reference M, then each thread
-// weights its chunks by exp2(m_c - M) and the parts meet in LDS.
+// weights its chunks by exp2(m_c - M) and the parts meet in LDS.  The record
+// loads do not wait for the device-resident cache length: they cover every
+// record slot the grid has (`stride`, the capacity's chunk count), and the
+// length, loaded with them, only decides which of the loaded records count.
 template <int D, int P, int MAXI>
 __global__ __launch_bounds__(D * P) void attn_decode_merge(const float* __restrict__ scr, bf16* __restrict__ O, int hl,
                                                           int stride, const int* __restrict__ len_dev, int ld_seq,
@@ -719,17 +722,18 @@ __global__ __launch_bounds__(D * P) void attn_decode_merge(const float* __restri
     const int head = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int dim = tid % D, part = tid / D;
-    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;   // chunks written by the chunk kernel
     const float* st = scr + ((long long)b * hl + head) * stride * (D + 2);
     float mv[MAXI], lv[MAXI], ov[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-        const int c = min(part + P * i, nchunks - 1);   // clamped: every load issued, in bounds
+        const int c = min(part + P * i, stride - 1);   // clamped to the record slots: every load in bounds
         const float* r = st + (long long)c * (D + 2);
         mv[i] = r[D];
         lv[i] = r[D + 1];
         ov[i] = r[dim];
     }
+    // chunks written by the chunk kernel; the others' slots hold older records
+    const int nchunks = (min(*len_dev + 1, ld_seq) + CH - 1) / CH;
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i)
