@@ -398,9 +398,10 @@ int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *l
  * 256x128 (32, 4), 128x384 (32, 4), 128x384 (32, 3); 11..13: register-
  * pipelined 256x256, 256x128 and 256x192 (K-step 64, eight waves); 14..16:
  * producer/consumer 256x256, 256x192 and 256x128 (eight MFMA waves, four
- * load waves).  A configuration that a projection cannot use (the 256x256
- * DMA rings with the rotary epilogue, the two-stage ring also with the GELU
- * and plain-store ones) falls back to the shape-based choice.
+ * load waves); 17: producer/consumer 256x192 with four MFMA waves of 64x192.
+ * A configuration that a projection cannot use (the 256x256 DMA rings and
+ * configuration 17 with the rotary epilogue, the two-stage ring also with
+ * the GELU and plain-store ones) falls back to the shape-based choice.
  * Process-wide, not thread-safe.
  * TP_E_ARG if out of range. */
 int tp_tune_set_gemm_config(int cfg);

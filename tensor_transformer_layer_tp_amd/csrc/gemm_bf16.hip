@@ -741,19 +741,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
 // wait for global memory and never issue a memory-unit instruction.  Two LDS
 // stages: while the MFMA waves read tile kt from one, the producers write
 // tile kt+1 into the other; one barrier per tile hands both over.  Register
-// budget: three waves per SIMD, 168 each (up to 128 accumulators + one set of
-// fragments; two register sets of staged loads on the producers); the rotary
-// epilogue gathers 4 rows at a time to stay inside it.
+// budget with eight MFMA waves: three waves per SIMD, 168 each (up to 128
+// accumulators + one set of fragments; two register sets of staged loads on
+// the producers); the rotary epilogue gathers 4 rows at a time to stay inside
+// it.  With four MFMA waves (WM x WN = 4) two waves share a SIMD, 256
+// registers each: a 64x192 wave tile holds 192 accumulators and reads 0.67
+// fragments per MFMA instead of the 32x192 tile's 1.17.
 template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A, long long lda,
-                                                      const bf16* __restrict__ B, long long ldb, int M, int N,
-                                                      int K, Epilogue epi, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(64 * (WM * WN + 4)) void gemm_ws_kernel(const bf16* __restrict__ A, long long lda,
+                                                                   const bf16* __restrict__ B, long long ldb,
+                                                                   int M, int N, int K, Epilogue epi, int tiles_m,
+                                                                   int tiles_n) {
     constexpr int BK = 64, KK = 4;
+    constexpr int NW = WM * WN;                  // MFMA waves; the four producer waves follow them
     constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
     constexpr int STAGE = (BM + BN) * BK;
     constexpr int RS = 32;                       // rows per producer load step (256 threads x 16 B)
     constexpr int NL = (BM + BN) / RS;           // 16-byte loads per producer thread per tile
-    static_assert(WM * WN == 8 && FN % 2 == 0 && BM % RS == 0 && BN % RS == 0, "tile shape");
+    static_assert((NW == 8 || NW == 4) && FN % 2 == 0 && BM % RS == 0 && BN % RS == 0, "tile shape");
     __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -764,12 +769,12 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
     const int m0 = tm * BM, n0 = tn * BN;
     const int KT = K / BK;
 
-    if (wave >= 8) {
+    if (wave >= NW) {
         // Producer thread p copies 16-byte chunk (p & 7) of rows (p >> 3) + 32 i
         // of the A tile (i < 8) and the B tile (i >= 8).  Rows past M (N) lie
         // outside the tile's buffer resource and read as zeros; tiles past
         // the end read zeros through an empty resource.
-        const int p = tid - 512, srow = p >> 3, skc = p & 7;
+        const int p = tid - 64 * NW, srow = p >> 3, skc = p & 7;
         const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(A + (long long)m0 * lda), (short)0, max(0, min(BM, M - m0)) * (int)lda * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
@@ -924,6 +929,64 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
         // no fragment read of this wave is still in flight when its epilogue
         // writes its part of LDS
         __builtin_amdgcn_s_waitcnt(0xc07f);
+    } else if constexpr (FN > 2) {
+        // Wide wave tiles (64x192): A fragments in two register sets, B in one.
+        // A slice's MFMAs run B-major; the next slice's A fragments are read
+        // during the first column of MFMAs, its B fragment j as soon as column
+        // j's MFMAs have issued, so every read has at least FM * (FN - 1)
+        // MFMAs to land.  Same MFMAs per accumulator, in the same k order.
+        bf16x8 xa[2][FM], xb[FN];
+        auto rd_a = [&](int st, int kk, int i, int set) {
+            const bf16* a_s = smem + st * STAGE + (wm * TM + frow) * BK;
+            xa[set][i] = *(const bf16x8*)(a_s + i * 32 * BK + (swz<8>(frow, 2 * kk + khalf) << 3));
+        };
+        auto rd_b = [&](int st, int kk, int j) {
+            const bf16* b_s = smem + st * STAGE + BM * BK + (wn * TN + frow) * BK;
+            xb[j] = *(const bf16x8*)(b_s + j * 32 * BK + (swz<8>(frow, 2 * kk + khalf) << 3));
+        };
+        // the MFMAs of the slice held in set `cur`, reading slice (st_n, kk_n)
+        auto slice = [&](auto cur_c, int st_n, int kk_n) {
+            constexpr int cur = decltype(cur_c)::value;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[cur][i], xb[j], acc[i][j], 0, 0, 0);
+                    if (j == 0) rd_a(st_n, kk_n, i, cur ^ 1);
+                }
+                rd_b(st_n, kk_n, j);
+            }
+#pragma unroll
+            for (int q = 0; q < FM; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read (A)
+            }
+            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);       // DS read (B 0)
+#pragma unroll
+            for (int q = 1; q < FN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, FM, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read (B q)
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        static_assert(KK == 4, "set parity per slice");
+#pragma unroll
+        for (int i = 0; i < FM; ++i) rd_a(0, 0, i, 0);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) rd_b(0, 0, j);
+        for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                slice(S0{}, st, 1);
+                slice(S1{}, st, 2);
+                slice(S0{}, st, 3);
+                __syncthreads();        // publishes tile kt + st + 1 in the other stage
+                slice(S1{}, st ^ 1, 0); // (past the last tile: a read whose result is unused)
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
     } else {
         for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
@@ -940,7 +1003,7 @@ __global__ __launch_bounds__(768) void gemm_ws_kernel(const bf16* __restrict__ A
     // Every wave, producers included, has passed the loop's last barrier:
     // no LDS read or write of the main loop is still pending, so each MFMA
     // wave may use a private part of the stages for its epilogue.
-    constexpr int RB = 2 * STAGE / 8;
+    constexpr int RB = 2 * STAGE / NW;
     constexpr bool staged = (MODE == EPI_SWIGLU && FM * 32 * (FN * 16 + 8) <= RB) ||
                             (MODE == EPI_F32 && 32 * (FN * 32 + 4) * 2 <= RB);
     if constexpr (staged)
@@ -1058,6 +1121,7 @@ const Cfg kCfgs[] = {
     {256, 256, 1.12f, 1},  // 14 producer/consumer 256x256 BK64, 8 MFMA waves + 4 load waves
     {256, 192, 1.10f, 1},  // 15 producer/consumer 256x192 BK64, 8 MFMA waves of 32x192 + 4 load waves
     {256, 128, 1.02f, 1},  // 16 producer/consumer 256x128 BK64, 8 MFMA waves of 64x64 + 4 load waves
+    {256, 192, 1.13f, 1},  // 17 producer/consumer 256x192 BK64, 4 MFMA waves of 64x192 + 4 load waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -1091,8 +1155,8 @@ void launch_pipe(const Args& a) {
 template <int BM, int BN, int WM, int WN, int MODE>
 void launch_ws(const Args& a) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
-    hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WM, WN, MODE>), dim3(tm * tn), dim3(768), 0, a.st, a.A, a.lda, a.B,
-                       a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
+    hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WM, WN, MODE>), dim3(tm * tn), dim3(64 * (WM * WN + 4)), 0, a.st, a.A,
+                       a.lda, a.B, a.ldb, a.M, a.N, a.K, a.epi, tm, tn);
 }
 
 template <int BM, int BN, int WM, int WN, int MODE>
@@ -1127,16 +1191,21 @@ void launch_cfg(int c, const Args& a) {
         case 13: launch_vgpr<256, 192, 8, 1, MODE>(a); break;
         case 14: launch_ws<256, 256, 2, 4, MODE>(a); break;
         case 15: launch_ws<256, 192, 8, 1, MODE>(a); break;
-        default: launch_ws<256, 128, 4, 2, MODE>(a); break;
+        case 16: launch_ws<256, 128, 4, 2, MODE>(a); break;
+        default:
+            // the rotary epilogue does not fit beside 192 accumulators (usable() keeps it away)
+            if constexpr (MODE != EPI_QKV) launch_ws<256, 192, 4, 1, MODE>(a);
+            break;
     }
 }
 
 // The 256x256 DMA kernels hold 256 accumulators per lane: the two-stage one
 // spills them with the rotary, erf and plain-store epilogues, the four-stage
-// ring with the rotary one.
+// ring with the rotary one.  The four-wave 256x192 producer/consumer tile's
+// 192 accumulators leave no room for the rotary epilogue either.
 bool usable(int c, int mode) {
     if (c == 3 && (mode == EPI_QKV || mode == EPI_GELU || mode == EPI_STORE)) return false;
-    return !(c == 4 && mode == EPI_QKV);
+    return !((c == 4 || c == 17) && mode == EPI_QKV);
 }
 
 // Modelled time of one launch: rounds of 256 tiles (one per CU), each the
@@ -1149,7 +1218,11 @@ constexpr double kLaunchUs = 3.0;
 double model_us(int c, int mode, int M, int N, int K) {
     const Cfg& f = kCfgs[c];
     const long long tiles = (long long)cdiv(M, f.bm) * cdiv(N, f.bn);
-    const double eff = f.eff * ((c >= 3 && c <= 10 && mode == EPI_QKV) ? 0.8 : 1.0);
+    double eff = f.eff * ((c >= 3 && c <= 10 && mode == EPI_QKV) ? 0.8 : 1.0);
+    // the four-wave 256x192 tile beat the eight-wave one only with the SwiGLU
+    // epilogue (7B gate/up 167-168 against 174-186 us); with the fp32 partial
+    // it ran 1-6 % behind the 256x128 and 256x256 tiles
+    if (c == 17 && mode != EPI_SWIGLU) eff = 0.95f;
     // a configuration with `occ` work-groups per CU reaches its rate only with all of them resident: a
     // round is 256 * occ tiles and costs occ tiles' time, however few tiles the last round has
     const long long per_round = 256LL * f.occ;

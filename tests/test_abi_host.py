@@ -247,8 +247,8 @@ def test_gemm_plan_column_splits():
     assert [c for _, c in gemm_plan(8192, 11008, 4096, "swiglu")] == [10240, 768]
     # 70B t=8 Q/K/V projection (B4 S4096)
     assert len(gemm_plan(16384, 1280, 8192, "qkv")) == 2
-    # the 7B t=2 prefill at 2048 tokens: single launches
-    assert len(gemm_plan(2048, 11008, 4096, "swiglu")) == 1
+    # the 7B t=2 prefill at 2048 tokens: single launches, gate/up on the four-wave 256x192 tile
+    assert gemm_plan(2048, 11008, 4096, "swiglu") == [(17, 11008)]
     assert len(gemm_plan(2048, 6144, 4096, "qkv")) == 1
     for M in (1, 128, 300, 2048, 8192, 16384, 524288):
         for N_, K, kind in ((6144, 4096, "qkv"), (12288, 4096, "qkv"), (1280, 8192, "qkv"), (11008, 4096, "swiglu"),
@@ -257,7 +257,9 @@ def test_gemm_plan_column_splits():
             plan = gemm_plan(M, N_, K, kind)
             assert sum(c for _, c in plan) == N_
             assert all(c % 64 == 0 for _, c in plan[:-1])
-            assert all(0 <= cfg < 17 for cfg, _ in plan)
+            assert all(0 <= cfg < 18 for cfg, _ in plan)
+            if kind == "qkv":   # the four-wave 256x192 tile has no room for the rotary epilogue
+                assert all(cfg != 17 for cfg, _ in plan)
     try:
         set_gemm_split(14, 16, 640)
         assert gemm_plan(2048, 11008, 4096, "swiglu") == [(14, 640), (16, 10368)]
