@@ -889,7 +889,7 @@ ROOF_KERNELS = {
 CFG_KERNEL = {11: "gemm_vgpr_kernel<256, 256, 2, 4, ", 12: "gemm_vgpr_kernel<256, 128, 4, 2, ",
               13: "gemm_vgpr_kernel<256, 192, 8, 1, ", 14: "gemm_ws_kernel<256, 256, 2, 4, ",
               15: "gemm_ws_kernel<256, 192, 8, 1, ", 16: "gemm_ws_kernel<256, 128, 4, 2, ",
-              17: "gemm_ws_kernel<256, 192, 4, 1, "}
+              17: "gemm_ws_kernel<256, 192, 4, 1, ", 18: "gemm_ws_kernel<256, 128, 4, 1, "}
 
 
 def roof_patterns(key):

@@ -398,7 +398,8 @@ int tp_shard_timing_read(tp_shard *s, int kernel, double *total_ms, long long *l
  * 256x128 (32, 4), 128x384 (32, 4), 128x384 (32, 3); 11..13: register-
  * pipelined 256x256, 256x128 and 256x192 (K-step 64, eight waves); 14..16:
  * producer/consumer 256x256, 256x192 and 256x128 (eight MFMA waves, four
- * load waves); 17: producer/consumer 256x192 with four MFMA waves of 64x192.
+ * load waves); 17, 18: producer/consumer 256x192 and 256x128 with four MFMA
+ * waves of 64x192 and 64x128.
  * A configuration that a projection cannot use (the 256x256 DMA rings and
  * configuration 17 with the rotary epilogue, the two-stage ring also with
  * the GELU and plain-store ones) falls back to the shape-based choice.

@@ -835,7 +835,7 @@ __global__ __launch_bounds__(64 * (WM * WN + 4)) void gemm_ws_kernel(const bf16*
     // run: into a second set where the register budget allows two (not with
     // 128 accumulators), else into the registers of the current set that its
     // MFMAs have finished with.
-    constexpr bool DB = FM * FN * 16 + 8 * (FM + FN) <= 152;
+    constexpr bool DB = FM * FN * 16 + 8 * (FM + FN) <= (NW == 4 ? 232 : 152);
     bf16x8 fa[DB ? 2 : 1][FM], fb[DB ? 2 : 1][FN];
     auto rd = [&](int st, int kk, int buf) {
         const bf16* a_s = smem + st * STAGE + (wm * TM + frow) * BK;
@@ -1122,6 +1122,7 @@ const Cfg kCfgs[] = {
     {256, 192, 1.10f, 1},  // 15 producer/consumer 256x192 BK64, 8 MFMA waves of 32x192 + 4 load waves
     {256, 128, 1.02f, 1},  // 16 producer/consumer 256x128 BK64, 8 MFMA waves of 64x64 + 4 load waves
     {256, 192, 1.13f, 1},  // 17 producer/consumer 256x192 BK64, 4 MFMA waves of 64x192 + 4 load waves
+    {256, 128, 1.05f, 1},  // 18 producer/consumer 256x128 BK64, 4 MFMA waves of 64x128 + 4 load waves
 };
 constexpr int kNumCfg = sizeof(kCfgs) / sizeof(kCfgs[0]);
 int g_forced_cfg = -1;
@@ -1192,10 +1193,11 @@ void launch_cfg(int c, const Args& a) {
         case 14: launch_ws<256, 256, 2, 4, MODE>(a); break;
         case 15: launch_ws<256, 192, 8, 1, MODE>(a); break;
         case 16: launch_ws<256, 128, 4, 2, MODE>(a); break;
-        default:
+        case 17:
             // the rotary epilogue does not fit beside 192 accumulators (usable() keeps it away)
             if constexpr (MODE != EPI_QKV) launch_ws<256, 192, 4, 1, MODE>(a);
             break;
+        default: launch_ws<256, 128, 4, 1, MODE>(a); break;
     }
 }
 
@@ -1223,6 +1225,9 @@ double model_us(int c, int mode, int M, int N, int K) {
     // epilogue (7B gate/up 167-168 against 174-186 us); with the fp32 partial
     // it ran 1-6 % behind the 256x128 and 256x256 tiles
     if (c == 17 && mode != EPI_SWIGLU) eff = 0.95f;
+    // the four-wave 256x128 tile beat the eight-wave one with the fp32
+    // partial (7B out and down 2-5 % faster), not with the other epilogues
+    if (c == 18 && mode != EPI_F32) eff = 0.95f;
     // a configuration with `occ` work-groups per CU reaches its rate only with all of them resident: a
     // round is 256 * occ tiles and costs occ tiles' time, however few tiles the last round has
     const long long per_round = 256LL * f.occ;
