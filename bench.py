@@ -278,10 +278,14 @@ def copy_ceiling(torch, mib=4096, reps=5):
 
 # ---------------------------------------------------------------- prefill
 
-def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, kv_cap=None):
+def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, kv_cap=None, fused=False):
     """Rank 0's shard plus the buffers of one prefill step.  The other
     ranks' partials are either computed by their own shards once
-    (exact_others) or seeded N(0, 0.1^2) stand-ins (timing only)."""
+    (exact_others) or seeded N(0, 0.1^2) stand-ins (timing only).  With
+    `fused`, each stage's reduce runs in its row-parallel projection's
+    epilogue and a norm kernel follows; otherwise the stage stores its
+    partial and a reduce kernel with the norm fused follows.  Returns the
+    shard, the cache, the step and the other variant's step."""
     from tensor_transformer_layer_tp_amd import ATTN, MLP, PRENORM, Shard, partial_reduce
     B, S = int(x.shape[0]), int(x.shape[1])
     sh = Shard(hidden, heads, kv_heads, ffn, t, 0)
@@ -320,7 +324,7 @@ def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others,
     n1 = sh.norm(1, x)
     torch.cuda.synchronize()
 
-    def step():
+    def step_reduce_norm():
         # ATTN stage on the normalised input, the reduce with the MLP stage's
         # norm, the MLP stage, the reduce with the next layer's input norm
         sh.prefill(ATTN | PRENORM, n1, kv, out=pa[0])
@@ -328,15 +332,28 @@ def prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others,
         sh.prefill(MLP | PRENORM, n2buf, out=pm[0])
         sh.reduce_norm(1, pm, residual=hbuf, out=ybuf, norm_out=n1next)
 
-    return sh, kv, step
+    oth_a, oth_m = [None] + pa[1:], [None] + pm[1:]
+
+    def step_fused():
+        # the same layer with each reduce in the row-parallel projection's
+        # epilogue, then the next stage's norm
+        sh.prefill_reduce(ATTN | PRENORM, n1, oth_a, residual=x, kv=kv, out=hbuf)
+        sh.norm(2, hbuf, out=n2buf)
+        sh.prefill_reduce(MLP | PRENORM, n2buf, oth_m, residual=hbuf, out=ybuf)
+        sh.norm(1, ybuf, out=n1next)
+
+    if fused:
+        return sh, kv, step_fused, step_reduce_norm
+    return sh, kv, step_reduce_norm, step_fused
 
 
-def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, roof_key):
+def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, roof_key, fused=False):
     """Times the rank-0 prefill step; the timed pass brackets only the
     dominant kernel (gate/up GEMM) with events, a second pass brackets
-    every kernel for the per-kernel breakdown."""
+    every kernel for the per-kernel breakdown, a third times the step with
+    the other placement of the reduces (unbracketed)."""
     B, S = int(x.shape[0]), int(x.shape[1])
-    sh, kv, step = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others)
+    sh, kv, step, other = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, exact_others, fused=fused)
     stream = torch.cuda.current_stream()
     dom = "gemm_up"
     for _ in range(args.warmup):
@@ -351,6 +368,9 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
     ms_marked, _ = timed(torch, step, args.steps, 0, stream)
     ktimes = sh.timing_read()
     sh.timing(False)
+    for _ in range(min(args.warmup, 5)):
+        other()
+    ms_other, dist_other = timed(torch, other, args.steps, 0, stream)
     kv.close()
     sh.close()
     gemm, attn = prefill_flops(hidden, heads, kv_heads, ffn, t, B, S)
@@ -377,9 +397,14 @@ def bench_prefill(args, torch, name, hidden, heads, kv_heads, ffn, t, wdev, x, e
         "tflops": round(total / (ms * 1e-3) / 1e12, 2),
         "mfma_frac": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops_per_step": total,
+        # with the reduces in the epilogues, the out and down projections' times include them
+        "gemm_times_include_reduces": fused,
         "gemm_tflops": round(sum(gemm.values()) / (gemm_us * 1e-6) / 1e12, 2),
         "gemm_mfma_frac": round(sum(gemm.values()) / (gemm_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_all_kernels_bracketed": round(ms_marked, 4),
+        "reduce_placement": ("in the row-parallel projections' epilogues, then a norm kernel" if fused
+                             else "a reduce kernel with the next norm fused, after each stage"),
+        ("ms_per_step_reduce_kernel" if fused else "ms_per_step_reduce_in_epilogue"): round(ms_other, 4),
         "kernels": {k: rounded(v) for k, v in kern.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -635,7 +660,7 @@ def run_70b(args, torch):
     pre = bench_prefill(args, torch,
                         "70b-t8-prefill: rank 0 of a 70B-shaped GQA layer split t=8 (hidden 8192, 8 of 64 query "
                         "heads + 1 of 8 KV heads x 128, SwiGLU 3584 of 28672), bf16, batch 4 x seq 4096, causal",
-                        w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, x, False, "gemm_up_70b_t8")
+                        w.hidden, w.heads, w.kv_heads, w.ffn, w.tp, wdev, x, False, "gemm_up_70b_t8", fused=True)
     del x
     dec = None
     if not args.no_decode:
@@ -689,7 +714,7 @@ def sweep_point(args, torch, wdev, hidden, heads, kv_heads, ffn, t, B, S):
     stream = torch.cuda.current_stream()
     x = synth.draw_normal_device((B, S, hidden), 1000 + B * 10000 + S)
     extra = 16                                   # decode steps the caches leave room for
-    sh, kv, step = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, False, kv_cap=S + extra)
+    sh, kv, step, _ = prefill_stack(torch, hidden, heads, kv_heads, ffn, t, wdev, x, False, kv_cap=S + extra)
     step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1171,8 +1196,9 @@ def main():
         config = {
             "workload": "70b-t8-prefill: rank 0 of a 70B-shaped GQA layer split t=8 (hidden 8192, 8 of 64 query heads "
                         "+ 1 of 8 KV heads x 128, SwiGLU 3584 of 28672, RMSNorm, RoPE), bf16, batch 4 x seq 4096, "
-                        "causal; step = ATTN stage + reduce of 8 partials with the MLP norm + MLP stage + reduce of "
-                        "8 partials with the next layer's input norm",
+                        "causal; step = ATTN stage ending in the reduce of 8 partials (in the out projection's "
+                        "epilogue) + the MLP norm + MLP stage ending in the reduce of 8 partials (in the down "
+                        "projection's epilogue) + the next layer's input norm",
             "global_batch": 4, "seq_len": 4096, "parallelism": "tp8 shard (rank 0) on 1 GPU",
         }
     else:
@@ -1199,9 +1225,11 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random-init)",
         "config": config,
     }
-    for k in ("step_ms", "mfma_frac", "flops_per_step", "gemm_tflops", "gemm_mfma_frac",
-              "ms_per_step_all_kernels_bracketed", "kernels", "clock", "roofline"):
-        line[k] = head[k]
+    for k in ("step_ms", "mfma_frac", "flops_per_step", "gemm_times_include_reduces", "gemm_tflops",
+              "gemm_mfma_frac", "ms_per_step_all_kernels_bracketed", "reduce_placement", "ms_per_step_reduce_kernel",
+              "ms_per_step_reduce_in_epilogue", "kernels", "clock", "roofline"):
+        if k in head:
+            line[k] = head[k]
     line["hbm_copy_GBps"] = copy_ceiling(torch)
     if big is not None and small is not None:
         line["prefill_7b"] = small[0]

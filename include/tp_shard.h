@@ -260,6 +260,35 @@ int tp_shard_forward_decode(tp_shard *s, int stage, const void *x, int batch,
 int tp_shard_forward_decode_noalloc(tp_shard *s, int stage, const void *x, int batch,
                                     tp_kv *kv, float *partial, void *stream);
 
+/* tp_shard_forward_prefill_reduce -- tp_shard_forward_prefill followed by
+ * tp_partial_reduce of its result with the other ranks' partials, as one
+ * call.  Each stage of a layer ends with the all-reduce of the row-parallel
+ * partials, and the next stage cannot start before it (byteledger "Tensor
+ * Parallelism: Splitting One Layer Across GPUs", "Communication is the
+ * constraint"; undercodenews post 110319, "the Original": the all-reduce
+ * follows the row-parallel output projection and the FFN's second linear).
+ * Here the sum is folded into the epilogue of the stage's row-parallel
+ * projection (bf16 shards with tp_degree <= 8), so this rank's partial is
+ * never stored; otherwise the partial goes to the workspace and the reduce
+ * runs after it.
+ *   out[i] = (sum_{r<t} P_r[i]) + residual[i], in rank order in fp32, then
+ *   stored in the shard's dtype (bf16 rounds to nearest even), where
+ *   P_rank is this call's own partial and P_r = partials[r] otherwise.
+ * The result equals tp_shard_forward_prefill + tp_partial_reduce bit for bit.
+ *   partials: HOST array of tp_degree device pointers, each [batch, seq,
+ *     hidden] fp32, 16-byte aligned; entry `rank` is not read (may be NULL);
+ *     a NULL entry for another rank (a lost rank) returns TP_E_ARG.
+ *   residual: [batch, seq, hidden] in the shard's dtype, or NULL for none;
+ *     may alias out.
+ *   out: [batch, seq, hidden] in the shard's dtype; must not overlap x or
+ *     another rank's partial (TP_E_ARG).
+ * The next stage's norm is not applied (the stage that follows normalises
+ * its input unless called with TP_STAGE_PRENORM).  Stages, cache handling
+ * and errors as tp_shard_forward_prefill. */
+int tp_shard_forward_prefill_reduce(tp_shard *s, int stage, const void *x, int batch, int seq, tp_kv *kv,
+                                    const float *const *partials, const void *residual, void *out,
+                                    void *stream);
+
 /* tp_shard_forward_decode_reduce -- tp_shard_forward_decode followed by
  * tp_partial_reduce of its result with the other ranks' partials, as one
  * call.  Each decode step of a layer ends both stages with the all-reduce of

@@ -212,6 +212,29 @@ class Shard:
             _dev(out, "partial", torch.float32, (B, S, self.hidden)), _stream(stream)), "tp_shard_forward_prefill")
         return out
 
+    def prefill_reduce(self, stage: int, x: torch.Tensor, partials, residual: torch.Tensor | None = None,
+                       kv: KVCache | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """One prefill stage and the reduce of its partial with the other ranks'
+        ``partials`` (a list of ``tp`` fp32 [B, S, hidden] tensors; entry ``rank``
+        is not read and may be None), plus ``residual``: returns the reduced
+        [B, S, hidden] in the shard's dtype."""
+        if x.dim() != 3 or x.shape[2] != self.hidden:
+            raise ValueError("x must be [batch, seq, hidden]")
+        B, S = int(x.shape[0]), int(x.shape[1])
+        if len(partials) != self.tp:
+            raise ValueError("partials must hold one entry per rank")
+        shape = (B, S, self.hidden)
+        ptrs = (C.c_void_p * self.tp)()
+        for r, p in enumerate(partials):
+            ptrs[r] = None if (p is None or r == self.rank) else _dev(p, f"partials[{r}]", torch.float32, shape).value
+        if out is None:
+            out = torch.empty(shape, dtype=self.torch_dtype, device=x.device)
+        res = None if residual is None else _dev(residual, "residual", self.torch_dtype, shape)
+        N.check(N.lib().tp_shard_forward_prefill_reduce(
+            self._h, stage, _dev(x, "x", self.torch_dtype), B, S, kv._h if kv is not None else None, ptrs, res,
+            _dev(out, "out", self.torch_dtype, shape), _stream(stream)), "tp_shard_forward_prefill_reduce")
+        return out
+
     def decode(self, stage: int, x: torch.Tensor, kv: KVCache | None = None, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
         """x [B, hidden] (one token per sequence) -> fp32 partial [B, hidden]."""

@@ -45,6 +45,8 @@ SIGNATURES = [
     ("tp_kv_get_len", C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
     ("tp_shard_forward_prefill", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
                                            C.c_void_p, C.c_void_p]),
+    ("tp_shard_forward_prefill_reduce", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
+                                                  C.POINTER(C.c_void_p), C.c_void_p, C.c_void_p, C.c_void_p]),
     ("tp_shard_forward_decode", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                                           C.c_void_p]),
     ("tp_shard_forward_decode_noalloc", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p,

@@ -63,6 +63,48 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The all-reduce's sum in a row-parallel projection's epilogue (EPI_SUM):
+// h = (sum over ranks, in rank order, of the partials) + residual at the W
+// consecutive elements from element offset `off` of the [M, ldo] partials,
+// with this projection's own values in slot `self` -- the order and rounding
+// of the reduce kernel.  The other ranks' partials are read once
+// (non-temporal); the residual is added only when present, so that a -0 sum
+// stays -0.
+template <int W>
+__device__ __forceinline__ void sum_ranks(const SumDest& sd, long long off, float (&v)[W]) {
+    float p[kSumMaxRanks][W];
+#pragma unroll
+    for (int j = 0; j < kSumMaxRanks; ++j) {
+        if (j < sd.t && j != sd.self) {
+            if constexpr (W == 4) {
+                const f32x4 q = __builtin_nontemporal_load((const f32x4*)(sd.p[j] + off));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[j][e] = q[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < W; ++e) p[j][e] = __builtin_nontemporal_load(sd.p[j] + off + e);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < W; ++e) p[j][e] = v[e];
+        }
+    }
+    float r[W];
+    if (sd.residual != nullptr) {
+#pragma unroll
+        for (int e = 0; e < W; ++e) r[e] = bf2f(sd.residual[off + e]);
+    }
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+        float a = p[0][e];
+#pragma unroll
+        for (int j = 1; j < kSumMaxRanks; ++j)
+            if (j < sd.t) a += p[j][e];
+        if (sd.residual != nullptr) a += r[e];
+        v[e] = a;
+    }
+}
+
 // Write the accumulator tile of one wave.  acc[i][j][r] sits at row
 // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of MFMA tile (i, j).
 template <int FM, int FN, int MODE, int QB = 16>
@@ -114,6 +156,23 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
                     const float g = acc[i][2 * p][r], u = acc[i][2 * p + 1][r];
                     if (row < M && gcol < N)
                         o[(long long)row * epi.ldo + ((cb + gcol) >> 1) + col_in] = f2bf(silu_f(g) * u);
+                }
+    } else if constexpr (MODE == EPI_SUM) {
+        bf16* o = (bf16*)epi.out;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wrow0 + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
+                    const int col = wcol0 + j * 32 + col_in;
+                    if (row < M && col < N) {
+                        const long long off = (long long)row * epi.ldo + cb + col;
+                        float v[1] = {acc[i][j][r]};
+                        sum_ranks<1>(epi.sum, off, v);
+                        o[off] = f2bf(v[0]);
+                    }
                 }
     } else {  // MODE == EPI_QKV
         // EPI_QKV: the 64-column group at gcol holds dims (i1, i1 + d/2) of one
@@ -240,7 +299,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], const Epilogue& 
 template <int FM, int FN, int MODE, int RB>
 __device__ __forceinline__ void epilogue_staged(f32x16 (&acc)[FM][FN], const Epilogue& epi, int lane, int wrow0,
                                                 int wcol0, int M, int N, bf16* sreg) {
-    static_assert(MODE == EPI_SWIGLU || MODE == EPI_F32, "staged epilogue modes");
+    static_assert(MODE == EPI_SWIGLU || MODE == EPI_F32 || MODE == EPI_SUM, "staged epilogue modes");
     const int col_in = lane & 31;
     const int row_in = 4 * (lane >> 5);
     const int cb = epi.col0;
@@ -288,11 +347,26 @@ __device__ __forceinline__ void epilogue_staged(f32x16 (&acc)[FM][FN], const Epi
                 const int rl = c / CPR, ch = c % CPR;
                 const int row = wrow0 + i * 32 + rl;
                 const int col = wcol0 + ch * 4;
-                // non-temporal: the partial is read once, by the reduce that follows,
-                // which then finds no dirty lines of it to write back from L2
-                if (row < M && col < N)
-                    __builtin_nontemporal_store(*(const u32x4_t*)(sf + rl * TNP + ch * 4),
-                                                (u32x4_t*)(o + (long long)row * epi.ldo + cb + col));
+                if constexpr (MODE == EPI_SUM) {
+                    // the reduce of the ranks' partials, stored as 4 bf16
+                    if (row < M && col < N) {
+                        const long long off = (long long)row * epi.ldo + cb + col;
+                        const f32x4 a = *(const f32x4*)(sf + rl * TNP + ch * 4);
+                        float v[4] = {a[0], a[1], a[2], a[3]};
+                        sum_ranks<4>(epi.sum, off, v);
+                        uint32_t w[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e)
+                            w[e] = (uint32_t)f2bf_bits(v[2 * e]) | ((uint32_t)f2bf_bits(v[2 * e + 1]) << 16);
+                        *(uint2*)((bf16*)epi.out + off) = make_uint2(w[0], w[1]);
+                    }
+                } else {
+                    // non-temporal: the partial is read once, by the reduce that follows,
+                    // which then finds no dirty lines of it to write back from L2
+                    if (row < M && col < N)
+                        __builtin_nontemporal_store(*(const u32x4_t*)(sf + rl * TNP + ch * 4),
+                                                    (u32x4_t*)(o + (long long)row * epi.ldo + cb + col));
+                }
             }
         }
     }
@@ -1005,7 +1079,7 @@ __global__ __launch_bounds__(64 * (WM * WN + 4)) void gemm_ws_kernel(const bf16*
     // wave may use a private part of the stages for its epilogue.
     constexpr int RB = 2 * STAGE / NW;
     constexpr bool staged = (MODE == EPI_SWIGLU && FM * 32 * (FN * 16 + 8) <= RB) ||
-                            (MODE == EPI_F32 && 32 * (FN * 32 + 4) * 2 <= RB);
+                            ((MODE == EPI_F32 || MODE == EPI_SUM) && 32 * (FN * 32 + 4) * 2 <= RB);
     if constexpr (staged)
         epilogue_staged<FM, FN, MODE, RB>(acc, epi, lane, m0 + wm * TM, n0 + wn * TN, M, N, smem + wave * RB);
     else
@@ -1227,7 +1301,7 @@ double model_us(int c, int mode, int M, int N, int K) {
     if (c == 17 && mode != EPI_SWIGLU) eff = 0.95f;
     // the four-wave 256x128 tile beat the eight-wave one with the fp32
     // partial (7B out and down 2-5 % faster), not with the other epilogues
-    if (c == 18 && mode != EPI_F32) eff = 0.95f;
+    if (c == 18 && mode != EPI_F32 && mode != EPI_SUM) eff = 0.95f;
     // a configuration with `occ` work-groups per CU reaches its rate only with all of them resident: a
     // round is 256 * occ tiles and costs occ tiles' time, however few tiles the last round has
     const long long per_round = 256LL * f.occ;
@@ -1317,6 +1391,7 @@ void gemm_bf16(const bf16* A, long long lda, const bf16* B, long long ldb, int M
             case EPI_QKV: launch_cfg<EPI_QKV>(p.cfg[i], a); break;
             case EPI_SWIGLU: launch_cfg<EPI_SWIGLU>(p.cfg[i], a); break;
             case EPI_GELU: launch_cfg<EPI_GELU>(p.cfg[i], a); break;
+            case EPI_SUM: launch_cfg<EPI_SUM>(p.cfg[i], a); break;
             default: launch_cfg<EPI_STORE>(p.cfg[i], a); break;
         }
     }

@@ -608,26 +608,75 @@ int tp_kv_get_len(const tp_kv* kv, int* len) {
     return v[1] ? TP_E_KV_FULL : TP_OK;
 }
 
-int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv, float* partial,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The all-reduce's sum of a fused-sum call: the t ranks' partials (slot
+// `self` unused), the residual and the reduced output.
+struct FuseSum {
+    const float* const* parts;
+    const void* residual;
+    void* out;
+};
+
+// Epilogue of a row-parallel projection whose all-reduce sum is folded in.
+Epilogue sum_epilogue(const tp_shard* s, const FuseSum& f) {
+    Epilogue e{};
+    e.mode = EPI_SUM;
+    e.out = f.out;
+    e.ldo = s->hidden;
+    for (int r = 0; r < kSumMaxRanks; ++r) e.sum.p[r] = r < s->t && r != s->rank ? f.parts[r] : nullptr;
+    e.sum.residual = (const bf16*)f.residual;
+    e.sum.t = s->t;
+    e.sum.self = s->rank;
+    return e;
+}
+
+// One prefill stage.  With `fuse`, the stage's row-parallel projection ends
+// in the all-reduce's sum: in its epilogue (bf16 shards, up to kSumMaxRanks
+// ranks), else through this rank's partial in the workspace and a reduce.
+int prefill_stage(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv, float* partial,
+                  hipStream_t st, const FuseSum* fuse) {
     const bool prenorm = (stage & TP_STAGE_PRENORM) != 0;
     stage &= ~TP_STAGE_PRENORM;
-    if (!s || !x || !partial || batch <= 0 || seq <= 0) return TP_E_ARG;
     if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return TP_E_ARG;
-    if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
     if (!s->loaded) return TP_E_STATE;
     const long long T = (long long)batch * seq;
     if (T > INT32_MAX / 2) return TP_E_ARG;
-    hipStream_t st = (hipStream_t)stream;
     if (stage == TP_STAGE_MLP && kv) return TP_E_ARG;
     if (stage == TP_STAGE_ATTN && kv) {
         if (kv->batch != batch || kv->dtype != s->o.dtype || kv->kvl != s->kvl) return TP_E_ARG;
         if (seq > kv->max_seq) return TP_E_KV_FULL;
     }
     if (s->o.dtype == TP_F32 && stage == TP_STAGE_ATTN && seq > 16000) return TP_E_ARG;
+    const bool bf = s->o.dtype == TP_BF16;
+    const bool sum_epi = fuse && bf && s->t <= kSumMaxRanks;
     Layout L = layout(s, T, 0, 0);
+    if (fuse && !sum_epi) {   // this rank's partial goes to the workspace, then the reduce
+        L.part = L.total;
+        L.total += al((size_t)T * s->hidden * sizeof(float));
+    }
     TRY(ensure_ws(s, L.total, st));
     char* ws = s->ws;
+    if (fuse && !sum_epi) partial = (float*)(ws + L.part);
+    // the stage's row-parallel projection: an fp32 partial, or the sum folded in
+    auto row_parallel = [&](const void* A, int K, const void* W, LenUpdate len) -> int {
+        if (!sum_epi) {
+            TRY(launch_proj(s, A, T, K, W, s->hidden, EPI_F32, partial, s->hidden, st, len));
+            if (!fuse) return TP_OK;
+            const float* ptrs[64];
+            for (int r = 0; r < s->t; ++r) ptrs[r] = r == s->rank ? partial : fuse->parts[r];
+            partial_reduce(ptrs, s->t, fuse->residual, fuse->out, T * s->hidden, bf, st);
+            LAUNCH_CHECK("partial_reduce");
+            return TP_OK;
+        }
+        Epilogue e = sum_epilogue(s, *fuse);
+        e.len = len;
+        gemm_bf16((const bf16*)A, K, (const bf16*)W, K, (int)T, s->hidden, K, e, st);
+        LAUNCH_CHECK("projection with the reduce");
+        return TP_OK;
+    };
     s->dbg_base = ws;
     s->off_n = L.n;
     s->off_o = L.o;
@@ -673,8 +722,8 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         }
         {
             KTimer kt(s, TP_K_GEMM_OUT, st);
-            TRY(launch_proj(s, ws + L.o, T, s->hl * s->d, s->w_o, s->hidden, EPI_F32, partial, s->hidden, st,
-                            kv ? LenUpdate{kv->dlen, seq, 0, kv->dlen + 1} : LenUpdate{nullptr, 0, 0, nullptr}));
+            TRY(row_parallel(ws + L.o, s->hl * s->d, s->w_o,
+                             kv ? LenUpdate{kv->dlen, seq, 0, kv->dlen + 1} : LenUpdate{nullptr, 0, 0, nullptr}));
         }
         if (kv) kv->len = seq;
         s->attn_seen = true;
@@ -691,23 +740,45 @@ int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, i
         }
         {
             KTimer kt(s, TP_K_GEMM_DOWN, st);
-            TRY(launch_proj(s, ws + L.act, T, s->fl, s->w_down, s->hidden, EPI_F32, partial, s->hidden, st));
+            TRY(row_parallel(ws + L.act, s->fl, s->w_down, LenUpdate{nullptr, 0, 0, nullptr}));
         }
     }
     return TP_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int tp_shard_forward_prefill(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv, float* partial,
+                             void* stream) {
+    if (!s || !x || !partial || batch <= 0 || seq <= 0) return TP_E_ARG;
+    if (!aligned16(x) || !aligned16(partial)) return TP_E_ARG;
+    return prefill_stage(s, stage, x, batch, seq, kv, partial, (hipStream_t)stream, nullptr);
+}
+
+int tp_shard_forward_prefill_reduce(tp_shard* s, int stage, const void* x, int batch, int seq, tp_kv* kv,
+                                    const float* const* partials, const void* residual, void* out, void* stream) {
+    if (!s || !x || !partials || !out || batch <= 0 || seq <= 0) return TP_E_ARG;
+    for (int r = 0; r < s->t; ++r)
+        if (r != s->rank && (!partials[r] || !aligned16(partials[r]))) return TP_E_ARG;
+    if (!aligned16(x) || !aligned16(out) || (residual && !aligned16(residual))) return TP_E_ARG;
+    // out must not overlap the stage's input or any other rank's partial
+    const size_t n = (size_t)batch * seq * s->hidden;
+    const uintptr_t xb = (uintptr_t)x, ob = (uintptr_t)out, oe = ob + n * s->esz;
+    if (xb < oe && ob < xb + n * s->esz) return TP_E_ARG;
+    for (int r = 0; r < s->t; ++r)
+        if (r != s->rank) {
+            const uintptr_t pb = (uintptr_t)partials[r];
+            if (pb < oe && ob < pb + n * sizeof(float)) return TP_E_ARG;
+        }
+    const FuseSum f{partials, residual, out};
+    return prefill_stage(s, stage, x, batch, seq, kv, nullptr, (hipStream_t)stream, &f);
+}
+
 }  // extern "C"
 
 namespace {
-
-// The all-reduce's sum of a fused-sum decode call: the t ranks' partials
-// (slot `self` unused), the residual and the reduced output.
-struct FuseSum {
-    const float* const* parts;
-    const void* residual;
-    void* out;
-};
 
 // One decode stage over the workspace at `base`: the library's own workspace
 // (grown on demand) or, for the allocation-free entry point, the device's

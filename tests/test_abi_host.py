@@ -141,6 +141,39 @@ def test_decode_reduce_argument_and_state_errors():
         lib.tp_shard_destroy(h)
 
 
+def test_prefill_reduce_argument_and_state_errors():
+    """tp_shard_forward_prefill_reduce validates on the host before any
+    device call: missing pointers, a lost other rank, misalignment and an
+    output overlapping the input or another rank's partial are argument
+    errors; a shard without weights is a state error."""
+    lib = N.lib()
+    h = C.c_void_p()
+    assert lib.tp_shard_create(4096, 32, 8, 11008, 2, 1, None, C.byref(h)) == N.TP_OK
+    x, out, p0 = 0x1000000, 0x2000000, 0x3000000   # 16 tokens of 4096 bf16 = 128 KB, fp32 partials 256 KB
+    parts = (C.c_void_p * 2)(p0, None)              # rank 1's own slot may be NULL
+    f = lib.tp_shard_forward_prefill_reduce
+    M = N.TP_STAGE_MLP
+    try:
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(out), None) == N.TP_E_STATE
+        assert f(h, M, C.c_void_p(x), 1, 16, None, None, None, C.c_void_p(out), None) == N.TP_E_ARG
+        lost = (C.c_void_p * 2)(None, p0)           # rank 0's partial missing
+        assert f(h, M, C.c_void_p(x), 1, 16, None, lost, None, C.c_void_p(out), None) == N.TP_E_ARG
+        mis = (C.c_void_p * 2)(p0 + 4, None)
+        assert f(h, M, C.c_void_p(x), 1, 16, None, mis, None, C.c_void_p(out), None) == N.TP_E_ARG
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(out + 8), None) == N.TP_E_ARG
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, C.c_void_p(x + 2), C.c_void_p(out), None) == N.TP_E_ARG
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, None, None) == N.TP_E_ARG
+        assert f(h, M, C.c_void_p(x), 1, 0, None, parts, None, C.c_void_p(out), None) == N.TP_E_ARG
+        # out overlapping x (16 x 4096 bf16 = 128 KB) or rank 0's partial (256 KB)
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(x + 65536), None) == N.TP_E_ARG
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(p0 + 196608), None) == N.TP_E_ARG
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(p0 + 262144), None) == N.TP_E_STATE
+        assert f(h, M, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(x + 131072), None) == N.TP_E_STATE
+        assert f(h, 7, C.c_void_p(x), 1, 16, None, parts, None, C.c_void_p(out), None) == N.TP_E_ARG
+    finally:
+        lib.tp_shard_destroy(h)
+
+
 def test_partial_reduce_argument_errors():
     lib = N.lib()
     fake = 0x10000

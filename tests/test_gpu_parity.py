@@ -578,6 +578,69 @@ def test_decode_reduce_graph_replay(B):
     del graph
 
 
+@pytest.mark.parametrize("dtype,tp,r,res,cfg", [
+    ("bf16", 2, 1, True, None),        # the planner's tiles (staged epilogue), own slot last
+    ("bf16", 8, 0, True, None),        # eight ranks, own slot first
+    ("bf16", 4, 2, False, None),       # no residual
+    ("bf16", 2, 0, True, 1),           # register-staged 128x128 tile: the per-element epilogue
+    ("bf16", 2, 1, True, 14),          # producer/consumer 256x256
+    ("bf16", 2, 1, True, 15),          # producer/consumer 256x192, eight MFMA waves
+    ("bf16", 2, 1, True, 17),          # producer/consumer 256x192, four MFMA waves
+    ("bf16", 2, 1, True, 18),          # producer/consumer 256x128, four MFMA waves
+    ("bf16", 2, 1, True, "split"),     # two launches over column ranges (the second at column 640)
+    ("f32", 2, 1, True, None),         # fp32 shard: workspace partial, then the reduce
+])
+def test_prefill_reduce_equals_two_calls(dtype, tp, r, res, cfg):
+    """tp_shard_forward_prefill_reduce against tp_shard_forward_prefill
+    followed by tp_partial_reduce with the same other-rank partials: h and y
+    bit for bit and the caches bit for bit, for both stages and on a ragged
+    token count; h also against the oracle's reduce of the oracle's partial
+    and the same other-rank partials."""
+    from tensor_transformer_layer_tp_amd import set_gemm_config, set_gemm_split
+    announce(f"prefill with the reduce folded in: {dtype} t={tp} rank {r} residual={res} tiles={cfg}")
+    hid, B, S = 1024, 2, 150
+    L = Layer(hid, 16, 8, 4096, dtype=dtype, batch=B, seq=S, gamma_noise=True, seed=61)
+    sh_a, sh_b = L.shard(tp, r), L.shard(tp, r)
+    kv_a, kv_b = sh_a.kv_cache(B, S), sh_b.kv_cache(B, S)
+    x = L.dev["x"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    oth_a = [torch.randn((B, S, hid), generator=g, device="cuda") for _ in range(tp)]
+    oth_m = [torch.randn((B, S, hid), generator=g, device="cuda") for _ in range(tp)]
+    resid = (lambda t: t) if res else (lambda t: None)
+    try:
+        if cfg == "split":
+            set_gemm_split(14, 16, 640)
+        elif cfg is not None:
+            set_gemm_config(cfg)
+        pa = sh_a.prefill(ATTN, x, kv_a)
+        h_ref = partial_reduce([pa if j == r else oth_a[j] for j in range(tp)], residual=resid(x), dtype=dtype)
+        pm = sh_a.prefill(MLP, h_ref)
+        y_ref = partial_reduce([pm if j == r else oth_m[j] for j in range(tp)], residual=resid(h_ref), dtype=dtype)
+        h = sh_b.prefill_reduce(ATTN, x, [None if j == r else oth_a[j] for j in range(tp)], residual=resid(x),
+                                kv=kv_b)
+        y = sh_b.prefill_reduce(MLP, h, [None if j == r else oth_m[j] for j in range(tp)], residual=resid(h))
+        torch.cuda.synchronize()
+    finally:
+        set_gemm_config(-1)
+        set_gemm_split(0, 0, 0)
+    assert torch.equal(h, h_ref), "h differs from prefill + partial_reduce"
+    assert torch.equal(y, y_ref), "y differs from prefill + partial_reduce"
+    ka, va = kv_a.read()
+    kb, vb = kv_b.read()
+    torch.cuda.synchronize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+    assert kv_b.length == S
+    ref = O.attn_stage(L.exact["x"], L.W, L.spec, tp, r)
+    parts = [ref["partial"] if j == r else to_np(oth_a[j]) for j in range(tp)]
+    resid_np = L.exact["x"] if res else np.zeros((B, S, hid))
+    assert_close(to_np(h), O.reduce(parts, resid_np, L.spec), "fused h vs the oracle's reduce", dtype)
+    refm = O.mlp_stage(to_np(h), L.W, L.spec, tp, r)
+    parts = [refm["partial"] if j == r else to_np(oth_m[j]) for j in range(tp)]
+    resid_np = to_np(h) if res else np.zeros((B, S, hid))
+    assert_close(to_np(y), O.reduce(parts, resid_np, L.spec), "fused y vs the oracle's reduce", dtype)
+
+
 @pytest.mark.parametrize("B", [1, 3, 70])   # GEMV, split-K and GEMM projection paths
 def test_decode_graph_replay(B):
     """A decode step (ATTN + MLP stage) captured in a HIP graph and replayed
