@@ -169,6 +169,27 @@ void flow(const Shape& sh, int dtype, int act, int fp8) {
     EXPECT_RC(tp_shard_forward_prefill(s, TP_STAGE_ATTN | TP_STAGE_PRENORM, x.p, B, S, nullptr, part.as<float>(),
                                        nullptr), TP_OK);
     EXPECT_RC(tp_shard_forward_prefill(s, TP_STAGE_MLP, x.p, B, S, nullptr, part.as<float>(), nullptr), TP_OK);
+    // prefill with the reduce folded in: the GEMM's sum epilogue (bf16), or
+    // the workspace partial and a reduce (fp32 shards)
+    {
+        const float* others[2] = {part.as<float>(), part2.as<float>()};
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_ATTN, x.p, B, S, kv, others, x.p, out.p, nullptr),
+                  TP_OK);
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_MLP | TP_STAGE_PRENORM, out.p, B, S, nullptr, others,
+                                                  out.p, nout.p, nullptr), TP_OK);
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_MLP, out.p, B, S, nullptr, others, nullptr, nout.p,
+                                                  nullptr), TP_OK);
+        const float* lost_other[2] = {sh.rank == 0 ? part.as<float>() : nullptr,
+                                      sh.rank == 1 ? part.as<float>() : nullptr};
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_MLP, out.p, B, S, nullptr, lost_other, out.p, nout.p,
+                                                  nullptr), TP_E_ARG);   // the other rank's partial is missing
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_MLP, out.p, B, S, nullptr, others, out.p,
+                                                  out.as<char>() + 64, nullptr), TP_E_ARG);   // out overlaps x
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_MLP, out.p, B, S, nullptr, nullptr, out.p, nout.p,
+                                                  nullptr), TP_E_ARG);
+        EXPECT_RC(tp_shard_forward_prefill_reduce(s, TP_STAGE_MLP, out.p, B, S, kv, others, out.p, nout.p, nullptr),
+                  TP_E_ARG);   // no cache for the MLP stage
+    }
     for (int w = 0; w < 3; ++w) EXPECT_RC(tp_shard_debug_view(s, w, &dbg), TP_OK);
     EXPECT_RC(tp_shard_debug_view(s, 3, &dbg), TP_E_ARG);
     int len = -1;
