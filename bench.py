@@ -1069,7 +1069,8 @@ def summarize_mfma(pmc_dir, out_name):
     kinds = {}
     for d in disp.values():
         kinds.setdefault(d["name"], []).append(d)
-    mode_of = {"0": "fp32 partial (out and down projections)", "1": "Q/K/V + rotary", "2": "gate/up + SwiGLU"}
+    mode_of = {"0": "fp32 partial (out and down projections)", "1": "Q/K/V + rotary", "2": "gate/up + SwiGLU",
+               "5": "out and down + reduce of the partials"}
     md = ["| kernel | dispatches | mean µs | MfmaUtil % | executed bf16 MFMA GFLOP per dispatch | clock GHz |",
           "|---|---:|---:|---:|---:|---:|"]
     for name, ds in sorted(kinds.items(), key=lambda kv: -statistics.mean(x["us"] for x in kv[1])):
