@@ -811,6 +811,50 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_vgpr_kernel(const bf16* __r
 // of 128x64, 256x192 as 8 x 1 of 32x192, or 256x128 as 4 x 2 of 64x64.
 // Waves 0-7 (two per SIMD) only read MFMA fragments from LDS and issue MFMAs;
 // waves 8-11 (one per SIMD) only move tiles from global memory into LDS.
+// The 256x256 tile's epilogue with the all-reduce's sum (EPI_SUM), shared
+// by all twelve waves: the tile goes through LDS as fp32 in two 128-row
+// halves, and every thread of the work-group -- producers included, whose
+// registers are free once the main loop ends -- streams the other ranks'
+// partials and the residual for two 16-byte chunks at a time.  A wave that
+// reduces only its own rows keeps about one chunk's loads in flight, its
+// accumulators filling the rest of its registers.
+constexpr int kCoopRows = 128, kCoopLd = 256 + 4;   // fp32 row stride of the staged half (padded)
+
+__device__ __forceinline__ void coop_sum_half(const float* sf, const Epilogue& epi, int row0, int n0, int M, int N,
+                                              int tid, int nthreads) {
+    constexpr int CPR = 256 / 4;                          // 16-byte chunks per row
+    constexpr int NCH = kCoopRows * CPR;
+    const int cb = epi.col0;
+    bf16* o = (bf16*)epi.out;
+    auto one = [&](int c, float (&v)[4], long long& off, bool& ok) {
+        const int rl = c / CPR, ch = c % CPR;
+        const int row = row0 + rl, col = n0 + ch * 4;
+        ok = c < NCH && row < M && col < N;
+        off = (long long)row * epi.ldo + cb + col;
+        const f32x4 a = *(const f32x4*)(sf + (c < NCH ? rl : 0) * kCoopLd + ch * 4);
+        v[0] = a[0];
+        v[1] = a[1];
+        v[2] = a[2];
+        v[3] = a[3];
+    };
+    auto put = [&](const float (&v)[4], long long off) {
+        uint32_t w0 = (uint32_t)f2bf_bits(v[0]) | ((uint32_t)f2bf_bits(v[1]) << 16);
+        uint32_t w1 = (uint32_t)f2bf_bits(v[2]) | ((uint32_t)f2bf_bits(v[3]) << 16);
+        *(uint2*)(o + off) = make_uint2(w0, w1);
+    };
+    for (int c = tid; c < NCH; c += 2 * nthreads) {
+        float v0[4], v1[4];
+        long long o0, o1;
+        bool k0, k1;
+        one(c, v0, o0, k0);
+        one(c + nthreads, v1, o1, k1);
+        if (k0) sum_ranks<4>(epi.sum, o0, v0);
+        if (k1) sum_ranks<4>(epi.sum, o1, v1);
+        if (k0) put(v0, o0);
+        if (k1) put(v1, o1);
+    }
+}
+
 // With the loads and LDS writes on waves of their own, the MFMA waves never
 // wait for global memory and never issue a memory-unit instruction.  Two LDS
 // stages: while the MFMA waves read tile kt from one, the producers write
@@ -833,7 +877,10 @@ __global__ __launch_bounds__(64 * (WM * WN + 4)) void gemm_ws_kernel(const bf16*
     constexpr int RS = 32;                       // rows per producer load step (256 threads x 16 B)
     constexpr int NL = (BM + BN) / RS;           // 16-byte loads per producer thread per tile
     static_assert((NW == 8 || NW == 4) && FN % 2 == 0 && BM % RS == 0 && BN % RS == 0, "tile shape");
-    __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+    // the 256x256 tile's sum epilogue runs on every wave (coop_sum_half)
+    constexpr bool COOP = MODE == EPI_SUM && BM == 256 && BN == 256 && WM == 2 && WN == 4;
+    constexpr int SMEM = COOP && kCoopRows * kCoopLd * 2 > 2 * STAGE ? kCoopRows * kCoopLd * 2 : 2 * STAGE;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -894,6 +941,17 @@ __global__ __launch_bounds__(64 * (WM * WN + 4)) void gemm_ws_kernel(const bf16*
             __syncthreads();
         }
         wait_vm<0>();
+        if constexpr (COOP) {
+            // the same four barriers as the MFMA waves' epilogue; no rows of their own to stage.
+            // Half 0 is reduced by the producers and the waves of row block 0 (512 threads),
+            // half 1 by every thread.
+            __syncthreads();
+            __syncthreads();
+            coop_sum_half((const float*)smem, epi, m0, n0, M, N, tid - 256, 512);
+            __syncthreads();
+            __syncthreads();
+            coop_sum_half((const float*)smem, epi, m0 + kCoopRows, n0, M, N, tid, 64 * (NW + 4));
+        }
         return;
     }
 
@@ -1073,6 +1131,40 @@ __global__ __launch_bounds__(64 * (WM * WN + 4)) void gemm_ws_kernel(const bf16*
                 __syncthreads();
             }
         }
+    }
+    if constexpr (COOP) {
+        // Half h holds the rows of MFMA row block h: its four waves stage their
+        // 128 x 64 tiles as fp32 rows, then the half is reduced.  Row block 1
+        // keeps its accumulators through half 0 and takes no part in reducing
+        // it (its registers are full); the paths differ per wave, the barrier
+        // count does not.
+        float* sf = (float*)smem;
+        const int col_in = lane & 31, row_in = 4 * (lane >> 5);
+        auto stage = [&]() {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        sf[(i * 32 + 8 * (r >> 2) + row_in + (r & 3)) * kCoopLd + wn * TN + j * 32 + col_in] =
+                            acc[i][j][r];
+        };
+        __syncthreads();   // every wave is past the main loop's LDS reads
+        if (wm == 0) {
+            stage();
+            __syncthreads();
+            coop_sum_half(sf, epi, m0, n0, M, N, tid, 512);
+            __syncthreads();   // half 0 read out of LDS
+            __syncthreads();
+        } else {
+            __syncthreads();
+            __syncthreads();
+            stage();
+            __syncthreads();
+        }
+        coop_sum_half(sf, epi, m0 + kCoopRows, n0, M, N, tid, 64 * (NW + 4));
+        return;
     }
     // Every wave, producers included, has passed the loop's last barrier:
     // no LDS read or write of the main loop is still pending, so each MFMA
