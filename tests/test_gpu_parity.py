@@ -583,7 +583,8 @@ def test_decode_reduce_graph_replay(B):
     ("bf16", 8, 0, True, None),        # eight ranks, own slot first
     ("bf16", 4, 2, False, None),       # no residual
     ("bf16", 2, 0, True, 1),           # register-staged 128x128 tile: the per-element epilogue
-    ("bf16", 2, 1, True, 14),          # producer/consumer 256x256
+    ("bf16", 2, 1, True, 14),          # producer/consumer 256x256 (the twelve-wave sum epilogue)
+    ("bf16", 8, 3, True, 14),          # ... with eight ranks, own slot in the middle
     ("bf16", 2, 1, True, 15),          # producer/consumer 256x192, eight MFMA waves
     ("bf16", 2, 1, True, 17),          # producer/consumer 256x192, four MFMA waves
     ("bf16", 2, 1, True, 18),          # producer/consumer 256x128, four MFMA waves
@@ -1108,6 +1109,41 @@ def test_70b_t8_prefill_sampled(layer70b):
     assert np.isfinite(pmg).all()
     refm = O.mlp_stage_rows(h.float().numpy(), L.W, L.spec, 8, 0, rows)
     assert_close(pmg[:, rows], refm["partial"], "70B mlp partial (sampled rows)", "bf16")
+
+
+def test_70b_t8_prefill_reduce_equals_two_calls(layer70b):
+    """The headline step's stages at their real shape (rank 0 of t=8, B=4,
+    S=4096: eight rounds of 256x256 tiles, the twelve-wave sum epilogue):
+    tp_shard_forward_prefill_reduce bit for bit against
+    tp_shard_forward_prefill followed by tp_partial_reduce with the same seven
+    other-rank partials, for h and y, and the caches."""
+    announce("70B-shaped t=8 prefill with the reduce folded in, B=4 S=4096, against prefill + reduce")
+    L = layer70b
+    B, S, hid, tp = 4, 4096, 8192, 8
+    sh_a, sh_b = L.shard(tp, 0), L.shard(tp, 0)
+    kv_a, kv_b = sh_a.kv_cache(B, S), sh_b.kv_cache(B, S)
+    x = L.dev["x"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    oth = [None] + [torch.randn((B, S, hid), generator=g, device="cuda") for _ in range(tp - 1)]
+    pa = sh_a.prefill(ATTN, x, kv_a)
+    h_ref = partial_reduce([pa] + oth[1:], residual=x)
+    del pa
+    h = sh_b.prefill_reduce(ATTN, x, oth, residual=x, kv=kv_b)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_ref), "h differs from prefill + partial_reduce"
+    ka, va = kv_a.read()
+    kb, vb = kv_b.read()
+    torch.cuda.synchronize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+    del ka, va, kb, vb
+    pm = sh_a.prefill(MLP, h_ref)
+    y_ref = partial_reduce([pm] + oth[1:], residual=h_ref)
+    del pm
+    y = sh_b.prefill_reduce(MLP, h, oth, residual=h)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref), "y differs from prefill + partial_reduce"
+    assert torch.isfinite(y.float()).all()
 
 
 def test_70b_t8_decode_full(layer70b):
