@@ -191,6 +191,18 @@ int tp_kv_view(tp_kv *kv, void **k, void **v);
 int tp_kv_set_len(tp_kv *kv, int len);
 int tp_kv_get_len(const tp_kv *kv, int *len);
 
+/* tp_kv_set_len_async / tp_kv_get_len_stream -- the same, ordered on
+ * `stream` instead of waiting for the whole device.  set_len_async writes
+ * the length and clears the overflow flag with a one-thread kernel on the
+ * stream (no host wait; it may be captured in a HIP graph, which records a
+ * kernel node, not a memset) and updates the host copy at once, so a
+ * forward call queued after it on the same stream sees the new length;
+ * TP_E_ARG as set_len.  get_len_stream copies the length on the stream and
+ * waits for that stream only, then behaves as get_len.  The caller orders
+ * other streams that use the cache. */
+int tp_kv_set_len_async(tp_kv *kv, int len, void *stream);
+int tp_kv_get_len_stream(const tp_kv *kv, int *len, void *stream);
+
 /* tp_shard_forward_prefill -- one stage over a prompt batch.  The stages
  * are the pages' split of a layer (undercodenews post 110319 on tensor
  * parallelism in transformers, "the Original"): ATTN = the column-parallel

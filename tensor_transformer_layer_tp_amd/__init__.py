@@ -109,6 +109,16 @@ class KVCache:
     def length(self, n: int) -> None:
         N.check(N.lib().tp_kv_set_len(self._h, int(n)), "tp_kv_set_len")
 
+    def set_length_async(self, n: int, stream=None) -> None:
+        """Set the length (and clear the overflow flag) in the stream's order."""
+        N.check(N.lib().tp_kv_set_len_async(self._h, int(n), _stream(stream)), "tp_kv_set_len_async")
+
+    def length_on(self, stream=None) -> int:
+        """The length, waiting for the stream only."""
+        n = C.c_int()
+        N.check(N.lib().tp_kv_get_len_stream(self._h, C.byref(n), _stream(stream)), "tp_kv_get_len_stream")
+        return n.value
+
     def write(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
         """Copy whole caches in (device tensors of the cache's shape and dtype)."""
         for name, src, dst in (("k", k, self._k), ("v", v, self._v)):

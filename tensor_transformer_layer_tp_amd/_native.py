@@ -43,6 +43,8 @@ SIGNATURES = [
     ("tp_kv_view", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p)]),
     ("tp_kv_set_len", C.c_int, [C.c_void_p, C.c_int]),
     ("tp_kv_get_len", C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
+    ("tp_kv_set_len_async", C.c_int, [C.c_void_p, C.c_int, C.c_void_p]),
+    ("tp_kv_get_len_stream", C.c_int, [C.c_void_p, C.POINTER(C.c_int), C.c_void_p]),
     ("tp_shard_forward_prefill", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
                                            C.c_void_p, C.c_void_p]),
     ("tp_shard_forward_prefill_reduce", C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p,

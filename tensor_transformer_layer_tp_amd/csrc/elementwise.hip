@@ -5,6 +5,15 @@ namespace tp {
 
 namespace {
 
+// The cache length and its overflow flag, written in stream order (a kernel,
+// so that a captured graph records no memset node).
+__global__ void set_len_kernel(int* dlen, int len) {
+    if (threadIdx.x == 0) {
+        dlen[0] = len;
+        dlen[1] = 0;
+    }
+}
+
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
     v = wave_sum_dpp(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -300,6 +309,10 @@ void zero_ints(int* p, int n, hipStream_t st) {
 
 void rope_turns(double* rev, int d, float theta, hipStream_t st) {
     hipLaunchKernelGGL(rope_turns_kernel, dim3(1), dim3(64), 0, st, rev, d, (double)theta);
+}
+
+void set_kv_len(int* dlen, int len, hipStream_t st) {
+    hipLaunchKernelGGL(set_len_kernel, dim3(1), dim3(64), 0, st, dlen, len);
 }
 
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float eps, hipStream_t st) {

@@ -610,6 +610,35 @@ int tp_kv_get_len(const tp_kv* kv, int* len) {
 
 }  // extern "C"
 
+namespace tp {
+// elementwise.hip: dlen[0] = len, dlen[1] = 0 (the cache length and a
+// cleared overflow flag), in stream order
+void set_kv_len(int* dlen, int len, hipStream_t st);
+}  // namespace tp
+
+extern "C" {
+
+int tp_kv_set_len_async(tp_kv* kv, int len, void* stream) {
+    if (!kv || len < 0 || len > kv->max_seq) return TP_E_ARG;
+    set_kv_len(kv->dlen, len, (hipStream_t)stream);
+    LAUNCH_CHECK("set_kv_len");
+    kv->len = len;
+    return TP_OK;
+}
+
+int tp_kv_get_len_stream(const tp_kv* kv, int* len, void* stream) {
+    if (!kv || !len) return TP_E_ARG;
+    int v[2] = {0, 0};
+    hipStream_t st = (hipStream_t)stream;
+    HIP_TRY(hipMemcpyAsync(v, kv->dlen, sizeof(v), hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    const_cast<tp_kv*>(kv)->len = v[0];
+    *len = v[0];
+    return v[1] ? TP_E_KV_FULL : TP_OK;
+}
+
+}  // extern "C"
+
 namespace {
 
 // The all-reduce's sum of a fused-sum call: the t ranks' partials (slot

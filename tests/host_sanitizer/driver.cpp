@@ -238,6 +238,16 @@ void flow(const Shape& sh, int dtype, int act, int fp8) {
         EXPECT_RC(tp_shard_forward_decode_reduce(s, TP_STAGE_MLP, out.p, B, nullptr, nullptr, out.p, nout.p,
                                                  nullptr), TP_E_ARG);
     }
+    // the cache length in stream order
+    EXPECT_RC(tp_kv_set_len_async(kv, cap + 1, nullptr), TP_E_ARG);
+    EXPECT_RC(tp_kv_set_len_async(nullptr, 1, nullptr), TP_E_ARG);
+    EXPECT_RC(tp_kv_set_len_async(kv, 3, nullptr), TP_OK);
+    {
+        int l3 = -1;
+        EXPECT_RC(tp_kv_get_len_stream(kv, &l3, nullptr), TP_OK);
+        EXPECT_RC(l3 == 3 ? TP_OK : TP_E_ARG, TP_OK);
+        EXPECT_RC(tp_kv_get_len_stream(kv, nullptr, nullptr), TP_E_ARG);
+    }
     // the cache fills up: an eager call on a full cache is refused up front
     EXPECT_RC(tp_kv_set_len(kv, cap + 1), TP_E_ARG);
     EXPECT_RC(tp_kv_set_len(kv, cap), TP_OK);

@@ -93,6 +93,8 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind ki
     return hipMemcpy(dst, src, n, kind);
 }
 
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+
 hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height,
                             hipMemcpyKind, hipStream_t) {
     if (!height || !width) return hipSuccess;
@@ -209,6 +211,12 @@ void gemm_f32(const float* A, long long lda, const float* B, long long ldb, int 
     in_alloc(A, ((long long)(M - 1) * lda + K) * 4, "GEMM A");
     in_alloc(B, ((long long)(N - 1) * ldb + K) * 4, "GEMM B");
     epilogue_ranges(epi, M, N, 4);
+}
+void set_kv_len(int* dlen, int len, hipStream_t) {
+    in_alloc(dlen, 8, "cache length and overflow flag");
+    dlen[0] = len;   // host memory here: the double performs the kernel's two stores
+    dlen[1] = 0;
+    ++g_launches;
 }
 void rmsnorm_bf16(const bf16* x, const bf16* g, bf16* out, int rows, int n, float, hipStream_t) {
     in_alloc(x, (long long)rows * n * 2, "norm input");

@@ -197,6 +197,8 @@ def test_kv_argument_errors():
     assert lib.tp_kv_get_len(None, C.byref(n)) == N.TP_E_ARG
     assert lib.tp_kv_view(None, None, None) == N.TP_E_ARG
     assert lib.tp_kv_create(None, 1, 16, C.byref(C.c_void_p())) == N.TP_E_ARG
+    assert lib.tp_kv_set_len_async(None, 3, None) == N.TP_E_ARG
+    assert lib.tp_kv_get_len_stream(None, C.byref(n), None) == N.TP_E_ARG
 
 
 def test_tune_hook_range():

@@ -703,6 +703,37 @@ def test_decode_graph_replay(B):
     del g
 
 
+def test_cache_length_in_stream_order():
+    """tp_kv_set_len_async / tp_kv_get_len_stream on a side stream: the length
+    set in the stream's order is the one a decode call queued after it on that
+    stream appends at, the overflow flag is cleared with it, and the decode
+    matches the same step after the synchronous tp_kv_set_len bit for bit."""
+    announce("cache length set and read in stream order")
+    L = Layer(512, 8, 4, 1024, batch=2, seq=40, gamma_noise=True, seed=71)
+    sh_a, sh_b = L.shard(2, 1), L.shard(2, 1)
+    kv_a, kv_b = sh_a.kv_cache(2, 48), sh_b.kv_cache(2, 48)
+    pre = L.dev["x"][:, :33].contiguous()
+    sh_a.prefill(ATTN, pre, kv_a)
+    sh_b.prefill(ATTN, pre, kv_b)
+    x = L.dev["x"][:, 33].contiguous()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    kv_a.length = 30                       # drop the last three positions
+    pa = sh_a.decode(ATTN, x, kv_a)
+    with torch.cuda.stream(s):
+        kv_b.set_length_async(30, stream=s)
+        pb = sh_b.decode(ATTN, x, kv_b, stream=s)
+        n = kv_b.length_on(s)
+    torch.cuda.synchronize()
+    assert n == 31
+    assert torch.equal(pa, pb)
+    ka, va = kv_a.read()
+    kb, vb = kv_b.read()
+    torch.cuda.synchronize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+    assert kv_a.length == 31
+
+
 def test_graph_replay_past_capacity_reports_overflow():
     """A captured decode call replayed once more than the cache holds
     appends nothing and raises the cache's overflow flag: the length query
