@@ -905,6 +905,11 @@ ROOF_KERNELS = {
                        2 * (16384 * 8192 + 7168 * 8192 + 16384 * 3584)),
     "gemm_up_7b_t2": ("gemm_bf16.hip", "gemm", (2048, 11008, 4096), ("prefill_7b", "roofline"), 1,
                       2 * (2048 * 4096 + 11008 * 4096 + 2048 * 5504)),
+    # traffic only (no bench-line figure): the 70B out and down projections with the reduce of the
+    # other seven ranks' partials in the epilogue share one kernel; their algorithmic bytes averaged
+    "gemm_sum_70b_t8": ("gemm_bf16.hip", "gemm_sum", (16384, 8192, 0), ("no line figure",), 0,
+                        (2 * (16384 * 1024 + 8192 * 1024) + 2 * (16384 * 3584 + 8192 * 3584)) // 2
+                        + 16384 * 8192 * (4 * 7 + 2 + 2)),
     "gemv_up_7b_t4": ("decode.hip", "gemv", (5504, 4096), ("decode", "roofline"), 0,
                       2 * (5504 * 4096 + 4096 + 2752)),
     "gemv_up_70b_t8": ("decode.hip", "gemv", (7168, 8192), ("decode_70b", "roofline"), 0,
@@ -921,6 +926,8 @@ def roof_patterns(key):
     """Regexes of the launch kinds of one roofline kernel."""
     import re
     _, kind, shape, _, _, _ = ROOF_KERNELS[key]
+    if kind == "gemm_sum":
+        return [re.escape("gemm_ws_kernel<256, 256, 2, 4, 5>")]
     if kind == "gemv":
         # batch-1 bf16 GEMV with the SwiGLU epilogue and the fused norm; its
         # NI (16-byte chunks per thread) follows from K
